@@ -1,0 +1,87 @@
+"""QLoRA NF4 quantized linear layer on AMD MI355X (gfx950).
+
+The compute lives in libqlora.so (hand-written HIP kernels behind the C ABI in
+include/qlora.h).  This package only binds it: ``_lib`` mirrors the C entry
+points one to one, and the helpers below allocate output tensors with torch
+and pass them through.  Nothing here computes any part of the layer.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+from . import _lib
+from ._lib import (QLoraError, lib, qlora_double_quant, qlora_double_quant_workspace,  # noqa: F401
+                   qlora_linear_bwd, qlora_linear_bwd_workspace, qlora_linear_fwd,
+                   qlora_linear_fwd_workspace, qlora_nf4_dequant, qlora_nf4_levels,
+                   qlora_nf4_quantize, qlora_nf4_sizes)
+
+
+@dataclasses.dataclass
+class QuantizedWeight:
+    """A frozen NF4 weight [N, K] with double-quantized constants (device tensors)."""
+    N: int
+    K: int
+    codes: "object"   # uint8 [N, K/2]
+    absmax: "object"  # fp32 [N*K/64] (first-level constants, kept for inspection)
+    c2: "object"      # uint8 [N*K/64]
+    c1: "object"      # fp32 [ceil(N*K/16384)]
+    mean: "object"    # fp32 [1]
+
+
+def quantize(W, stream=None) -> QuantizedWeight:
+    """NF4-quantize an fp32 [N, K] device tensor and double-quantize its constants."""
+    import torch
+    N, K = W.shape
+    code_bytes, n_c2, n_c1 = qlora_nf4_sizes(N, K)
+    dev = W.device
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    absmax = torch.empty(n_c2, dtype=torch.float32, device=dev)
+    c2 = torch.empty(n_c2, dtype=torch.uint8, device=dev)
+    c1 = torch.empty(max(n_c1, 1), dtype=torch.float32, device=dev)
+    mean = torch.zeros(1, dtype=torch.float32, device=dev)
+    qlora_nf4_quantize(W, codes, absmax, stream)
+    ws = torch.empty(max(qlora_double_quant_workspace(n_c2), 8), dtype=torch.uint8, device=dev)
+    qlora_double_quant(absmax, c2, c1, mean, ws, stream)
+    return QuantizedWeight(N, K, codes, absmax, c2, c1, mean)
+
+
+def dequantize(q: QuantizedWeight, stream=None):
+    """bf16 [N, K] weight (returned as int16 bit patterns viewed as bfloat16)."""
+    import torch
+    out = torch.empty((q.N, q.K), dtype=torch.bfloat16, device=q.codes.device)
+    qlora_nf4_dequant(q.codes, q.c2, q.c1, q.mean, q.N, q.K, out, stream)
+    return out
+
+
+def fwd_workspace(M: int, N: int, K: int, r: int, device):
+    """A zero-filled forward workspace (the kernels leave it zero-filled after each call)."""
+    import torch
+    n = max(qlora_linear_fwd_workspace(M, N, K, r), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def linear_fwd(X, q: QuantizedWeight, A, B, alpha: float, workspace=None, want_h: bool = True, stream=None):
+    """Y = X W_deq^T + (alpha/r) (X A^T) B^T.  X, A, B bf16; returns (Y bf16 [M,N], H fp32 [M,r] or None)."""
+    import torch
+    M = X.shape[0]
+    r = A.shape[0]
+    Y = torch.empty((M, q.N), dtype=torch.bfloat16, device=X.device)
+    H = torch.empty((M, r), dtype=torch.float32, device=X.device) if want_h else None
+    if workspace is None:
+        workspace = fwd_workspace(M, q.N, q.K, r, X.device)
+    qlora_linear_fwd(X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, Y, H, workspace, q.N, stream)
+    return Y, H
+
+
+def linear_bwd(dY, X, q: QuantizedWeight, A, B, alpha: float, H=None, want_dx: bool = True, stream=None):
+    """Gradients (dX or None, dA, dB) of the QLoRA linear; the NF4 weight gets none."""
+    import torch
+    M, K = X.shape
+    r = A.shape[0]
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device) if want_dx else None
+    dA = torch.empty((r, K), dtype=torch.bfloat16, device=X.device)
+    dB = torch.empty((q.N, r), dtype=torch.bfloat16, device=X.device)
+    ws = torch.empty(max(qlora_linear_bwd_workspace(M, q.N, K, r), 256), dtype=torch.uint8, device=X.device)
+    qlora_linear_bwd(dY, X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, H, dX, dA, dB, ws, stream)
+    return dX, dA, dB

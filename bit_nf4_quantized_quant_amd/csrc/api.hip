@@ -1,0 +1,208 @@
+// C ABI of libqlora.so: argument validation on the host, then kernel launches
+// on the caller's stream.  Every check runs before the first HIP call, so a
+// rejected call touches neither the device nor the stream.
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/qlora.h"
+#include "launch.h"
+#include "nf4_table.h"
+
+namespace qlora {
+size_t decode_workspace_bytes(int64_t M, int64_t r);
+hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int64_t r, float* H,
+                            float* scratch, hipStream_t s);
+size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r);
+size_t gemm_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+}  // namespace qlora
+
+using namespace qlora;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;       // every extent must fit a 32-bit grid index
+constexpr int64_t kMaxElems = int64_t(1) << 40;     // elements of any one tensor
+constexpr int64_t kDecodeMaxM = 16;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shape checks shared by forward and backward.
+int check_layer(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M < 0 || N < 0 || K < 0 || r < 0) return QLORA_EINVAL;
+  if (K % 64 != 0) return QLORA_ESHAPE;
+  if (r < 1 || r > 128) return QLORA_ESHAPE;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return QLORA_ESHAPE;
+  if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return QLORA_ESHAPE;
+  return QLORA_OK;
+}
+
+int check_weight(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean) {
+  if (!codes || !c2 || !c1 || !mean) return QLORA_EINVAL;
+  if (!aligned(codes, 16) || !aligned(c1, 4) || !aligned(mean, 4)) return QLORA_EINVAL;
+  return QLORA_OK;
+}
+
+size_t fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M <= kDecodeMaxM) return round256(decode_workspace_bytes(M, r));
+  return round256((size_t)M * r * sizeof(float)) + round256(lora_down_scratch_bytes(M, K, r));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_str(int status) {
+  switch (status) {
+    case QLORA_OK: return "QLORA_OK";
+    case QLORA_EINVAL: return "QLORA_EINVAL: null, negative, misaligned argument or workspace too small";
+    case QLORA_ESHAPE: return "QLORA_ESHAPE: unsupported shape (K % 64, r outside [1,128], size limit)";
+    case QLORA_EHIP: return "QLORA_EHIP: the HIP runtime rejected a kernel launch";
+    default: return "QLORA: unknown status";
+  }
+}
+
+int qlora_nf4_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* n_c2, int64_t* n_c1) {
+  if (N < 0 || K < 0) return QLORA_EINVAL;
+  if (K % 64 != 0) return QLORA_ESHAPE;
+  if (N >= kMaxDim || K >= kMaxDim || N * K >= kMaxElems) return QLORA_ESHAPE;
+  const int64_t p = N * K;
+  if (code_bytes) *code_bytes = p / 2;
+  if (n_c2) *n_c2 = p / 64;
+  if (n_c1) *n_c1 = (p / 64 + 255) / 256;
+  return QLORA_OK;
+}
+
+int qlora_nf4_levels(float* levels16) {
+  if (!levels16) return QLORA_EINVAL;
+  std::memcpy(levels16, nf4_table().level, 16 * sizeof(float));
+  return QLORA_OK;
+}
+
+int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax, void* stream) {
+  int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
+  if (st) return st;
+  if (N * K == 0) return QLORA_OK;
+  if (!W || !codes || !absmax) return QLORA_EINVAL;
+  if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(absmax, 4)) return QLORA_EINVAL;
+  return status_of(launch_nf4_quantize(W, N, K, codes, absmax, (hipStream_t)stream));
+}
+
+size_t qlora_double_quant_workspace(int64_t n_c2) {
+  (void)n_c2;
+  return double_quant_workspace_bytes();
+}
+
+int qlora_double_quant(const float* absmax, int64_t n_c2, uint8_t* c2, float* c1, float* mean, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (n_c2 < 0) return QLORA_EINVAL;
+  if (n_c2 >= kMaxElems / 64) return QLORA_ESHAPE;
+  if (n_c2 == 0) return QLORA_OK;
+  if (!absmax || !c2 || !c1 || !mean || !workspace) return QLORA_EINVAL;
+  if (!aligned(absmax, 4) || !aligned(c1, 4) || !aligned(mean, 4) || !aligned(workspace, 8)) return QLORA_EINVAL;
+  if (workspace_bytes < double_quant_workspace_bytes()) return QLORA_EINVAL;
+  return status_of(launch_double_quant(absmax, n_c2, c2, c1, mean, workspace, (hipStream_t)stream));
+}
+
+int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
+                      int64_t K, uint16_t* W_bf16, void* stream) {
+  int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
+  if (st) return st;
+  if (N * K == 0) return QLORA_OK;
+  if ((st = check_weight(codes, c2, c1, mean))) return st;
+  if (!W_bf16 || !aligned(W_bf16, 16)) return QLORA_EINVAL;
+  return status_of(launch_nf4_dequant(codes, c2, c1, mean, N, K, W_bf16, (hipStream_t)stream));
+}
+
+size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (check_layer(M, N, K, r)) return 0;
+  return fwd_ws(M, N, K, r);
+}
+
+int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes, const uint8_t* c2,
+                     const float* c1, const float* mean, const uint16_t* A, const uint16_t* B, int64_t r,
+                     float alpha, uint16_t* Y, float* H_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_layer(M, N, K, r);
+  if (st) return st;
+  if (K == 0) return QLORA_ESHAPE;
+  if (M == 0 || N == 0) return QLORA_OK;
+  if ((st = check_weight(codes, c2, c1, mean))) return st;
+  if (!X || !A || !B || !Y || !workspace) return QLORA_EINVAL;
+  if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(Y, 2) || !aligned(workspace, 256))
+    return QLORA_EINVAL;
+  if (H_out && !aligned(H_out, 4)) return QLORA_EINVAL;
+  if (workspace_bytes < fwd_ws(M, N, K, r)) return QLORA_EINVAL;
+
+  FwdArgs a;
+  a.X = X;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.r = r;
+  a.w = Nf4Weight{codes, c2, c1, mean};
+  a.A = A;
+  a.B = B;
+  a.scale = alpha / (float)r;
+  a.Y = Y;
+  a.H = H_out;
+  a.workspace = workspace;
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= kDecodeMaxM) return status_of(launch_decode_fwd(a, s));
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* H = H_out ? H_out : reinterpret_cast<float*>(ws);
+  float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
+  a.H = H;
+  hipError_t e = launch_lora_down(X, M, K, A, r, H, scratch, s);
+  if (e != hipSuccess) return QLORA_EHIP;
+  return status_of(launch_gemm_fwd(a, s));
+}
+
+size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (check_layer(M, N, K, r)) return 0;
+  return gemm_bwd_workspace_bytes(M, N, K, r);
+}
+
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                     const uint8_t* c2, const float* c1, const float* mean, const uint16_t* A, const uint16_t* B,
+                     int64_t r, float alpha, const float* H, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_layer(M, N, K, r);
+  if (st) return st;
+  if (K == 0) return QLORA_ESHAPE;
+  if ((st = check_weight(codes, c2, c1, mean))) return st;
+  if (!A || !B || !dA || !dB || !workspace) return QLORA_EINVAL;
+  if (M > 0 && (!dY || !X)) return QLORA_EINVAL;
+  if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(dA, 16) ||
+      !aligned(dB, 2) || !aligned(workspace, 256))
+    return QLORA_EINVAL;
+  if (H && !aligned(H, 4)) return QLORA_EINVAL;
+  if (dX && !aligned(dX, 16)) return QLORA_EINVAL;
+  if (workspace_bytes < gemm_bwd_workspace_bytes(M, N, K, r)) return QLORA_EINVAL;
+  if (N == 0) return QLORA_OK;
+
+  BwdArgs a;
+  a.dY = dY;
+  a.X = X;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.r = r;
+  a.w = Nf4Weight{codes, c2, c1, mean};
+  a.A = A;
+  a.B = B;
+  a.scale = alpha / (float)r;
+  a.H = H;
+  a.dX = dX;
+  a.dA = dA;
+  a.dB = dB;
+  a.workspace = workspace;
+  return status_of(launch_linear_bwd(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,738 @@
+// LDS-tiled bf16 MFMA engine with operand loaders that dequantize NF4 on the
+// way into LDS (gfx950).  Serves the forward at M > 16 and every product of
+// the backward.
+//
+// itwiki "QLoRA", section on the computation: the layer output is
+// X doubleDequant(c1, c2, W) + X L1 L2 with bf16 compute; weights are
+// dequantized again for every forward and backward product and only the
+// input and the LoRA factors receive gradients.  minnong511 "quantization":
+// y = W x + (alpha/r) B A x; backward updates A and B only.
+//
+// The engine computes C[i][j] = sum_k Aop[i][k] * Bop[j][k] for a BM x BN
+// output tile: both operands are staged in LDS as [rows][64 + 8] bf16 tiles
+// (reduction contiguous, 16-byte pad so that 16-byte fragment reads of eight
+// consecutive rows hit distinct banks), double-buffered with one barrier per
+// 64-wide reduction step.  Four waves in a 2 x 2 grid each own
+// (BM/2) x (BN/2) of the tile as 32x32x16 MFMA accumulators.
+//
+// Loaders turn every source layout into that LDS form:
+//   RowsBf16  bf16 [rows][red] (X, dY, A, B)
+//   Nf4Rows   NF4 codes [rows][K/2] -> bf16 W_deq, bit-exact with the spec
+//   Nf4Cols   NF4 codes read as [red = n][rows = k]: the transposed weight for dX
+//   ColsBf16  bf16 [red][rows] (transposed operands of the LoRA gradients)
+//   RowsF32 / ColsF32  fp32 sources (H, dH) rounded to bf16, optionally scaled
+// A transposed source is read as 4 x 8 patches (4 rows of 8 contiguous
+// elements) and written to LDS as 8 rows of 4 reduction elements.
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace qlora {
+namespace {
+
+constexpr int BK = 64;
+constexpr int PITCH = BK + 8;  // bf16 elements per LDS row
+constexpr int NT = 256;        // threads per workgroup
+
+typedef uint16_t lds_t;
+
+__device__ __forceinline__ void st_lds16(lds_t* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st_lds8(lds_t* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ uint32_t lo16(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ __forceinline__ uint32_t hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- loaders
+
+// bf16 source, rows contiguous in the reduction index.
+template <int R>
+struct RowsBf16 {
+  static constexpr int kChunks = R * BK / 8 / NT;  // 16-byte chunks per thread
+  const uint16_t* src;
+  int64_t ld;       // elements between rows
+  int rows;         // valid rows from row0
+  int red;          // valid reduction length
+  int64_t row0;
+  bool vec;         // ld % 8 == 0 and 16-byte aligned base
+  u32x4 reg[kChunks];
+
+  __device__ void load(int kt) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int rr = idx >> 3, ch = idx & 7;
+      const int k = kt * BK + ch * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rr < rows) {
+        const uint16_t* p = src + (row0 + rr) * ld + k;
+        if (vec && k + 8 <= red) {
+          v = ld16(p);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) e[q] = (k + q < red) ? p[q] : 0u;
+          v = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+        }
+      }
+      reg[c] = v;
+    }
+  }
+  __device__ void store(lds_t* t) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      st_lds16(t + (idx >> 3) * PITCH + (idx & 7) * 8, reg[c]);
+    }
+  }
+};
+
+// fp32 source with rows contiguous in the reduction index, scaled and rounded to bf16.
+template <int R>
+struct RowsF32 {
+  static constexpr int kChunks = R * BK / 8 / NT;
+  const float* src;
+  int64_t ld;
+  int rows;
+  int red;
+  int64_t row0;
+  float scale;
+  u32x4 reg[kChunks];
+
+  __device__ void load(int kt) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int rr = idx >> 3, ch = idx & 7;
+      const int k = kt * BK + ch * 8;
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f[q] = 0.f;
+      if (rr < rows) {
+        const float* p = src + (row0 + rr) * ld + k;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (k + q < red) f[q] = p[q] * scale;
+      }
+      reg[c] = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7])};
+    }
+  }
+  __device__ void store(lds_t* t) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      st_lds16(t + (idx >> 3) * PITCH + (idx & 7) * 8, reg[c]);
+    }
+  }
+};
+
+// bf16 source stored [red][rows]: tile row i is source column col0 + i.
+template <int R>
+struct ColsBf16 {
+  static constexpr int kPatches = 2 * R;  // (BK/4) x (R/8) patches of 4 red x 8 cols
+  const uint16_t* src;
+  int64_t ld;    // elements between source rows (reduction steps)
+  int cols;      // valid tile rows (source columns) from col0
+  int red;       // valid reduction length
+  int64_t col0;
+  bool vec;
+  u32x4 reg[4];
+  bool active;
+
+  __device__ void load(int kt) {
+    const int pid = threadIdx.x;
+    active = pid < kPatches;
+    if (!active) return;
+    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+    const int c = pc * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = kt * BK + pr * 4 + q;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (k < red) {
+        const uint16_t* p = src + (int64_t)k * ld + col0 + c;
+        if (vec && c + 8 <= cols) {
+          v = ld16(p);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int z = 0; z < 8; ++z) e[z] = (c + z < cols) ? p[z] : 0u;
+          v = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+        }
+      }
+      reg[q] = v;
+    }
+  }
+  __device__ void store(lds_t* t) const {
+    if (!active) return;
+    const int pid = threadIdx.x;
+    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // columns 2w (low halves) and 2w+1 (high halves)
+      const u32x2 a = {lo16(reg[0][w], reg[1][w]), lo16(reg[2][w], reg[3][w])};
+      const u32x2 b = {hi16(reg[0][w], reg[1][w]), hi16(reg[2][w], reg[3][w])};
+      st_lds8(t + (pc * 8 + 2 * w) * PITCH + pr * 4, a);
+      st_lds8(t + (pc * 8 + 2 * w + 1) * PITCH + pr * 4, b);
+    }
+  }
+};
+
+// fp32 source stored [red][rows], rounded to bf16 (optionally scaled).
+template <int R>
+struct ColsF32 {
+  static constexpr int kPatches = 2 * R;
+  const float* src;
+  int64_t ld;
+  int cols;
+  int red;
+  int64_t col0;
+  float scale;
+  uint32_t reg[8][2];
+  bool active;
+
+  __device__ void load(int kt) {
+    const int pid = threadIdx.x;
+    active = pid < kPatches;
+    if (!active) return;
+    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+    const int c = pc * 8;
+    float f[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = kt * BK + pr * 4 + q;
+      const float* p = src + (int64_t)k * ld + col0 + c;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) f[q][z] = (k < red && c + z < cols) ? p[z] * scale : 0.f;
+    }
+#pragma unroll
+    for (int z = 0; z < 8; ++z) {
+      reg[z][0] = pack_bf16x2(f[0][z], f[1][z]);
+      reg[z][1] = pack_bf16x2(f[2][z], f[3][z]);
+    }
+  }
+  __device__ void store(lds_t* t) const {
+    if (!active) return;
+    const int pid = threadIdx.x;
+    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+#pragma unroll
+    for (int z = 0; z < 8; ++z) st_lds8(t + (pc * 8 + z) * PITCH + pr * 4, u32x2{reg[z][0], reg[z][1]});
+  }
+};
+
+// NF4 weight rows [n][k]: tile row i = weight row n0 + i, reduction = k.  One
+// 64-wide reduction step is exactly one NF4 block per row, so every thread
+// needs a single constant: thread t dequantizes half a block (32 codes) of row
+// t/2 (for R = 128) to bf16( fp32(level * c_hat) ).
+template <int R>
+struct Nf4Rows {
+  static constexpr int kUnits = R * 2 / NT;  // half-blocks per thread
+  const uint8_t* codes;
+  const uint8_t* c2;
+  const float* c1;
+  float mean;
+  int64_t K;
+  int rows;
+  int64_t row0;
+  const float* lut;  // 16 levels in LDS
+  u32x4 q[kUnits];
+  float chat[kUnits];
+
+  __device__ void load(int kt) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int idx = threadIdx.x + u * NT;
+      const int rr = idx >> 1, h = idx & 1;
+      if (rr < rows) {
+        const int64_t n = row0 + rr;
+        q[u] = ld16(codes + n * (K / 2) + kt * 32 + h * 16);
+        const int64_t bi = n * (K / 64) + kt;
+        chat[u] = dequant_constant(c2[bi], c1[bi >> 8], mean);
+      } else {
+        q[u] = u32x4{0u, 0u, 0u, 0u};
+        chat[u] = 0.f;
+      }
+    }
+  }
+  __device__ void store(lds_t* t) const {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int idx = threadIdx.x + u * NT;
+      const int rr = idx >> 1, h = idx & 1;
+      lds_t* dst = t + rr * PITCH + h * 32;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t word = q[u][w];
+        u32x4 o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float lo = __fmul_rn(lut[(word >> (8 * b)) & 15u], chat[u]);
+          const float hi = __fmul_rn(lut[(word >> (8 * b + 4)) & 15u], chat[u]);
+          o[b] = pack_bf16x2(lo, hi);
+        }
+        st_lds16(dst + w * 8, o);
+      }
+    }
+  }
+};
+
+// NF4 weight read transposed: tile row i = weight column k0 + i, reduction =
+// weight row n.  A thread takes a patch of 4 rows (n) x 8 columns (k); the 8
+// columns lie in one block of each row, so it needs 4 constants.
+template <int R>
+struct Nf4Cols {
+  static constexpr int kPatches = 2 * R;
+  const uint8_t* codes;
+  const uint8_t* c2;
+  const float* c1;
+  float mean;
+  int64_t N, K;
+  int64_t col0;
+  const float* lut;
+  uint32_t word[4];
+  float chat[4];
+  bool active;
+
+  __device__ void load(int kt) {
+    const int pid = threadIdx.x;
+    active = pid < kPatches;
+    if (!active) return;
+    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+    const int64_t k = col0 + pc * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = (int64_t)kt * BK + pr * 4 + q;
+      if (n < N && k < K) {
+        word[q] = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + k / 2);
+        const int64_t bi = n * (K / 64) + k / 64;
+        chat[q] = dequant_constant(c2[bi], c1[bi >> 8], mean);
+      } else {
+        word[q] = 0u;
+        chat[q] = 0.f;
+      }
+    }
+  }
+  __device__ void store(lds_t* t) const {
+    if (!active) return;
+    const int pid = threadIdx.x;
+    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+#pragma unroll
+    for (int z = 0; z < 8; ++z) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = __fmul_rn(lut[(word[q] >> (4 * z)) & 15u], chat[q]);
+      st_lds8(t + (pc * 8 + z) * PITCH + pr * 4, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+    }
+  }
+};
+
+// ---------------------------------------------------------------- engine
+
+template <int BM, int BN>
+struct Acc {
+  static constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32;
+  f32x16 c[TM][TN];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void mma_tile(const lds_t* sa, const lds_t* sb, Acc<BM, BN>& acc) {
+  constexpr int TM = Acc<BM, BN>::TM, TN = Acc<BM, BN>::TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, kq = (lane >> 5) * 8;
+#pragma unroll
+  for (int kk = 0; kk < BK; kk += 16) {
+    bf16x8 fa[TM], fb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[i] = __builtin_bit_cast(bf16x8, ld16(sa + (wm * (BM / 2) + i * 32 + r) * PITCH + kk + kq));
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[j] = __builtin_bit_cast(bf16x8, ld16(sb + (wn * (BN / 2) + j * 32 + r) * PITCH + kk + kq));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+template <int BM, int BN, class LA, class LB>
+__device__ void run_phase(LA& la, LB& lb, int kt0, int kt1, lds_t* sa, lds_t* sb, Acc<BM, BN>& acc) {
+  if (kt0 >= kt1) return;
+  constexpr int SA = BM * PITCH, SB = BN * PITCH;
+  la.load(kt0);
+  lb.load(kt0);
+  la.store(sa);
+  lb.store(sb);
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) {
+      la.load(kt + 1);
+      lb.load(kt + 1);
+    }
+    mma_tile<BM, BN>(sa + cur * SA, sb + cur * SB, acc);
+    if (more) {
+      la.store(sa + (cur ^ 1) * SA);
+      lb.store(sb + (cur ^ 1) * SB);
+    }
+    __syncthreads();
+  }
+}
+
+// Lane l of a 32x32 accumulator holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4.
+template <int BM, int BN, class F>
+__device__ __forceinline__ void for_each_out(const Acc<BM, BN>& acc, F f) {
+  constexpr int TM = Acc<BM, BN>::TM, TN = Acc<BM, BN>::TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int col = wn * (BN / 2) + j * 32 + (lane & 31);
+        f(row, col, acc.c[i][j][v]);
+      }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void zero(Acc<BM, BN>& acc) {
+#pragma unroll
+  for (int i = 0; i < Acc<BM, BN>::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Acc<BM, BN>::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.f;
+}
+
+__device__ __forceinline__ void load_lut(float* lut, const Nf4Table& tab) {
+  if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xFFFFu); }
+
+// ---------------------------------------------------------------- kernels
+
+constexpr int FBM = 128, FBN = 128;
+
+// Forward, M > 16: Y = bf16( X W_deq^T + (s H) B^T ).  Phase 1 streams X and
+// the NF4 weight over K; phase 2 appends the LoRA product as r more reduction
+// steps with s*H (bf16) against B.
+struct FwdGemmParams {
+  const uint16_t* X;
+  int64_t M, N, K;
+  int r;
+  const uint8_t* codes;
+  const uint8_t* c2;
+  const float* c1;
+  const float* mean;
+  const float* H;
+  const uint16_t* B;
+  bool b_vec;
+  float scale;
+  uint16_t* Y;
+  Nf4Table tab;
+};
+
+__global__ void __launch_bounds__(NT) fwd_gemm_kernel(FwdGemmParams p) {
+  __shared__ __attribute__((aligned(16))) lds_t sa[2 * FBM * PITCH];
+  __shared__ __attribute__((aligned(16))) lds_t sb[2 * FBN * PITCH];
+  __shared__ float lut[16];
+  load_lut(lut, p.tab);
+  const int64_t m0 = (int64_t)blockIdx.y * FBM, n0 = (int64_t)blockIdx.x * FBN;
+  Acc<FBM, FBN> acc;
+  zero(acc);
+  __syncthreads();
+  {
+    RowsBf16<FBM> la{p.X, p.K, (int)min<int64_t>(FBM, p.M - m0), (int)p.K, m0, true};
+    Nf4Rows<FBN> lb{p.codes, p.c2, p.c1, *p.mean, p.K, (int)min<int64_t>(FBN, p.N - n0), n0, lut};
+    run_phase<FBM, FBN>(la, lb, 0, (int)(p.K / BK), sa, sb, acc);
+  }
+  {
+    RowsF32<FBM> la{p.H, p.r, (int)min<int64_t>(FBM, p.M - m0), p.r, m0, p.scale};
+    RowsBf16<FBN> lb{p.B, p.r, (int)min<int64_t>(FBN, p.N - n0), p.r, n0, p.b_vec};
+    run_phase<FBM, FBN>(la, lb, 0, (p.r + BK - 1) / BK, sa, sb, acc);
+  }
+  for_each_out(acc, [&](int i, int j, float v) {
+    const int64_t m = m0 + i, n = n0 + j;
+    if (m < p.M && n < p.N) p.Y[m * p.N + n] = to_bf16(v);
+  });
+}
+
+// Generic bf16 x bf16 product with fp32 output (split-K partials or final):
+// out[split][i][j] = scale * sum_{k in split} Aop[i][k] Bop[j][k].
+template <int BM, int BN, class LA, class LB>
+struct SkinnyParams {
+  LA la;
+  LB lb;
+  int64_t rows, cols;   // output extent
+  int ksteps;           // total 64-wide reduction steps
+  int steps_per_split;
+  float* out;           // [splits][rows][cols]
+};
+
+template <int BM, int BN, class LA, class LB>
+__global__ void __launch_bounds__(NT) skinny_kernel(SkinnyParams<BM, BN, LA, LB> p) {
+  __shared__ __attribute__((aligned(16))) lds_t sa[2 * BM * PITCH];
+  __shared__ __attribute__((aligned(16))) lds_t sb[2 * BN * PITCH];
+  const int64_t i0 = (int64_t)blockIdx.y * BM, j0 = (int64_t)blockIdx.x * BN;
+  LA la = p.la;
+  LB lb = p.lb;
+  la.row_origin(i0, p.rows);
+  lb.row_origin(j0, p.cols);
+  Acc<BM, BN> acc;
+  zero(acc);
+  const int kt0 = blockIdx.z * p.steps_per_split;
+  const int kt1 = min(p.ksteps, kt0 + p.steps_per_split);
+  run_phase<BM, BN>(la, lb, kt0, kt1, sa, sb, acc);
+  float* out = p.out + (int64_t)blockIdx.z * p.rows * p.cols;
+  for_each_out(acc, [&](int i, int j, float v) {
+    const int64_t a = i0 + i, b = j0 + j;
+    if (a < p.rows && b < p.cols) out[a * p.cols + b] = v;
+  });
+}
+
+// Sum split-K partials: out = scale * sum_s part[s]; bf16 or fp32 output.
+__global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t count, float scale,
+                                                            uint16_t* __restrict__ out_bf16,
+                                                            float* __restrict__ out_f32) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    float s = 0.f;
+    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * count + i];
+    s *= scale;
+    if (out_bf16) out_bf16[i] = to_bf16(s);
+    if (out_f32) out_f32[i] = s;
+  }
+}
+
+// dX = dY W_deq + dH A (bf16 output).  Phase 1 contracts over n with the
+// transposed NF4 weight; phase 2 appends r steps of dH against A^T.
+struct DxParams {
+  const uint16_t* dY;
+  int64_t M, N, K;
+  int r;
+  const uint8_t* codes;
+  const uint8_t* c2;
+  const float* c1;
+  const float* mean;
+  const float* dH;
+  const uint16_t* A;
+  uint16_t* dX;
+  Nf4Table tab;
+};
+
+__global__ void __launch_bounds__(NT) dx_gemm_kernel(DxParams p) {
+  __shared__ __attribute__((aligned(16))) lds_t sa[2 * FBM * PITCH];
+  __shared__ __attribute__((aligned(16))) lds_t sb[2 * FBN * PITCH];
+  __shared__ float lut[16];
+  load_lut(lut, p.tab);
+  const int64_t m0 = (int64_t)blockIdx.y * FBM, k0 = (int64_t)blockIdx.x * FBN;
+  Acc<FBM, FBN> acc;
+  zero(acc);
+  __syncthreads();
+  {
+    RowsBf16<FBM> la{p.dY, p.N, (int)min<int64_t>(FBM, p.M - m0), (int)p.N, m0, (p.N % 8) == 0};
+    Nf4Cols<FBN> lb{p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut};
+    run_phase<FBM, FBN>(la, lb, 0, (int)((p.N + BK - 1) / BK), sa, sb, acc);
+  }
+  {
+    RowsF32<FBM> la{p.dH, p.r, (int)min<int64_t>(FBM, p.M - m0), p.r, m0, 1.0f};
+    ColsBf16<FBN> lb{p.A, p.K, (int)min<int64_t>(FBN, p.K - k0), p.r, k0, true};
+    run_phase<FBM, FBN>(la, lb, 0, (p.r + BK - 1) / BK, sa, sb, acc);
+  }
+  for_each_out(acc, [&](int i, int j, float v) {
+    const int64_t m = m0 + i, k = k0 + j;
+    if (m < p.M && k < p.K) p.dX[m * p.K + k] = to_bf16(v);
+  });
+}
+
+// Skinny-product loaders with a per-tile origin, built on the loaders above.
+template <int R>
+struct SRowsBf16 : RowsBf16<R> {
+  __device__ void row_origin(int64_t o, int64_t total) {
+    this->row0 = o;
+    this->rows = (int)min<int64_t>(R, total - o);
+  }
+};
+template <int R>
+struct SColsBf16 : ColsBf16<R> {
+  __device__ void row_origin(int64_t o, int64_t total) {
+    this->col0 = o;
+    this->cols = (int)min<int64_t>(R, total - o);
+  }
+};
+template <int R>
+struct SColsF32 : ColsF32<R> {
+  __device__ void row_origin(int64_t o, int64_t total) {
+    this->col0 = o;
+    this->cols = (int)min<int64_t>(R, total - o);
+  }
+};
+
+unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+template <int BM, int BN, class LA, class LB>
+hipError_t launch_skinny(const LA& la, const LB& lb, int64_t rows, int64_t cols, int64_t red, int splits,
+                         float* out, hipStream_t s) {
+  SkinnyParams<BM, BN, LA, LB> p{la, lb, rows, cols, 0, 0, out};
+  p.ksteps = (int)((red + BK - 1) / BK);
+  p.steps_per_split = (p.ksteps + splits - 1) / splits;
+  // splits that receive no steps (and an empty reduction) still write zeros
+  dim3 grid(cdiv(cols, BN), cdiv(rows, BM), (unsigned)splits);
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((skinny_kernel<BM, BN, LA, LB>), grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+int pick_splits(int64_t tiles, int64_t ksteps) {
+  int s = 1;
+  while (tiles * s < 512 && s * 2 <= ksteps && s < 64) s *= 2;
+  return s;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ host side
+
+// H = X A^T as fp32 [M, r] (single split: written directly).
+hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int64_t r,
+                            float* H, float* scratch, hipStream_t s) {
+  SRowsBf16<128> la;
+  la.src = X; la.ld = K; la.red = (int)K; la.vec = true;
+  SRowsBf16<64> lb;
+  lb.src = A; lb.ld = K; lb.red = (int)K; lb.vec = true;
+  const int64_t ksteps = K / BK;
+  const int splits = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), ksteps);
+  float* out = splits == 1 ? H : scratch;
+  hipError_t e = launch_skinny<128, 64>(la, lb, M, r, K, splits, out, s);
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(M * r, 256)), dim3(256), 0, s, scratch, splits,
+                     (int64_t)(M * r), 1.0f, (uint16_t*)nullptr, H);
+  return hipGetLastError();
+}
+
+size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r) {
+  const int splits = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), K / BK);
+  return splits == 1 ? 0 : (size_t)splits * M * r * sizeof(float);
+}
+
+hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
+  FwdGemmParams p;
+  p.X = a.X;
+  p.M = a.M;
+  p.N = a.N;
+  p.K = a.K;
+  p.r = (int)a.r;
+  p.codes = a.w.codes;
+  p.c2 = a.w.c2;
+  p.c1 = a.w.c1;
+  p.mean = a.w.mean;
+  p.H = a.H;
+  p.B = a.B;
+  p.b_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
+  p.scale = a.scale;
+  p.Y = a.Y;
+  p.tab = nf4_table();
+  hipLaunchKernelGGL(fwd_gemm_kernel, dim3(cdiv(a.N, FBN), cdiv(a.M, FBM)), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+// Backward workspace: H (if recomputed), dH, and split-K partials.
+struct BwdPlan {
+  int s_dh, s_db, s_da;
+  size_t off_H, off_dH, off_part, bytes;
+};
+
+static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
+  BwdPlan b;
+  b.s_dh = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), (N + BK - 1) / BK);
+  b.s_db = pick_splits((int64_t)cdiv(N, 128) * cdiv(r, 64), (M + BK - 1) / BK);
+  b.s_da = pick_splits((int64_t)cdiv(r, 64) * cdiv(K, 128), (M + BK - 1) / BK);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  b.off_H = 0;
+  b.off_dH = al((size_t)M * r * 4);
+  b.off_part = b.off_dH + al((size_t)M * r * 4);
+  size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * r, (size_t)b.s_da * r * K}) * 4;
+  part = std::max(part, lora_down_scratch_bytes(M, K, r));
+  b.bytes = b.off_part + al(part);
+  return b;
+}
+
+size_t gemm_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  return bwd_plan(M, N, K, r).bytes;
+}
+
+hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
+  const BwdPlan plan = bwd_plan(a.M, a.N, a.K, a.r);
+  char* ws = reinterpret_cast<char*>(a.workspace);
+  float* H = const_cast<float*>(a.H);
+  float* dH = reinterpret_cast<float*>(ws + plan.off_dH);
+  float* part = reinterpret_cast<float*>(ws + plan.off_part);
+  hipError_t e;
+  if (a.M > 0 && !H) {
+    H = reinterpret_cast<float*>(ws + plan.off_H);
+    if ((e = launch_lora_down(a.X, a.M, a.K, a.A, a.r, H, part, s)) != hipSuccess) return e;
+  }
+  const bool n_vec = (a.N % 8) == 0;
+  const bool r_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
+  // dH = s dY B : rows m, cols j, reduction n
+  if (a.M > 0) {
+    SRowsBf16<128> la;
+    la.src = a.dY; la.ld = a.N; la.red = (int)a.N; la.vec = n_vec;
+    SColsBf16<64> lb;
+    lb.src = a.B; lb.ld = a.r; lb.red = (int)a.N; lb.vec = r_vec;
+    if ((e = launch_skinny<128, 64>(la, lb, a.M, a.r, a.N, plan.s_dh, part, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.M * a.r, 256)), dim3(256), 0, s, part, plan.s_dh,
+                       (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
+  }
+  // dB = s dY^T H : rows n, cols j, reduction m
+  {
+    SColsBf16<128> la;
+    la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
+    SColsF32<64> lb;
+    lb.src = H; lb.ld = a.r; lb.red = (int)a.M; lb.scale = 1.0f;
+    if ((e = launch_skinny<128, 64>(la, lb, a.N, a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, part, plan.s_db,
+                       (int64_t)(a.N * a.r), a.scale, a.dB, (float*)nullptr);
+  }
+  // dA = dH^T X : rows j, cols k, reduction m
+  {
+    SColsF32<64> la;
+    la.src = dH; la.ld = a.r; la.red = (int)a.M; la.scale = 1.0f;
+    SColsBf16<128> lb;
+    lb.src = a.X; lb.ld = a.K; lb.red = (int)a.M; lb.vec = true;
+    if ((e = launch_skinny<64, 128>(la, lb, a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.r * a.K, 256)), dim3(256), 0, s, part, plan.s_da,
+                       (int64_t)(a.r * a.K), 1.0f, a.dA, (float*)nullptr);
+  }
+  // dX = dY W_deq + dH A
+  if (a.dX && a.M > 0) {
+    DxParams p;
+    p.dY = a.dY;
+    p.M = a.M;
+    p.N = a.N;
+    p.K = a.K;
+    p.r = (int)a.r;
+    p.codes = a.w.codes;
+    p.c2 = a.w.c2;
+    p.c1 = a.w.c1;
+    p.mean = a.w.mean;
+    p.dH = dH;
+    p.A = a.A;
+    p.dX = a.dX;
+    p.tab = nf4_table();
+    hipLaunchKernelGGL(dx_gemm_kernel, dim3(cdiv(a.K, FBN), cdiv(a.M, FBM)), dim3(NT), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qlora

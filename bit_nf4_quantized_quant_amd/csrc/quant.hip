@@ -1,0 +1,210 @@
+// Blockwise NF4 quantization, double quantization of the constants and
+// standalone dequantization to bf16 (gfx950).
+//
+// itwiki "QLoRA", NF4 section: each run of 64 weights is divided by its
+// absmax and every quotient is replaced by the index of the nearest of the 16
+// NF4 levels.  Double quantization section: the absmax constants are centred
+// on their mean and stored as 8-bit floats in runs of 256, with one fp32
+// constant per run.  Section on the computation: doubleDequant gives the bf16
+// weight used by the matrix products.
+//
+// All three passes stream HBM once with 16-byte vector accesses; none of them
+// needs a matrix core.
+#include "common.h"
+#include "exact_mean.h"
+#include "launch.h"
+
+namespace qlora {
+namespace {
+
+// ------------------------------------------------------------------ quantize
+//
+// One thread per float4: 16 consecutive lanes hold one 64-element block.  The
+// block absmax is a 4-step xor-shuffle reduction inside the 16-lane group; the
+// quotient uses IEEE fp32 division and the level index is the count of
+// thresholds at or below it.  Codes leave as one 16-bit store per thread
+// (4 nibbles), i.e. 128 contiguous bytes per wave.
+__global__ void __launch_bounds__(256) nf4_quantize_kernel(const float4* __restrict__ W,
+                                                           uint64_t n_vec4,
+                                                           uint16_t* __restrict__ codes,
+                                                           float* __restrict__ absmax,
+                                                           Nf4Table tab) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec4; i += stride) {
+    const float4 w = W[i];
+    float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    a = fmaxf(a, __shfl_xor(a, 8));
+    uint32_t packed;
+    if (a > 0.0f) {
+      const uint32_t c0 = nf4_code(w.x / a, tab);
+      const uint32_t c1 = nf4_code(w.y / a, tab);
+      const uint32_t c2 = nf4_code(w.z / a, tab);
+      const uint32_t c3 = nf4_code(w.w / a, tab);
+      packed = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
+    } else {
+      packed = 0x7777u;  // the zero level
+    }
+    codes[i] = (uint16_t)packed;
+    if ((threadIdx.x & 15) == 0) absmax[i >> 4] = a;
+  }
+}
+
+// ------------------------------------------------------------------ double quant
+
+// Zero the global mean buckets (a fill kernel, so the pass stays capturable).
+__global__ void dq_zero_kernel(unsigned long long* buckets) {
+  buckets[threadIdx.x] = 0ull;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Exact per-exponent mantissa sums.  A wave handles 64 constants at a time:
+// it repeatedly takes the exponent of the first pending lane, sums the
+// mantissas of all lanes with that exponent and adds the sum to an LDS bucket,
+// so there is one LDS atomic per distinct exponent per wave (a handful).
+__global__ void __launch_bounds__(256) dq_bucket_kernel(const float* __restrict__ absmax, uint64_t n,
+                                                        unsigned long long* __restrict__ buckets) {
+  __shared__ unsigned long long lb[kMeanBuckets];
+  lb[threadIdx.x] = 0ull;
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  for (uint64_t base = (uint64_t)blockIdx.x * 256 + wave * 64; base < n; base += stride) {
+    const uint64_t i = base + lane;
+    const bool valid = i < n;
+    const uint32_t bits = valid ? __float_as_uint(absmax[i]) : 0u;
+    const uint32_t e = (bits >> 23) & 0xFFu;
+    const uint32_t b = e ? e : 1u;
+    const unsigned long long m = (bits & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+    bool pending = valid && m != 0ull;
+    while (true) {
+      const unsigned long long mask = __ballot(pending);
+      if (mask == 0ull) break;
+      const int leader = __builtin_ctzll(mask);
+      const uint32_t eb = __shfl(b, leader);
+      const bool mine = pending && b == eb;
+      const unsigned long long s = wave_sum_u64(mine ? m : 0ull);
+      if (lane == 0) atomicAdd(&lb[eb], s);
+      pending = pending && !mine;
+    }
+  }
+  __syncthreads();
+  const unsigned long long v = lb[threadIdx.x];
+  if (v) atomicAdd(&buckets[threadIdx.x], v);
+}
+
+__global__ void dq_mean_kernel(const unsigned long long* __restrict__ buckets, uint64_t n,
+                               float* __restrict__ mean) {
+  if (threadIdx.x == 0) mean[0] = __uint_as_float(mean_from_buckets(buckets, n));
+}
+
+// One workgroup per run of 256 constants: centre on the mean, find the run's
+// largest magnitude, scale to +-448 and round to E4M3.
+__global__ void __launch_bounds__(256) dq_encode_kernel(const float* __restrict__ absmax, uint64_t n,
+                                                        const float* __restrict__ mean,
+                                                        uint8_t* __restrict__ c2,
+                                                        float* __restrict__ c1) {
+  __shared__ float wmax[4];
+  const uint64_t i = (uint64_t)blockIdx.x * kDqBlock + threadIdx.x;
+  const bool valid = i < n;
+  const float mu = mean[0];
+  const float x = valid ? __fsub_rn(absmax[i], mu) : 0.0f;
+  float m = fabsf(x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float scale = amax / 448.0f;
+  uint32_t code = 0u;
+  if (scale > 0.0f) code = f32_to_e4m3(x / scale);
+  if (valid) c2[i] = (uint8_t)code;
+  if (threadIdx.x == 0) c1[blockIdx.x] = scale;
+}
+
+// ------------------------------------------------------------------ dequant
+//
+// One thread per 16 bytes of codes (32 weights, half a block); the level table
+// sits in LDS (16 banks, no conflicts) and the output leaves as four 16-byte
+// stores.
+__global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint4* __restrict__ codes, uint64_t n_units,
+                                                          const uint8_t* __restrict__ c2,
+                                                          const float* __restrict__ c1,
+                                                          const float* __restrict__ mean,
+                                                          uint4* __restrict__ out, Nf4Table tab) {
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
+  __syncthreads();
+  const float mu = mean[0];
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units; u += stride) {
+    const uint64_t blk = u >> 1;
+    const float chat = dequant_constant(c2[blk], c1[blk >> 8], mu);
+    const uint4 q = codes[u];
+    const uint32_t words[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      const uint32_t w = words[wi];
+      uint4 o;
+      uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float lo = __fmul_rn(lut[(w >> (8 * p)) & 15u], chat);
+        const float hi = __fmul_rn(lut[(w >> (8 * p + 4)) & 15u], chat);
+        op[p] = pack_bf16x2(lo, hi);
+      }
+      out[u * 4 + wi] = o;
+    }
+  }
+}
+
+unsigned grid_for(uint64_t work_items, unsigned per_block, unsigned cap) {
+  uint64_t g = (work_items + per_block - 1) / per_block;
+  if (g > cap) g = cap;
+  return g ? (unsigned)g : 1u;
+}
+
+}  // namespace
+
+hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                               hipStream_t s) {
+  const uint64_t n_vec4 = (uint64_t)N * (uint64_t)K / 4;
+  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(W), n_vec4, reinterpret_cast<uint16_t*>(codes),
+                     absmax, nf4_table());
+  return hipGetLastError();
+}
+
+size_t double_quant_workspace_bytes() { return kMeanBuckets * sizeof(unsigned long long); }
+
+hipError_t launch_double_quant(const float* absmax, int64_t n, uint8_t* c2, float* c1, float* mean,
+                               void* workspace, hipStream_t s) {
+  auto* buckets = reinterpret_cast<unsigned long long*>(workspace);
+  hipLaunchKernelGGL(dq_zero_kernel, dim3(1), dim3(kMeanBuckets), 0, s, buckets);
+  hipLaunchKernelGGL(dq_bucket_kernel, dim3(grid_for((uint64_t)n, 256 * 8, 2048)), dim3(256), 0, s,
+                     absmax, (uint64_t)n, buckets);
+  hipLaunchKernelGGL(dq_mean_kernel, dim3(1), dim3(64), 0, s, buckets, (uint64_t)n, mean);
+  const uint64_t nb = ((uint64_t)n + kDqBlock - 1) / kDqBlock;
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)nb), dim3(256), 0, s, absmax, (uint64_t)n, mean,
+                     c2, c1);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
+                              int64_t N, int64_t K, uint16_t* out, hipStream_t s) {
+  const uint64_t n_units = (uint64_t)N * (uint64_t)K / 32;
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(n_units, 256, 65536)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(codes), n_units, c2, c1, mean,
+                     reinterpret_cast<uint4*>(out), nf4_table());
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -1,0 +1,174 @@
+/*
+ * qlora.h -- C ABI of libqlora.so: the QLoRA NF4 quantized linear layer on one
+ * AMD MI355X (gfx950).
+ *
+ * The layer (itwiki "QLoRA", section on the computation; minnong511
+ * "quantization", the boxed y = W x + (alpha/r) B A x equation):
+ *
+ *     Y = X * W_deq^T + s * (X * A^T) * B^T,      s = alpha / r
+ *     W_deq = doubleDequant(c1, c2, W_nf4)        (bf16)
+ *
+ * with X [M,K], W [N,K] (out x in), A [r,K], B [N,r] (kdkrkwhr "LoRA vs
+ * Q-LoRA", section 1: B is d x r, A is r x k).  The frozen base weight is kept
+ * as 4-bit NormalFloat codes in blocks of 64 with one absmax constant per block
+ * (itwiki "QLoRA", NF4 section); the constants are double-quantized: centred
+ * on their tensor mean and stored as E4M3 bytes in blocks of 256, one fp32
+ * scale per block (itwiki "QLoRA", double quantization section).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to row-major, contiguous storage.
+ *     bf16 values are passed as uint16_t bit patterns.  Sizes are element
+ *     counts (int64_t).
+ *   - The caller allocates and owns every buffer (inputs, outputs and the
+ *     workspaces sized by the *_workspace helpers).  The library never
+ *     allocates, frees or synchronizes; it validates arguments on the host and
+ *     queues kernels on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Return value: QLORA_OK or an error code.  On an error nothing has been
+ *     queued.  Faults inside kernels surface at the caller's next
+ *     synchronization, as for any HIP kernel.
+ *   - Inputs must be finite; non-finite inputs give unspecified results.
+ *   - Zero-sized problems (N, M or K equal to 0, as allowed per entry point)
+ *     are accepted and queue nothing.
+ *   - Alignment: pointers to fp32/bf16 matrices and to the packed codes must be
+ *     16-byte aligned; absmax, c1, mean and H need 4-byte alignment; c2 and B
+ *     need only their natural alignment.
+ *   - Calls are thread-safe and keep no state between calls, except the
+ *     forward/backward workspaces, which the kernels leave ready for reuse.
+ *     Two calls that share a workspace must not run concurrently.
+ *
+ * Storage of one quantized weight W [N,K] (P = N*K, K % 64 == 0):
+ *   codes  uint8 [N, K/2]       code of element 2i in the low nibble of byte i,
+ *                               element 2i+1 in the high nibble
+ *   absmax float [P/64]         first-level constants (input to double quant)
+ *   c2     uint8 [P/64]         E4M3 (OCP e4m3fn) code of (absmax - mean)/c1
+ *   c1     float [ceil(P/16384)] second-level fp32 constant per 256 c2 values
+ *   mean   float [1]            tensor mean of absmax (device memory)
+ * Block b covers elements [64b, 64b+64) of row-major W, so every block lies in
+ * one row; c2[b] belongs to c1[b / 256].
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_OK 0
+#define QLORA_EINVAL 1  /* null pointer, negative size, misaligned pointer, workspace too small */
+#define QLORA_ESHAPE 2  /* K % 64 != 0, r outside [1,128], sizes past the supported range */
+#define QLORA_EHIP 3    /* the HIP runtime rejected a launch (hipGetLastError) */
+
+/* Human-readable name of a status code (static string). */
+const char* qlora_status_str(int status);
+
+/*
+ * Host-only.  Storage sizes of a quantized [N,K] weight: packed code bytes,
+ * number of c2 bytes (= absmax floats) and number of c1 floats.  Any output
+ * pointer may be NULL.  Returns QLORA_ESHAPE if K % 64 != 0.
+ */
+int qlora_nf4_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* n_c2, int64_t* n_c1);
+
+/*
+ * Host-only.  Copies the library's 16 NF4 levels (fp32, ascending, code i ->
+ * levels[i]) into host memory `levels16`.  The table is built from the
+ * quantile construction on the itwiki "QLoRA" page (NF4 section): standard
+ * normal quantiles at 8 probabilities spaced evenly from 0.5 (excluded) to the
+ * offset 0.9677083 for the positive half, 7 for the negative half, an exact 0,
+ * normalized by the largest magnitude.
+ */
+int qlora_nf4_levels(float* levels16);
+
+/*
+ * Blockwise NF4 quantization (itwiki "QLoRA", NF4 section; minnong511
+ * "quantization", block-wise quantization).
+ *   W      in   fp32 [N,K]      weights (16-B aligned)
+ *   codes  out  uint8 [N,K/2]   packed codes (16-B aligned)
+ *   absmax out  fp32 [N*K/64]   max |w| of each 64-element block
+ * Each element becomes the index of the level nearest to fp32(w / absmax)
+ * (IEEE division; an exact tie goes to the lower level); a block with absmax
+ * 0 stores code 7 (the zero level).  N >= 0; K >= 0 with K % 64 == 0.
+ */
+int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                       void* stream);
+
+/* Workspace bytes needed by qlora_double_quant for n_c2 constants. */
+size_t qlora_double_quant_workspace(int64_t n_c2);
+
+/*
+ * Double quantization of the absmax constants (itwiki "QLoRA", double
+ * quantization section).
+ *   absmax    in   fp32 [n_c2]
+ *   c2        out  uint8 [n_c2]          E4M3 codes
+ *   c1        out  fp32 [ceil(n_c2/256)]  per-256 scale amax/448
+ *   mean      out  fp32 [1]              the exact mean of absmax rounded once to fp32
+ *   workspace      scratch of qlora_double_quant_workspace(n_c2) bytes (8-B aligned),
+ *                  contents on entry do not matter
+ * With x = fp32(absmax - mean): c1_b = fp32(max_b |x| / 448); c2 = e4m3(fp32(x / c1_b)),
+ * round to nearest even, saturating at +-448; a block whose c1 is 0 stores 0.
+ */
+int qlora_double_quant(const float* absmax, int64_t n_c2, uint8_t* c2, float* c1, float* mean,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Standalone dequantization to bf16 (itwiki "QLoRA", section on the
+ * computation: doubleDequant; irregular6612 "QLoRA - Efficient Finetuning of
+ * Quantized LLMs": the base weight is dequantized to bf16 before merging).
+ *   W_bf16 out  bf16 [N,K]:  W_deq = bf16( fp32( L[code] * c_hat ) ),
+ *   c_hat = fp32( fp32( e4m3(c2) * c1 ) + mean )   (no fused multiply-add).
+ */
+int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
+                      int64_t N, int64_t K, uint16_t* W_bf16, void* stream);
+
+/* Workspace bytes needed by qlora_linear_fwd. */
+size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
+
+/*
+ * Forward of the QLoRA linear (itwiki "QLoRA", section on the computation;
+ * minnong511 "quantization", y = W x + (alpha/r) B A x).
+ *   X      in   bf16 [M,K]       activations (16-B aligned)
+ *   codes, c2, c1, mean          the quantized weight W [N,K] (see above)
+ *   A      in   bf16 [r,K]       LoRA down factor (16-B aligned)
+ *   B      in   bf16 [N,r]       LoRA up factor
+ *   r, alpha                     rank (1..128) and LoRA alpha; s = alpha / r in fp32
+ *   Y      out  bf16 [M,N]       Y = bf16( X W_deq^T + s H B^T ), fp32 accumulation
+ *   H_out  out  fp32 [M,r]       H = X A^T (may be NULL; keep it for the backward)
+ *   workspace                    qlora_linear_fwd_workspace(M,N,K,r) bytes,
+ *                                256-B aligned, zero-filled once before first use;
+ *                                every call leaves it zero-filled again
+ * Requires K % 64 == 0.
+ */
+int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                     const uint8_t* c2, const float* c1, const float* mean, const uint16_t* A,
+                     const uint16_t* B, int64_t r, float alpha, uint16_t* Y, float* H_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by qlora_linear_bwd. */
+size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
+
+/*
+ * Backward of the QLoRA linear for the input and the LoRA factors; the NF4
+ * weight is frozen and gets no gradient (itwiki "QLoRA", section on the
+ * computation; minnong511 "quantization", backward: W not updated, A and B
+ * get gradients).  With H = X A^T and s = alpha / r:
+ *   dH = s dY B      dB = s dY^T H      dA = dH^T X      dX = dY W_deq + dH A
+ *   dY  in   bf16 [M,N];  X in bf16 [M,K]
+ *   H   in   fp32 [M,r] from the forward, or NULL to recompute it
+ *   dX  out  bf16 [M,K] (may be NULL to skip the input gradient)
+ *   dA  out  bf16 [r,K];  dB out bf16 [N,r]
+ *   workspace  qlora_linear_bwd_workspace(M,N,K,r) bytes, 256-B aligned
+ *              (contents on entry do not matter)
+ */
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N, int64_t K,
+                     const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
+                     const uint16_t* A, const uint16_t* B, int64_t r, float alpha, const float* H,
+                     uint16_t* dX, uint16_t* dA, uint16_t* dB, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,156 @@
+"""Host-side checks of libqlora.so: it loads, exports every entry point that
+include/qlora.h declares, and rejects bad arguments before touching a GPU.
+
+No call here reaches a kernel launch: each one fails host validation first
+(null or misaligned pointers, bad shapes, small workspaces), so these tests
+run on a machine without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_nf4_quantized_quant_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libqlora.so not built")
+
+A16 = 0x10000      # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10002      # misaligned fake address
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared()
+    assert len(names) == 11
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings():
+    for s in range(4):
+        assert _lib.status_str(s).startswith("QLORA")
+    assert "unknown" in _lib.status_str(99)
+
+
+def test_sizes():
+    assert _lib.qlora_nf4_sizes(4096, 4096) == (4096 * 2048, 262144, 1024)
+    assert _lib.qlora_nf4_sizes(22016, 8192) == (22016 * 4096, 2818048, 11008)
+    assert _lib.qlora_nf4_sizes(1, 64) == (32, 1, 1)
+    L = _lib.lib()
+    assert L.qlora_nf4_sizes(4, 65, None, None, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_nf4_sizes(-1, 64, None, None, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_sizes(0, 0, None, None, None) == _lib.QLORA_OK
+
+
+def test_library_levels_match_oracle_table():
+    import oracle
+    lv = np.array(_lib.qlora_nf4_levels(), dtype=np.float32)
+    assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels_f32().view(np.uint32))
+
+
+def test_quantize_validation():
+    L = _lib.lib()
+    assert L.qlora_nf4_quantize(None, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(A16, 4, 64, None, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(MIS, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(A16, 4, 64, MIS, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(A16, 4, 96, A16, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_nf4_quantize(A16, -4, 64, A16, A16, None) == _lib.QLORA_EINVAL
+    # empty problems are accepted and queue nothing
+    assert L.qlora_nf4_quantize(None, 0, 64, None, None, None) == _lib.QLORA_OK
+    assert L.qlora_nf4_quantize(None, 8, 0, None, None, None) == _lib.QLORA_OK
+
+
+def test_double_quant_validation():
+    L = _lib.lib()
+    need = L.qlora_double_quant_workspace(1000)
+    assert need >= 256 * 8
+    assert L.qlora_double_quant(A16, 1000, A16, A16, A16, A16, need - 1, None) == _lib.QLORA_EINVAL
+    assert L.qlora_double_quant(None, 1000, A16, A16, A16, A16, need, None) == _lib.QLORA_EINVAL
+    assert L.qlora_double_quant(A16, 1000, A16, A16, A16, None, need, None) == _lib.QLORA_EINVAL
+    assert L.qlora_double_quant(A16 + 2, 1000, A16, A16, A16, A16, need, None) == _lib.QLORA_EINVAL
+    assert L.qlora_double_quant(A16, -1, A16, A16, A16, A16, need, None) == _lib.QLORA_EINVAL
+    assert L.qlora_double_quant(None, 0, None, None, None, None, 0, None) == _lib.QLORA_OK
+
+
+def test_dequant_validation():
+    L = _lib.lib()
+    assert L.qlora_nf4_dequant(None, A16, A16, A16, 4, 64, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_dequant(A16, A16, A16, A16, 4, 64, MIS, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_dequant(A16, A16, A16, A16, 4, 100, A16, None) == _lib.QLORA_ESHAPE
+
+
+def _fwd(L, **kw):
+    a = dict(X=A16, M=4, N=64, K=64, codes=A16, c2=A16, c1=A16, mean=A16, A=A16, B=A16, r=8, alpha=16.0,
+             Y=A16, H=None, ws=A16, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = L.qlora_linear_fwd_workspace(max(a["M"], 0), max(a["N"], 0), max(a["K"], 0),
+                                                min(max(a["r"], 1), 128))
+    return L.qlora_linear_fwd(a["X"], a["M"], a["N"], a["K"], a["codes"], a["c2"], a["c1"], a["mean"],
+                              a["A"], a["B"], a["r"], a["alpha"], a["Y"], a["H"], a["ws"], a["wsb"], None)
+
+
+def test_fwd_validation():
+    L = _lib.lib()
+    assert _fwd(L, K=96) == _lib.QLORA_ESHAPE
+    assert _fwd(L, K=0) == _lib.QLORA_ESHAPE
+    assert _fwd(L, r=0) == _lib.QLORA_ESHAPE
+    assert _fwd(L, r=129) == _lib.QLORA_ESHAPE
+    assert _fwd(L, M=-1) == _lib.QLORA_EINVAL
+    assert _fwd(L, X=None) == _lib.QLORA_EINVAL
+    assert _fwd(L, X=MIS) == _lib.QLORA_EINVAL
+    assert _fwd(L, codes=MIS) == _lib.QLORA_EINVAL
+    assert _fwd(L, mean=None) == _lib.QLORA_EINVAL
+    assert _fwd(L, ws=None) == _lib.QLORA_EINVAL
+    assert _fwd(L, ws=A16 + 16) == _lib.QLORA_EINVAL          # workspace must be 256-B aligned
+    assert _fwd(L, wsb=1) == _lib.QLORA_EINVAL
+    assert _fwd(L, H=A16 + 2) == _lib.QLORA_EINVAL
+    assert _fwd(L, M=0, X=None, Y=None) == _lib.QLORA_OK     # empty batch queues nothing
+    assert _fwd(L, N=0) == _lib.QLORA_OK
+    assert L.qlora_linear_fwd_workspace(4, 64, 96, 8) == 0   # invalid shapes report 0
+    # decode-sized and large batches both need a workspace
+    assert L.qlora_linear_fwd_workspace(1, 4096, 4096, 64) > 256
+    assert L.qlora_linear_fwd_workspace(4096, 22016, 8192, 64) >= 4096 * 64 * 4
+
+
+def test_bwd_validation():
+    L = _lib.lib()
+    need = L.qlora_linear_bwd_workspace(32, 64, 128, 8)
+    assert need >= 2 * 32 * 8 * 4
+
+    def call(**kw):
+        a = dict(dY=A16, X=A16, M=32, N=64, K=128, codes=A16, c2=A16, c1=A16, mean=A16, A=A16, B=A16, r=8,
+                 alpha=16.0, H=None, dX=A16, dA=A16, dB=A16, ws=A16, wsb=need)
+        a.update(kw)
+        return L.qlora_linear_bwd(a["dY"], a["X"], a["M"], a["N"], a["K"], a["codes"], a["c2"], a["c1"],
+                                  a["mean"], a["A"], a["B"], a["r"], a["alpha"], a["H"], a["dX"], a["dA"],
+                                  a["dB"], a["ws"], a["wsb"], None)
+
+    assert call(K=100) == _lib.QLORA_ESHAPE
+    assert call(r=200) == _lib.QLORA_ESHAPE
+    assert call(dY=None) == _lib.QLORA_EINVAL
+    assert call(dA=None) == _lib.QLORA_EINVAL
+    assert call(dB=None) == _lib.QLORA_EINVAL
+    assert call(dX=MIS) == _lib.QLORA_EINVAL
+    assert call(wsb=need - 1) == _lib.QLORA_EINVAL
+    assert call(N=0) == _lib.QLORA_OK
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.lib()

@@ -1,0 +1,255 @@
+"""GPU parity: libqlora.so (through the C ABI) against the CPU oracle.
+
+Integer and byte results (packed codes, absmax, c2, c1, the mean, the bf16
+dequantized weight) must match bit for bit.  Floating-point layer outputs
+(Y, H, dX, dA, dB) must meet the tolerance in gpu_util (relative Frobenius
+error <= 5e-3, max error <= 2e-2 x RMS).  Every input comes from the seeded
+generators in ``synth``; every expected value comes from ``oracle``.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bf16_f64, check_close, dev_bf16, dev_f32, host, host_bf16_bits
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - the GPU suite runs on the GPU machine
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bit_nf4_quantized_quant_amd as qa  # noqa: E402  (raises if libqlora.so is missing)
+
+qa.lib()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gpu_quantize(W):
+    q = qa.quantize(dev_f32(W))
+    torch.cuda.synchronize()
+    return q
+
+
+def check_quantized(q, ref, rows=None):
+    N, K = q.N, q.K
+    codes = host(q.codes)
+    if rows is None:
+        assert np.array_equal(codes, ref["codes"]), "packed codes differ"
+    else:
+        assert np.array_equal(codes[rows], ref["codes"]), "packed codes differ (sampled rows)"
+    assert np.array_equal(host(q.absmax).view(np.uint32), ref["absmax"].view(np.uint32)), "absmax differs"
+    assert host(q.mean).view(np.uint32)[0] == np.float32(ref["mu"]).view(np.uint32), \
+        f"mean differs: {host(q.mean)[0]!r} vs {ref['mu']!r}"
+    assert np.array_equal(host(q.c1).view(np.uint32)[:ref["c1"].size], ref["c1"].view(np.uint32)), "c1 differs"
+    assert np.array_equal(host(q.c2), ref["c2"]), "c2 differs"
+
+
+def special_weight(N, K, seed):
+    """N(0, 0.02) weights plus the degenerate cases of blockwise NF4."""
+    W = synth.normal_f32(seed, (N, K), 0.02)
+    L = oracle.nf4_levels_f32()
+    W[0, :64] = 0.0                                      # all-zero block -> code 7, absmax 0
+    if K >= 128:
+        W[0, 64] = 1.0                                   # block max 1: quotients equal the weights
+        mids = [(float(L[j]) + float(L[j + 1])) / 2 for j in range(15)]
+        exact = [np.float32(m) for m in mids if float(np.float32(m)) == m]
+        W[0, 65:65 + len(exact)] = exact                 # exact ties -> lower level
+        W[0, 80] = -0.0
+        W[0, 81] = np.float32(1e-40)                     # fp32 subnormal
+    if N > 1:
+        W[1, :64] = -np.abs(W[1, :64])                   # negative block maximum
+        W[1, 5] = np.float32(3e30)                       # huge outlier
+    return W
+
+
+# ------------------------------------------------------------------ quantize / double quant / dequant
+
+@pytest.mark.parametrize("N,K", [(256, 256), (1, 64), (5, 192), (17, 1024), (300, 832)])
+def test_quantize_and_double_quant_bitexact(N, K):
+    say(f"[quantize] N={N} K={K}")
+    W = special_weight(N, K, seed=N * 7 + K)
+    ref = oracle.quantize_layer(W)
+    check_quantized(gpu_quantize(W), ref)
+
+
+def test_quantize_decode_layer_bitexact():
+    say("[quantize] decode layer 4096x4096")
+    W = synth.normal_f32(synth.SEED_W, (4096, 4096), 0.02)
+    check_quantized(gpu_quantize(W), oracle.quantize_layer(W))
+
+
+def test_quantize_constant_constants_and_zero_weight():
+    # every block has the same absmax -> centred constants are all 0 -> c1 = 0, c2 = 0
+    W = np.zeros((8, 256), np.float32)
+    W[:, ::64] = 0.5
+    ref = oracle.quantize_layer(W)
+    assert np.all(ref["c1"] == 0)
+    check_quantized(gpu_quantize(W), ref)
+    Z = np.zeros((4, 128), np.float32)
+    check_quantized(gpu_quantize(Z), oracle.quantize_layer(Z))
+
+
+@pytest.mark.parametrize("N,K", [(256, 256), (5, 192), (33, 1088)])
+def test_dequant_bitexact(N, K):
+    W = special_weight(N, K, seed=3 * N + K)
+    W[1, 5] = 0.1
+    q = gpu_quantize(W)
+    ref = oracle.quantize_layer(W)
+    wd = qa.dequantize(q)
+    torch.cuda.synchronize()
+    exp = oracle.dequant_weight(ref["codes"], ref["c2"], ref["c1"], ref["mu"], N, K)
+    assert np.array_equal(host_bf16_bits(wd), exp)
+
+
+def test_e4m3_decode_every_code():
+    """Each finite E4M3 byte dequantizes to its exact value (level 1.0, c1 = 1, mean 0)."""
+    codes8 = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    N, K = codes8.size, 64
+    packed = torch.full((N, K // 2), 0xFF, dtype=torch.uint8, device="cuda")   # code 15 = +1.0
+    c2 = torch.from_numpy(codes8).cuda()
+    c1 = torch.ones(1, dtype=torch.float32, device="cuda")
+    mean = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    qa.qlora_nf4_dequant(packed, c2, c1, mean, N, K, out)
+    torch.cuda.synchronize()
+    got = bf16_f64(host_bf16_bits(out))
+    exp = oracle.e4m3_value(codes8)
+    assert np.array_equal(got[:, 0], exp) and np.all(got == got[:, :1])
+    # the sign of zero survives (0x80 -> -0.0)
+    assert np.signbit(got[list(codes8).index(0x80), 0])
+
+
+# ------------------------------------------------------------------ forward
+
+def oracle_layer(d, alpha, r):
+    ref = oracle.quantize_layer(d["W"])
+    N, K = d["W"].shape
+    wd = oracle.dequant_weight(ref["codes"], ref["c2"], ref["c1"], ref["mu"], N, K)
+    return ref, wd
+
+
+def run_fwd(d, q, alpha, r, ws=None):
+    X, A, B = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"])
+    Y, H = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)
+    torch.cuda.synchronize()
+    return Y, H
+
+
+FWD_CASES = [
+    # M, N, K, r   (decode path for M <= 16, tiled MFMA path above)
+    (16, 256, 256, 8), (1, 256, 256, 8), (4, 100, 320, 5), (3, 33, 64, 1), (16, 130, 192, 128),
+    (17, 130, 192, 16), (33, 257, 128, 1), (130, 300, 448, 72), (256, 512, 1024, 64), (64, 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r", FWD_CASES)
+def test_forward_parity(M, N, K, r):
+    say(f"[fwd] M={M} N={N} K={K} r={r}")
+    shape = synth.LayerShape("t", M=M, N=N, K=K, r=r, seed_offset=M * 1000 + N + K + r)
+    d = synth.make_layer(shape)
+    alpha = 16.0
+    ref, wd = oracle_layer(d, alpha, r)
+    q = gpu_quantize(d["W"])
+    Y, H = run_fwd(d, q, alpha, r)
+    Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y")
+    check_close(host(H), Hr, "H")
+
+
+def test_forward_special_cases():
+    M, N, K, r = 16, 192, 256, 8
+    for Mx in (M, 40):
+        d = synth.make_layer(synth.LayerShape("t", M=Mx, N=N, K=K, r=r, seed_offset=77 + Mx))
+        # B = 0: the plain dequantized product
+        d0 = dict(d, B=np.zeros_like(d["B"]))
+        ref, wd = oracle_layer(d0, 16.0, r)
+        Y, _ = run_fwd(d0, gpu_quantize(d0["W"]), 16.0, r)
+        Yr = bf16_f64(d0["X"]) @ bf16_f64(wd).T
+        check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (B=0)")
+        # W = 0: codes 7, constants 0 -> exactly the LoRA branch s (X A^T) B^T
+        dz = dict(d, W=np.zeros_like(d["W"]))
+        Y, _ = run_fwd(dz, gpu_quantize(dz["W"]), 16.0, r)
+        Yr = 2.0 * (bf16_f64(d["X"]) @ bf16_f64(d["A"]).T) @ bf16_f64(d["B"]).T
+        check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (W=0)")
+
+
+def test_forward_one_hot_rows_select_weight_columns():
+    """One-hot X rows with B = 0 reproduce columns of the dequantized weight."""
+    N, K, r = 128, 256, 8
+    for M in (4, 32, 64):
+        d = synth.make_layer(synth.LayerShape("t", M=M, N=N, K=K, r=r, seed_offset=5 + M))
+        X = np.zeros((M, K), np.float32)
+        cols = (np.arange(M) * 37) % K
+        X[np.arange(M), cols] = 1.0
+        d = dict(d, X=synth.f32_to_bf16_bits(X), B=np.zeros_like(d["B"]))
+        ref, wd = oracle_layer(d, 16.0, r)
+        Y, _ = run_fwd(d, gpu_quantize(d["W"]), 16.0, r)
+        got = host_bf16_bits(Y).astype(np.int32)
+        exp = wd[:, cols].T.astype(np.int32)
+        if M > 16:
+            assert np.array_equal(got, exp)          # tiled path multiplies the exact bf16 W_deq
+        else:
+            # the decode path scales hi+lo bf16 levels in fp32 after the product, so a
+            # value lying within 2^-17 of a bf16 rounding boundary may land one ulp over
+            assert np.max(np.abs(got - exp)) <= 1
+
+
+def test_forward_deterministic_and_workspace_reusable():
+    for M in (1, 16, 64):
+        d = synth.make_layer(synth.LayerShape("t", M=M, N=512, K=512, r=16, seed_offset=900 + M))
+        q = gpu_quantize(d["W"])
+        ws = qa.fwd_workspace(M, 512, 512, 16, "cuda")
+        Y1, H1 = run_fwd(d, q, 16.0, 16, ws)
+        Y2, H2 = run_fwd(d, q, 16.0, 16, ws)
+        assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+        assert torch.equal(H1, H2)
+        if M <= 16:
+            assert int(ws[:16].view(torch.int32)[:4].abs().sum()) == 0, "counters not reset"
+
+
+# ------------------------------------------------------------------ backward
+
+BWD_CASES = [(16, 256, 256, 8), (3, 100, 320, 5), (70, 130, 192, 16), (257, 300, 448, 72), (1, 64, 64, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,r", BWD_CASES)
+def test_backward_parity(M, N, K, r):
+    say(f"[bwd] M={M} N={N} K={K} r={r}")
+    shape = synth.LayerShape("t", M=M, N=N, K=K, r=r, seed_offset=31 * M + N + K + r)
+    d = synth.make_layer(shape, with_dy=True)
+    alpha = 16.0
+    ref, wd = oracle_layer(d, alpha, r)
+    g = oracle.linear_bwd(d["dY"], d["X"], wd, d["A"], d["B"], alpha, r)
+    q = gpu_quantize(d["W"])
+    X, A, B, dY = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"]), dev_bf16(d["dY"])
+    _, H = qa.linear_fwd(X, q, A, B, alpha)
+    for Hin in (H, None):
+        dX, dA, dB = qa.linear_bwd(dY, X, q, A, B, alpha, H=Hin)
+        torch.cuda.synchronize()
+        check_close(bf16_f64(host_bf16_bits(dX)), g["dX"], "dX")
+        check_close(bf16_f64(host_bf16_bits(dA)), g["dA"], "dA")
+        check_close(bf16_f64(host_bf16_bits(dB)), g["dB"], "dB")
+    _, dA2, dB2 = qa.linear_bwd(dY, X, q, A, B, alpha, H=H, want_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dA2.view(torch.int16), dA.view(torch.int16))
+    assert torch.equal(dB2.view(torch.int16), dB.view(torch.int16))
+
+
+def test_backward_empty_batch_gives_zero_lora_grads():
+    N, K, r = 64, 128, 8
+    d = synth.make_layer(synth.LayerShape("t", M=1, N=N, K=K, r=r, seed_offset=4242))
+    q = gpu_quantize(d["W"])
+    X = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    dY = torch.zeros((0, N), dtype=torch.bfloat16, device="cuda")
+    A, B = dev_bf16(d["A"]), dev_bf16(d["B"])
+    dX, dA, dB = qa.linear_bwd(dY, X, q, A, B, 16.0)
+    torch.cuda.synchronize()
+    assert dX.numel() == 0
+    assert float(dA.float().abs().sum()) == 0.0 and float(dB.float().abs().sum()) == 0.0
