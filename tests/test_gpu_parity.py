@@ -119,11 +119,14 @@ def test_e4m3_decode_every_code():
     out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     qa.qlora_nf4_dequant(packed, c2, c1, mean, N, K, out)
     torch.cuda.synchronize()
-    got = bf16_f64(host_bf16_bits(out))
+    got_bits = host_bf16_bits(out)
+    got = bf16_f64(got_bits)
     exp = oracle.e4m3_value(codes8)
     assert np.array_equal(got[:, 0], exp) and np.all(got == got[:, :1])
-    # the sign of zero survives (0x80 -> -0.0)
-    assert np.signbit(got[list(codes8).index(0x80), 0])
+    # bit patterns too, through the oracle's own dequantization (-0 * 1 + 0 = +0)
+    ref = oracle.dequant_weight(np.full((N, K // 2), 0xFF, np.uint8), codes8, np.ones(1, np.float32),
+                                np.float32(0.0), N, K)
+    assert np.array_equal(got_bits, ref)
 
 
 # ------------------------------------------------------------------ forward
