@@ -1,0 +1,344 @@
+"""Benchmark of the QLoRA NF4 linear on one MI355X.
+
+Headline (the `value` of the JSON line): forward HBM throughput at M = 1 on
+the 4096 x 4096 decode layer (NF4 weight + double-quantized constants, LoRA
+r = 64, alpha = 16), with inputs resident in HBM and the weights rotated over
+enough distinct copies (> 512 MB) that every call streams its weight from HBM
+rather than from the 256 MB Infinity Cache.  A step is one forward call of the
+layer (one kernel launch); the timed steps are captured in a HIP graph and
+replayed once between HIP events, so host launch cost stays out of the figure.
+
+Also measured in the same run and reported under "extra": M = 4 and 16 on the
+decode layer, the Llama-7B MLP shapes at M = 1, the 65B-scale training layer
+(22016 x 8192, M = 4096) forward and backward in TFLOP/s, and quantize +
+double quant throughput.  The CPU oracle is timed on a bounded sample of the
+headline workload (`cpu_baseline`).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd: HBM GB/s at M=1, TFLOP/s at M=4096 (% of peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, public spec
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, public spec
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+def weight_bytes(N, K):
+    """Packed codes + c2 + c1 + mean of one quantized weight."""
+    n_c2 = N * K // 64
+    return N * K // 2 + n_c2 + 4 * ((n_c2 + 255) // 256) + 4
+
+
+def fwd_bytes(M, N, K, r):
+    """Algorithmic HBM bytes of one forward: W once, X, Y, A, B in bf16 once each."""
+    return weight_bytes(N, K) + 2 * M * K + 2 * M * N + 2 * r * K + 2 * N * r
+
+
+def fwd_flops(M, N, K, r):
+    return 2 * M * N * K + 2 * M * r * (K + N)
+
+
+def bwd_flops(M, N, K, r):
+    # dX main + H recompute-free: dH (2MNr), dB (2MNr), dA (2MrK), dX LoRA (2MrK), dX main (2MNK)
+    return 2 * M * N * K + 4 * M * N * r + 4 * M * r * K
+
+
+def bwd_bytes(M, N, K, r):
+    return weight_bytes(N, K) + 2 * M * N + 2 * M * K * 2 + 4 * M * r + 2 * r * K * 2 + 2 * N * r * 2
+
+
+# ----------------------------------------------------------------------------- GPU helpers
+
+def make_layer_gpu(torch, qa, N, K, r, copies, seed):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    W = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    q = qa.quantize(W)
+    del W
+    A = (torch.randn((r, K), generator=gen, device="cuda") / K).to(torch.bfloat16)
+    B = (torch.randn((N, r), generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    sets = []
+    for i in range(copies):
+        qi = qa.QuantizedWeight(N, K, q.codes.clone(), q.absmax, q.c2.clone(), q.c1.clone(), q.mean.clone())
+        sets.append((qi, A.clone(), B.clone()))
+    torch.cuda.synchronize()
+    return sets
+
+
+def timed_graph(torch, fn, steps, warmup):
+    """Run fn(i) warmup times eagerly, capture `steps` calls in one graph, replay it
+    between events; returns ms per call."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()                      # one untimed replay
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def timed_eager(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_fwd(torch, qa, M, N, K, r, steps, warmup, copies, seed=0, graph=True):
+    sets = make_layer_gpu(torch, qa, N, K, r, copies, seed)
+    xs = [torch.randn((M, K), device="cuda").to(torch.bfloat16) for _ in range(copies)]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    H = torch.empty((M, r), dtype=torch.float32, device="cuda")
+    ws = qa.fwd_workspace(M, N, K, r, "cuda")
+
+    def call(i):
+        q, A, B = sets[i % copies]
+        qa.qlora_linear_fwd(xs[i % copies], q.codes, q.c2, q.c1, q.mean, A, B, 16.0, Y, H, ws, N)
+
+    ms = (timed_graph if graph else timed_eager)(torch, call, steps, warmup)
+    byts = fwd_bytes(M, N, K, r)
+    fl = fwd_flops(M, N, K, r)
+    del sets, xs
+    return {"M": M, "N": N, "K": K, "r": r, "ms": ms, "GBps": byts / ms / 1e6, "TFLOPs": fl / ms / 1e9,
+            "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS, "mfma_frac": fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "bytes": byts, "flops": fl, "copies": copies}
+
+
+def bench_bwd(torch, qa, M, N, K, r, steps, warmup, seed=0):
+    sets = make_layer_gpu(torch, qa, N, K, r, 1, seed)
+    q, A, B = sets[0]
+    X = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+    dY = torch.randn((M, N), device="cuda").to(torch.bfloat16)
+    H = torch.empty((M, r), dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws_f = qa.fwd_workspace(M, N, K, r, "cuda")
+    qa.qlora_linear_fwd(X, q.codes, q.c2, q.c1, q.mean, A, B, 16.0, Y, H, ws_f, N)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(qa.qlora_linear_bwd_workspace(M, N, K, r), dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        qa.qlora_linear_bwd(dY, X, q.codes, q.c2, q.c1, q.mean, A, B, 16.0, H, dX, dA, dB, ws)
+
+    ms = timed_eager(torch, call, steps, warmup)
+    fl = bwd_flops(M, N, K, r)
+    return {"M": M, "N": N, "K": K, "r": r, "ms": ms, "TFLOPs": fl / ms / 1e9,
+            "mfma_frac": fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
+
+
+def bench_quantize(torch, qa, N, K, steps, warmup):
+    W = torch.randn((N, K), device="cuda", dtype=torch.float32) * 0.02
+    code_bytes, n_c2, n_c1 = qa.qlora_nf4_sizes(N, K)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    absmax = torch.empty(n_c2, dtype=torch.float32, device="cuda")
+    c2 = torch.empty(n_c2, dtype=torch.uint8, device="cuda")
+    c1 = torch.empty(n_c1, dtype=torch.float32, device="cuda")
+    mean = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qa.qlora_double_quant_workspace(n_c2), dtype=torch.uint8, device="cuda")
+    ms_q = timed_eager(torch, lambda i: qa.qlora_nf4_quantize(W, codes, absmax), steps, warmup)
+    ms_dq = timed_eager(torch, lambda i: qa.qlora_double_quant(absmax, c2, c1, mean, ws), steps, warmup)
+    qbytes = N * K * 4 + N * K // 2 + 4 * n_c2
+    return {"N": N, "K": K, "quantize_ms": ms_q, "quantize_GBps": qbytes / ms_q / 1e6,
+            "quantize_hbm_frac": qbytes / ms_q / 1e6 / HBM_PEAK_GBS, "double_quant_ms": ms_dq,
+            "double_quant_GBps": (5 * n_c2 + 4 * n_c1) / ms_dq / 1e6}
+
+
+# ----------------------------------------------------------------------------- traffic from counters
+
+def kernel_source_hash(name):
+    with open(os.path.join(ROOT, "bit_nf4_quantized_quant_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(summary_name, source_name):
+    """HBM bytes per launch recorded in a profiles/ summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", summary_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]+)", text)
+    m_traf = re.search(r"HBM traffic per launch \(bytes\):\s*([0-9.e+]+)", text)
+    if not m_hash or not m_traf or m_hash.group(1) != kernel_source_hash(source_name):
+        return None
+    return float(m_traf.group(1))
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle's forward on a bounded sample of the headline workload:
+    rows of the 4096x4096 decode layer at M = 1, timed single-threaded."""
+    import numpy as np
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    import synth
+
+    shape = synth.DECODE[0]
+    d = synth.make_layer(shape)
+    q = oracle.quantize_layer(d["W"])
+    rows_per = 256
+    rng = np.random.default_rng(0)
+    done_rows = 0
+    t_total = 0.0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        while t_total < budget_s:
+            rows = np.sort(rng.choice(shape.N, rows_per, replace=False))
+            t0 = time.perf_counter()
+            wd = oracle.dequant_weight(q["codes"], q["c2"], q["c1"], q["mu"], shape.N, shape.K, rows=rows)
+            oracle.linear_fwd(d["X"], wd, d["A"], d["B"][rows], shape.alpha, shape.r)
+            t_total += time.perf_counter() - t0
+            done_rows += rows_per
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    frac = done_rows / shape.N
+    byts = fwd_bytes(shape.M, shape.N, shape.K, shape.r) * frac
+    return {"value": byts / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_rows} output rows (in blocks of {rows_per}) of decode_4096x4096_m1, "
+                      f"oracle dequant + fp64 forward, {t_total:.1f} s single-threaded; bytes scaled "
+                      f"by the row fraction"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import bit_nf4_quantized_quant_amd as qa
+    qa.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
+
+    N, K, r = 4096, 4096, 64
+    copies = max(2, int(2 * MALL_BYTES / fwd_bytes(1, N, K, r)) + 1)
+    log(f"[bench] decode fwd M=1 {N}x{K} r={r}: {copies} weight copies, {args.steps} steps")
+    head = bench_fwd(torch, qa, 1, N, K, r, args.steps, args.warmup, copies)
+    log(f"[bench] M=1: {head['ms'] * 1e3:.2f} us/call, {head['GBps']:.0f} GB/s")
+
+    if args.copy_calibration:
+        a = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    extra = {}
+    if not args.quick:
+        for M in (4, 16):
+            res = bench_fwd(torch, qa, M, N, K, r, args.steps, args.warmup, copies)
+            extra[f"decode_4096x4096_m{M}"] = res
+            log(f"[bench] M={M}: {res['ms'] * 1e3:.2f} us/call, {res['GBps']:.0f} GB/s")
+        for nm, n, k in (("mlp_gate_up_11008x4096", 11008, 4096), ("mlp_down_4096x11008", 4096, 11008)):
+            cp = max(2, int(2 * MALL_BYTES / fwd_bytes(1, n, k, r)) + 1)
+            res = bench_fwd(torch, qa, 1, n, k, r, args.steps, args.warmup, cp)
+            extra[f"{nm}_m1"] = res
+            log(f"[bench] {nm} M=1: {res['ms'] * 1e3:.2f} us/call, {res['GBps']:.0f} GB/s")
+        Ml, Nl, Kl = 4096, 22016, 8192
+        res = bench_fwd(torch, qa, Ml, Nl, Kl, r, 10, 2, 3, graph=False)
+        extra["train65b_22016x8192_m4096_fwd"] = res
+        log(f"[bench] 65B layer fwd M=4096: {res['ms']:.3f} ms, {res['TFLOPs']:.0f} TFLOP/s")
+        res = bench_bwd(torch, qa, Ml, Nl, Kl, r, 5, 1)
+        extra["train65b_22016x8192_m4096_bwd"] = res
+        log(f"[bench] 65B layer bwd M=4096: {res['ms']:.3f} ms, {res['TFLOPs']:.0f} TFLOP/s")
+        res = bench_quantize(torch, qa, Nl, Kl, 5, 1)
+        extra["quantize_22016x8192"] = res
+        log(f"[bench] quantize: {res['quantize_GBps']:.0f} GB/s, double quant {res['double_quant_ms'] * 1e3:.1f} us")
+        torch.cuda.empty_cache()
+
+    traffic = recorded_traffic("qlora_decode_kernel_decode_4096x4096_m1.md", "decode.hip")
+    line = {
+        "metric": METRIC,
+        "value": round(head["GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_4096x4096_m1", "M": 1, "N": N, "K": K, "r": r, "alpha": 16.0,
+                   "weight": "NF4 block 64 + E4M3 double quant block 256", "parallelism": "single GPU",
+                   "cold_cache_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(head["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["hbm_frac"], 4), "traffic": traffic},
+    }
+    if "train65b_22016x8192_m4096_fwd" in extra:
+        f = extra["train65b_22016x8192_m4096_fwd"]
+        line["m4096"] = {"workload": "train65b_22016x8192_m4096_fwd", "TFLOPs": round(f["TFLOPs"], 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(f["mfma_frac"], 4), "ms": f["ms"]}
+    if not args.no_cpu:
+        log("[bench] cpu oracle baseline ...")
+        line["cpu_baseline"] = cpu_baseline()
+    line["extra"] = extra
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

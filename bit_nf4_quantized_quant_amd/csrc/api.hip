@@ -48,9 +48,18 @@ int check_weight(const uint8_t* codes, const uint8_t* c2, const float* c1, const
   return QLORA_OK;
 }
 
+// Forward workspace: the decode kernel keeps its launch counters in the first
+// kFwdReserved bytes whatever M is, so one workspace can serve both paths.
+constexpr size_t kFwdReserved = 2048;
+
+bool use_decode(int64_t M, int64_t N, int64_t K) {
+  // the decode kernel addresses the codes with 32-bit byte offsets
+  return M <= kDecodeMaxM && N * K / 2 < (int64_t(1) << 31);
+}
+
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
-  if (M <= kDecodeMaxM) return round256(decode_workspace_bytes(M, r));
-  return round256((size_t)M * r * sizeof(float)) + round256(lora_down_scratch_bytes(M, K, r));
+  if (use_decode(M, N, K)) return round256(decode_workspace_bytes(M, r));
+  return kFwdReserved + round256((size_t)M * r * sizeof(float)) + round256(lora_down_scratch_bytes(M, K, r));
 }
 
 }  // namespace
@@ -153,8 +162,8 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
   a.H = H_out;
   a.workspace = workspace;
   hipStream_t s = (hipStream_t)stream;
-  if (M <= kDecodeMaxM) return status_of(launch_decode_fwd(a, s));
-  char* ws = reinterpret_cast<char*>(workspace);
+  if (use_decode(M, N, K)) return status_of(launch_decode_fwd(a, s));
+  char* ws = reinterpret_cast<char*>(workspace) + kFwdReserved;
   float* H = H_out ? H_out : reinterpret_cast<float*>(ws);
   float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
   a.H = H;

@@ -33,8 +33,8 @@
  *     16-byte aligned; absmax, c1, mean and H need 4-byte alignment; c2 and B
  *     need only their natural alignment.
  *   - Calls are thread-safe and keep no state between calls, except the
- *     forward/backward workspaces, which the kernels leave ready for reuse.
- *     Two calls that share a workspace must not run concurrently.
+ *     launch counters the forward keeps in its workspace.  Two calls that
+ *     share a workspace must not run concurrently.
  *
  * Storage of one quantized weight W [N,K] (P = N*K, K % 64 == 0):
  *   codes  uint8 [N, K/2]       code of element 2i in the low nibble of byte i,
@@ -136,8 +136,11 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  *   Y      out  bf16 [M,N]       Y = bf16( X W_deq^T + s H B^T ), fp32 accumulation
  *   H_out  out  fp32 [M,r]       H = X A^T (may be NULL; keep it for the backward)
  *   workspace                    qlora_linear_fwd_workspace(M,N,K,r) bytes,
- *                                256-B aligned, zero-filled once before first use;
- *                                every call leaves it zero-filled again
+ *                                256-B aligned, zero-filled once before its first
+ *                                use.  The library keeps launch counters in it
+ *                                between calls (any shapes may share one workspace
+ *                                as long as it is large enough); do not modify it,
+ *                                and zero it again after a call that faulted.
  * Requires K % 64 == 0.
  */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
