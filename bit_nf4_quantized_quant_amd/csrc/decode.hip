@@ -15,23 +15,26 @@
 //     quarter of K, giving partial sums of H = X A^T.  They never wait.
 //   * The remaining workgroups are weight tiles: 16 output rows, all of K,
 //     split over the 8 waves of the workgroup.  Each 64-element NF4 block is
-//     one scaling unit: the levels enter bf16 16x16x32 MFMAs as a hi + lo pair
-//     (together exact to ~2^-17) and the block's fp32 constant c_hat scales
-//     the block's partial product in fp32 afterwards.  Loads use buffer
+//     one scaling unit: the levels enter bf16 16x16x32 MFMAs as bf16(level)
+//     and the block's fp32 constant c_hat scales the block's partial product
+//     in fp32 afterwards, i.e. the weight used is bf16(level) * c_hat rather
+//     than bf16(level * c_hat): the same size of rounding, one place earlier.
+//     A byte of two codes indexes a table of bf16 pairs in LDS (32 copies, one
+//     per lane%32, so lookups never conflict on a bank).  Loads use buffer
 //     instructions with immediate offsets; rows past N read as zero.
-//   * A weight tile then waits (bounded spin) until the LoRA-down partials of
-//     this launch are published, sums them into H, adds s H B^T in fp32 and
+//   * A weight tile then polls (bounded spin) until the LoRA-down partials of
+//     this launch are present, sums them into H, adds s H B^T in fp32 and
 //     stores bf16 Y.  Workgroups are dispatched in index order, so the
 //     LoRA-down tiles are running or done before any weight tile waits.
 //
-// Launch epochs instead of counter resets: every launch adds exactly 2^20 to
-// each counter it uses, however many workgroups share the counter.  A weight
-// tile's own counter update returns (epoch << 20) + something < 2^20, which
-// names the epoch; the partials of this launch are complete once the
-// LoRA-down counter reaches (epoch + 1) << 20.  Weight tiles spread their
-// updates over 8 counters so no address sees more than ~1/8 of them.  The
-// counter updates are issued at the start and their results are only needed
-// at the wait, so their latency hides behind the weight stream.
+// Launch epochs: every launch adds exactly 2^20 to each counter it uses,
+// however many workgroups share the counter, so a workgroup's own counter
+// update returns (epoch << 20) + something < 2^20, which names the launch.
+// LoRA-down tiles store each partial as one 64-bit word (epoch tag, value),
+// so a partial is valid exactly when its tag is this launch's; nothing has to
+// be reset or waited for on the producer side.  Weight tiles spread their
+// counter updates over 8 counters, issue them first and use the result only
+// at the poll, so the update latency hides behind the weight stream.
 #include "common.h"
 #include "launch.h"
 
@@ -41,15 +44,16 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 16;          // output rows per weight tile
-constexpr int kLutCopies = 16;     // pair table replicated per lane%16
+constexpr int kLutCopies = 32;     // pair table replicated per lane%32
 constexpr int kHSplit = 4;         // K slices per LoRA-down row group
 constexpr int kSlots = 8;          // weight-tile epoch counters
 constexpr uint64_t kEpoch = uint64_t(1) << 20;
-constexpr unsigned kSpinLimit = 1u << 24;
+constexpr unsigned kSpinLimit = 1u << 20;  // ~50 ms per polled word, a safety net only
 constexpr int kXLdsBytes = 16384;  // X staged in LDS when M*K*2 fits
 
 // Workspace layout (bytes): [0] LoRA-down counter (u64), [128*(1+s)] weight
-// counter s (u64), [128*9] timeout flag (u32), [kHpartOff..] partial sums.
+// counter s (u64), [128*9] timeout flag (u32), [kHpartOff..] tagged partial
+// sums (u64: tag << 32 | fp32 bits).
 constexpr size_t kHpartOff = 2048;
 
 struct DecodeParams {
@@ -67,11 +71,13 @@ struct DecodeParams {
   float scale;
   uint16_t* Y;
   float* H;        // H [M, r] for the caller, or null
-  float* Hpart;    // [kHSplit][M][r16] partial sums (r16 = r rounded up to 16)
+  uint64_t* Hpart; // [kHSplit][M][r16] tagged partial sums (r16 = r rounded up to 16)
   char* ws;
   int n_htiles;
   int n_wtiles;
-  Nf4HiLo hilo;
+  int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
+  int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
+  uint32_t hi[16]; // bf16(level) per code
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -88,13 +94,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_b
 
 // Cross-workgroup data (H partials, counters) moves only through relaxed
 // agent-scope atomics, which are coherent across the XCDs' separate L2 caches
-// on their own.  Ordering comes from waiting for this thread's stores to
-// complete (s_waitcnt 0) before a barrier and the counter update, so no L2
+// on their own; each partial carries its launch tag in the same 64-bit word,
+// so no ordering between separate stores is needed and no L2
 // write-back/invalidate fence is ever issued.
-__device__ __forceinline__ void st_shared_f32(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_tagged(uint64_t* p, uint32_t tag, float v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_shared_f32(const float* p) {
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_ctr(const uint64_t* p) {
@@ -103,7 +109,6 @@ __device__ __forceinline__ uint64_t ld_ctr(const uint64_t* p) {
 __device__ __forceinline__ uint64_t add_ctr(uint64_t* p, uint64_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
 // i-th of n equal integer shares of 2^20 (the shares add up to exactly 2^20)
 __device__ __forceinline__ uint64_t epoch_share(uint32_t i, uint32_t n) {
@@ -116,7 +121,8 @@ __device__ __forceinline__ uint64_t epoch_share(uint32_t i, uint32_t n) {
 // carry copies of row M-1; their outputs are discarded.
 constexpr int kHBatch = 8;
 
-__device__ void lora_down_tile(const DecodeParams& p, int tile, float* red) {
+// ticket: thread 0's LoRA-down counter update (its epoch names this launch).
+__device__ void lora_down_tile(const DecodeParams& p, int tile, float* red, uint32_t* tag_lds, uint64_t ticket) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rg = tile / kHSplit, ks = tile % kHSplit;
   const int j0 = rg * kRows;
@@ -146,6 +152,7 @@ __device__ void lora_down_tile(const DecodeParams& p, int tile, float* red) {
   // acc[v] = partial H[m = 4g + v][j0 + jl]; reduce over the waves
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave * 256 + (4 * g + v) * 16 + jl] = acc[v];
+  if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
   __syncthreads();
   if (threadIdx.x < 256) {
     const int m = threadIdx.x >> 4, jj = threadIdx.x & 15;
@@ -153,7 +160,7 @@ __device__ void lora_down_tile(const DecodeParams& p, int tile, float* red) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sum += red[w * 256 + threadIdx.x];
     const int r16 = (p.r + 15) & ~15;
-    if (m < p.M) st_shared_f32(&p.Hpart[((size_t)ks * p.M + m) * r16 + j0 + jj], sum);
+    if (m < p.M) st_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j0 + jj], *tag_lds, sum);
   }
 }
 
@@ -165,8 +172,8 @@ constexpr int kBatch = 4;
 template <bool kXLds>
 struct BlockLoads {
   u32x2 cw[kBatch];  // 8 code bytes per block (this lane's 16 elements)
-  uint32_t c2[kBatch];
-  float c1[kBatch];
+  uint32_t c2w;      // the 4 E4M3 constants of the batch's blocks, one byte each
+  float c1a, c1b;    // second-level constants of the batch's first and last block
   u32x4 x0[kBatch], x1[kBatch];  // only when X is read from global memory
 };
 
@@ -177,21 +184,33 @@ struct WeightCtx {
   uint32_t x_off;      // byte offset of this lane's X row at k = 16g
   const char* xs;      // X in LDS (bytes) or null
   int b_end;
+  int c2_vec;
 };
 
+// One batch = kBatch (= 4) consecutive blocks of this lane's row, starting at
+// a multiple of 4 so that their c2 bytes form one aligned dword.  Few, wide
+// loads keep the texture-address unit from backing up.
 template <bool kXLds>
 __device__ __forceinline__ void load_blocks(const WeightCtx& c, BlockLoads<kXLds>& L, int b0) {
 #pragma unroll
   for (int i = 0; i < kBatch; ++i) {
     const uint32_t b = (uint32_t)min(b0 + i, c.b_end - 1);
     L.cw[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(c.rc, c.code_off + 32 * b, 0, 0));
-    L.c2[i] = __builtin_amdgcn_raw_buffer_load_b8(c.r2, c.blk0 + b, 0, 0);
-    L.c1[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.r1, ((c.blk0 + b) >> 8) * 4, 0, 0));
     if (!kXLds) {
       L.x0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.x_off + 128 * b, 0, 0));
       L.x1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.x_off + 128 * b + 16, 0, 0));
     }
   }
+  if (c.c2_vec) {
+    L.c2w = __builtin_amdgcn_raw_buffer_load_b32(c.r2, c.blk0 + (uint32_t)b0, 0, 0);
+  } else {
+    L.c2w = 0u;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      L.c2w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(c.r2, c.blk0 + (uint32_t)b0 + i, 0, 0) << (8 * i);
+  }
+  L.c1a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.r1, ((c.blk0 + b0) >> 8) * 4, 0, 0));
+  L.c1b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.r1, ((c.blk0 + b0 + kBatch - 1) >> 8) * 4, 0, 0));
 }
 
 template <bool kXLds>
@@ -200,27 +219,25 @@ __device__ __forceinline__ void mul_blocks(const WeightCtx& c, const BlockLoads<
 #pragma unroll
   for (int i = 0; i < kBatch; ++i) {
     if (b0 + i >= c.b_end) break;
-    const float chat = dequant_constant(L.c2[i], L.c1[i], mu);
+    const uint32_t blk = c.blk0 + (uint32_t)(b0 + i);
+    const float c1 = ((blk >> 8) == ((c.blk0 + b0) >> 8)) ? L.c1a : L.c1b;
+    const float chat = dequant_constant((L.c2w >> (8 * i)) & 0xFFu, c1, mu);
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t w = L.cw[i][h];
-      u32x4 whi, wlo;
+      u32x4 wv;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t byte = (w >> (8 * q)) & 0xFFu;
-        const uint2 e = *reinterpret_cast<const uint2*>(lutb + ((byte << 7) | cb));
-        whi[q] = e.x;
-        wlo[q] = e.y;
+        wv[q] = *reinterpret_cast<const uint32_t*>(lutb + ((byte << 7) | cb));
       }
       u32x4 xv;
       if (kXLds)
         xv = *reinterpret_cast<const u32x4*>(c.xs + c.x_off + 128 * (b0 + i) + 16 * h);
       else
         xv = h ? L.x1[i] : L.x0[i];
-      const bf16x8 xa = as_bf16x8(xv);
-      t = mfma16(xa, as_bf16x8(whi), t);
-      t = mfma16(xa, as_bf16x8(wlo), t);
+      t = mfma16(as_bf16x8(xv), as_bf16x8(wv), t);
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(chat, t[v], acc[v]);
@@ -228,25 +245,36 @@ __device__ __forceinline__ void mul_blocks(const WeightCtx& c, const BlockLoads<
 }
 
 template <bool kXLds>
-__device__ void weight_tile(const DecodeParams& p, int tile, const uint2* lut, const char* xs, float* red,
-                            float* hs, float* bs, uint64_t ticket) {
+// ticket: thread 0's weight-counter update (its epoch names this launch).
+__device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char* xs, uint32_t* words, float* red,
+                            float* hs, float* bs, uint32_t* tag_lds, uint64_t ticket) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = tile * kRows;
   const int nl = lane & 15, g = lane >> 4;
   const int nblk = p.K / 64;
   const float mu = *p.mean;
-  const uint32_t cb = (uint32_t)(lane & 15) * 8u;  // this lane's table copy (bytes)
+  const uint32_t cb = (uint32_t)(lane & 31) * 4u;  // this lane's table copy (bytes)
   const char* lutb = reinterpret_cast<const char*>(lut);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  // rows n0..n0+15 of B: issued now, parked in LDS after the weight stream
-  constexpr int kBPer = 16 * 128 / kThreads;
+  // rows n0..n0+15 of B (16 x r bf16, contiguous): issued now as 16-byte
+  // chunks, parked in LDS after the weight stream (row stride r+1: no bank
+  // conflicts when the 16 rows are read together)
+  const int bs_ld = p.r + 1;
+  const int b_chunks = p.b_vec ? (16 * p.r) / 8 : 0;
+  const rsrc_t rb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
+  u32x4 bchunk = {0u, 0u, 0u, 0u};
+  if (threadIdx.x < b_chunks)
+    bchunk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ((uint32_t)n0 * p.r + 8 * threadIdx.x) * 2, 0, 0));
+  constexpr int kBPer = 16 * 128 / kThreads;   // element loads when B is not 16-byte friendly
   uint32_t bv[kBPer];
+  if (!p.b_vec) {
 #pragma unroll
-  for (int i = 0; i < kBPer; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    const int br = e / p.r, bc = e - br * p.r;
-    bv[i] = (e < 16 * p.r && n0 + br < p.N) ? p.B[(size_t)(n0 + br) * p.r + bc] : 0u;
+    for (int i = 0; i < kBPer; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int br = e / p.r, bc = e - br * p.r;
+      bv[i] = (e < 16 * p.r && n0 + br < p.N) ? p.B[(size_t)(n0 + br) * p.r + bc] : 0u;
+    }
   }
 
   WeightCtx c;
@@ -260,14 +288,53 @@ __device__ void weight_tile(const DecodeParams& p, int tile, const uint2* lut, c
   c.blk0 = row * (uint32_t)nblk;
   c.x_off = ((uint32_t)min(nl, p.M - 1) * p.K + 16u * g) * 2u;
   c.xs = xs;
-  const int per = (nblk + kWaves - 1) / kWaves;
-  const int b_beg = wave * per;
+  c.c2_vec = p.c2_vec;
+  // each wave takes a run of whole batches (multiples of 4 blocks)
+  const int per = ((nblk + kWaves - 1) / kWaves + kBatch - 1) / kBatch * kBatch;
+  const int b_beg = min(nblk, wave * per);
   c.b_end = min(nblk, b_beg + per);
-  if (b_beg < c.b_end) {
-    BlockLoads<kXLds> La, Lb;
+
+  // Put the first two batches of weight loads and the X loads in flight
+  // before building the code table, so a single memory round trip covers them.
+  BlockLoads<kXLds> La, Lb;
+  const bool work = b_beg < c.b_end;
+  if (work) {
     load_blocks(c, La, b_beg);
+    if (b_beg + kBatch < c.b_end) load_blocks(c, Lb, b_beg + kBatch);
+  }
+  constexpr int kXPer = kXLdsBytes / 16 / kThreads;
+  u32x4 xv[kXPer];
+  const int n16 = p.M * p.K / 8;  // 16-byte chunks of X
+  if (kXLds) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int j = threadIdx.x + i * kThreads;
+      if (j < n16) xv[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * j);
+    }
+  }
+  // pair table: entry for code byte e is bf16(level[e & 15]) | bf16(level[e >> 4]) << 16,
+  // one copy per lane%32 (entry stride 128 bytes)
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) words[i] = p.hi[i];   // constant indices: scalar kernel-argument reads
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256 * kLutCopies; i += kThreads) {
+    const int e = i >> 5;
+    lut[i] = words[e & 15] | (words[e >> 4] << 16);
+  }
+  if (kXLds) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int j = threadIdx.x + i * kThreads;
+      if (j < n16) reinterpret_cast<u32x4*>(xs)[j] = xv[i];
+    }
+  }
+  __syncthreads();
+
+  if (work) {
     for (int b0 = b_beg; b0 < c.b_end; b0 += 2 * kBatch) {
-      if (b0 + kBatch < c.b_end) load_blocks(c, Lb, b0 + kBatch);
+      if (b0 != b_beg && b0 + kBatch < c.b_end) load_blocks(c, Lb, b0 + kBatch);
       mul_blocks(c, La, b0, mu, lutb, cb, acc);
       if (b0 + 2 * kBatch < c.b_end) load_blocks(c, La, b0 + 2 * kBatch);
       if (b0 + kBatch < c.b_end) mul_blocks(c, Lb, b0 + kBatch, mu, lutb, cb, acc);
@@ -276,37 +343,49 @@ __device__ void weight_tile(const DecodeParams& p, int tile, const uint2* lut, c
   // acc[v] = partial Y0[m = 4g + v][n0 + nl]
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave * 256 + (4 * g + v) * 16 + nl] = acc[v];
+  if (threadIdx.x < b_chunks) {
+    const int e0 = 8 * threadIdx.x, br = e0 / p.r, bc = e0 - br * p.r;
 #pragma unroll
-  for (int i = 0; i < kBPer; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    if (e < 16 * p.r) bs[e] = __uint_as_float(bv[i] << 16);
-  }
-
-  // wait until this launch's LoRA-down partials are published
-  if (threadIdx.x == 0) {
-    const uint64_t target = ((ticket >> 20) + 1) << 20;
-    const uint64_t* hctr = reinterpret_cast<const uint64_t*>(p.ws);
-    unsigned spins = 0;
-    while (ld_ctr(hctr) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(reinterpret_cast<unsigned*>(p.ws + 128 * 9), 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
+    for (int q = 0; q < 4; ++q) {
+      bs[br * bs_ld + bc + 2 * q] = bf16_lo(bchunk[q]);
+      bs[br * bs_ld + bc + 2 * q + 1] = bf16_hi(bchunk[q]);
     }
   }
+  if (!p.b_vec) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int br = e / p.r, bc = e - br * p.r;
+      if (e < 16 * p.r) bs[br * bs_ld + bc] = __uint_as_float(bv[i] << 16);
+    }
+  }
+
+  // collect this launch's LoRA-down partials (tag = epoch + 1), polling until
+  // present; only thread 0 holds the counter update, so it shares the tag
+  if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
   __syncthreads();
+  const uint32_t tag = *tag_lds;
   {
     const int r16 = (p.r + 15) & ~15;
     for (int i = threadIdx.x; i < p.M * p.r; i += kThreads) {
       const int m = i / p.r, j = i - m * p.r;
-      float part[kHSplit];
-#pragma unroll
-      for (int ks = 0; ks < kHSplit; ++ks) part[ks] = ld_shared_f32(&p.Hpart[((size_t)ks * p.M + m) * r16 + j]);
       float h = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < kHSplit; ++ks) h += part[ks];
+      for (int ks = 0; ks < kHSplit; ++ks) {
+        const uint64_t* src = &p.Hpart[((size_t)ks * p.M + m) * r16 + j];
+        uint64_t v = ld_tagged(src);
+        unsigned spins = 0;
+        while ((uint32_t)(v >> 32) != tag) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > kSpinLimit) {
+            __hip_atomic_store(reinterpret_cast<unsigned*>(p.ws + 128 * 9), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          v = ld_tagged(src);
+        }
+        h += __uint_as_float((uint32_t)v);
+      }
       hs[i] = h;
       if (tile == 0 && p.H) p.H[i] = h;
     }
@@ -320,7 +399,7 @@ __device__ void weight_tile(const DecodeParams& p, int tile, const uint2* lut, c
     for (int w = 0; w < kWaves; ++w) y += red[w * 256 + threadIdx.x];
     const int n = n0 + nn;
     if (m < p.M && n < p.N) {
-      const float* brow = bs + nn * p.r;
+      const float* brow = bs + nn * bs_ld;
       const float* hrow = hs + m * p.r;
       float lora = 0.f;
       for (int j = 0; j < p.r; ++j) lora = __builtin_fmaf(hrow[j], brow[j], lora);
@@ -333,20 +412,20 @@ __device__ void weight_tile(const DecodeParams& p, int tile, const uint2* lut, c
 // Two 512-thread workgroups per CU (4 waves per SIMD): at most 128 VGPRs.
 template <bool kXLds>
 __global__ void __launch_bounds__(kThreads, 4) qlora_decode_kernel(DecodeParams p) {
-  __shared__ uint2 lut[256 * kLutCopies];       // 32 KiB
+  __shared__ uint32_t lut[256 * kLutCopies];    // 32 KiB
   __shared__ __attribute__((aligned(16))) char xs[kXLds ? kXLdsBytes : 16];
   __shared__ float red[kWaves * 256];           // 8 KiB
   __shared__ float hs[16 * 128];                // 8 KiB: H rows for the epilogue
-  __shared__ float bs[16 * 128];                // 8 KiB: B rows of the tile
+  __shared__ float bs[16 * 129];                // B rows of the tile, stride r+1
   __shared__ uint32_t words[16];
   const int tile = (int)blockIdx.x;
 
   if (tile < p.n_htiles) {
-    lora_down_tile(p, tile, red);
-    wait_stores();
-    __syncthreads();
+    __shared__ uint32_t htag;
+    uint64_t hticket = 0;
     if (threadIdx.x == 0)
-      add_ctr(reinterpret_cast<uint64_t*>(p.ws), epoch_share((uint32_t)tile, (uint32_t)p.n_htiles));
+      hticket = add_ctr(reinterpret_cast<uint64_t*>(p.ws), epoch_share((uint32_t)tile, (uint32_t)p.n_htiles));
+    lora_down_tile(p, tile, red, &htag, hticket);
     return;
   }
 
@@ -367,29 +446,15 @@ __global__ void __launch_bounds__(kThreads, 4) qlora_decode_kernel(DecodeParams 
     }
   }
 
-  // pair table: entry for code byte e holds the hi and lo bf16 pairs of
-  // (level[e & 15], level[e >> 4]), one copy per lane%16
-  if (threadIdx.x < 16) words[threadIdx.x] = p.hilo.word[threadIdx.x];
-  if (kXLds) {
-    const int n16 = p.M * p.K / 8;  // 16-byte chunks of X
-    for (int i = threadIdx.x; i < n16; i += kThreads)
-      reinterpret_cast<u32x4*>(xs)[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * i);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 256 * kLutCopies; i += kThreads) {
-    const int e = i >> 4;
-    const uint32_t w0 = words[e & 15], w1 = words[e >> 4];
-    lut[i] = make_uint2((w0 & 0xFFFFu) | (w1 << 16), (w0 >> 16) | (w1 & 0xFFFF0000u));
-  }
-  __syncthreads();
-  weight_tile<kXLds>(p, wt, lut, xs, red, hs, bs, ticket);
+  __shared__ uint32_t wtag;
+  weight_tile<kXLds>(p, wt, lut, xs, words, red, hs, bs, &wtag, ticket);
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int64_t M, int64_t r) {
   const int64_t r16 = (r + 15) & ~15;
-  return kHpartOff + (size_t)(kHSplit * M * r16) * sizeof(float);
+  return kHpartOff + (size_t)(kHSplit * M * r16) * sizeof(uint64_t);
 }
 
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
@@ -408,12 +473,15 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   p.scale = a.scale;
   p.Y = a.Y;
   p.ws = reinterpret_cast<char*>(a.workspace);
-  p.Hpart = reinterpret_cast<float*>(p.ws + kHpartOff);
+  p.Hpart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff);
   p.H = a.H;
   const int64_t r16 = (a.r + 15) & ~15;
   p.n_htiles = (int)(r16 / kRows) * kHSplit;
   p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
-  p.hilo = nf4_hilo();
+  p.c2_vec = (a.K % 256 == 0) && (reinterpret_cast<uintptr_t>(a.w.c2) % 4 == 0);
+  p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
+  const Nf4HiLo& hl = nf4_hilo();
+  for (int i = 0; i < 16; ++i) p.hi[i] = hl.word[i] & 0xFFFFu;
   const dim3 grid(p.n_htiles + p.n_wtiles);
   if ((size_t)a.M * a.K * 2 <= (size_t)kXLdsBytes)
     hipLaunchKernelGGL(qlora_decode_kernel<true>, grid, dim3(kThreads), 0, s, p);

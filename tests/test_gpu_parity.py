@@ -148,6 +148,8 @@ def run_fwd(d, q, alpha, r, ws=None):
 FWD_CASES = [
     # M, N, K, r   (decode path for M <= 16, tiled MFMA path above)
     (16, 256, 256, 8), (1, 256, 256, 8), (4, 100, 320, 5), (3, 33, 64, 1), (16, 130, 192, 128),
+    (2, 300, 1024, 16), (7, 129, 512, 24), (1, 1000, 2048, 64), (5, 77, 768, 12), (16, 64, 4096, 64),
+    (1, 96, 11008, 64), (12, 40, 1280, 40),
     (17, 130, 192, 16), (33, 257, 128, 1), (130, 300, 448, 72), (256, 512, 1024, 64), (64, 64, 64, 64),
 ]
 
@@ -226,6 +228,20 @@ def test_forward_deterministic_and_workspace_reusable():
                 assert torch.equal(H, first[key][1]), key
     # the decode kernel's bounded wait never timed out
     assert int(ws[128 * 9:128 * 9 + 4].view(torch.int32)[0]) == 0
+
+
+@pytest.mark.parametrize("shape", synth.DECODE, ids=lambda sh: sh.name)
+def test_forward_decode_layer_full_size(shape):
+    """The 4096 x 4096 decode layer at M = 1, 4, 16: every output against the oracle."""
+    say(f"[fwd full] {shape.name}")
+    d = synth.make_layer(shape)
+    ref, wd = oracle_layer(d, shape.alpha, shape.r)
+    q = gpu_quantize(d["W"])
+    check_quantized(q, ref)
+    Y, H = run_fwd(d, q, shape.alpha, shape.r)
+    Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], shape.alpha, shape.r)
+    check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y")
+    check_close(host(H), Hr, "H")
 
 
 # ------------------------------------------------------------------ backward
