@@ -32,19 +32,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // --------------------------------------------------------------- E4M3 (OCP e4m3fn)
 
-// Exact decode of an E4M3 byte (never NaN here: the encoder saturates at 448).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t sign = (c & 0x80u) << 24;
-  const uint32_t e = (c >> 3) & 0xFu;
-  const uint32_t m = c & 0x7u;
-  float mag;
-  if (e == 0) {
-    mag = (float)m * 0.001953125f;  // m * 2^-9 (subnormal)
-  } else {
-    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
-  }
-  return __uint_as_float(__float_as_uint(mag) | sign);
+// Exact decode of an E4M3 byte: gfx950's v_cvt_f32_fp8 takes the OCP e4m3fn
+// format (bias 7, subnormals, max 448); every E4M3 value is exact in fp32.
+// `sel` picks the byte of `w` (a constant, encoded in the instruction).
+template <int sel>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, sel);
 }
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return e4m3_byte_to_f32<0>(c); }
 
 // fp32 -> E4M3 byte: round to nearest, ties to even, saturate to +-448, keep
 // the sign of zero.  Written on the fp32 bit pattern.
@@ -73,6 +69,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float t) {
 __device__ __forceinline__ float dequant_constant(uint32_t c2, float c1, float mean) {
   const float p = __fmul_rn(e4m3_to_f32(c2), c1);
   return __fadd_rn(p, mean);
+}
+
+// The same for byte `sel` of a word holding four c2 codes.
+template <int sel>
+__device__ __forceinline__ float dequant_constant_byte(uint32_t c2w, float c1, float mean) {
+  return __fadd_rn(__fmul_rn(e4m3_byte_to_f32<sel>(c2w), c1), mean);
 }
 
 __device__ __forceinline__ uint32_t nf4_code(float x, const Nf4Table& t) {

@@ -75,6 +75,7 @@ struct DecodeParams {
   char* ws;
   int n_htiles;
   int n_wtiles;
+  int epi_group;   // threads per output in the epilogue (power of two, <= 32)
   int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
   int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
   uint32_t hi[16]; // bf16(level) per code
@@ -221,7 +222,10 @@ __device__ __forceinline__ void mul_blocks(const WeightCtx& c, const BlockLoads<
     if (b0 + i >= c.b_end) break;
     const uint32_t blk = c.blk0 + (uint32_t)(b0 + i);
     const float c1 = ((blk >> 8) == ((c.blk0 + b0) >> 8)) ? L.c1a : L.c1b;
-    const float chat = dequant_constant((L.c2w >> (8 * i)) & 0xFFu, c1, mu);
+    const float chat = i == 0 ? dequant_constant_byte<0>(L.c2w, c1, mu)
+                     : i == 1 ? dequant_constant_byte<1>(L.c2w, c1, mu)
+                     : i == 2 ? dequant_constant_byte<2>(L.c2w, c1, mu)
+                              : dequant_constant_byte<3>(L.c2w, c1, mu);
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -294,14 +298,9 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
   const int b_beg = min(nblk, wave * per);
   c.b_end = min(nblk, b_beg + per);
 
-  // Put the first two batches of weight loads and the X loads in flight
-  // before building the code table, so a single memory round trip covers them.
-  BlockLoads<kXLds> La, Lb;
-  const bool work = b_beg < c.b_end;
-  if (work) {
-    load_blocks(c, La, b_beg);
-    if (b_beg + kBatch < c.b_end) load_blocks(c, Lb, b_beg + kBatch);
-  }
+  // X (for staging) first, then the first two batches of weight loads: loads
+  // complete in issue order, so staging X waits only for X, and the first
+  // batch can be multiplied while the second is still arriving.
   constexpr int kXPer = kXLdsBytes / 16 / kThreads;
   u32x4 xv[kXPer];
   const int n16 = p.M * p.K / 8;  // 16-byte chunks of X
@@ -311,6 +310,12 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
       const int j = threadIdx.x + i * kThreads;
       if (j < n16) xv[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * j);
     }
+  }
+  BlockLoads<kXLds> La, Lb;
+  const bool work = b_beg < c.b_end;
+  if (work) {
+    load_blocks(c, La, b_beg);
+    if (b_beg + kBatch < c.b_end) load_blocks(c, Lb, b_beg + kBatch);
   }
   // pair table: entry for code byte e is bf16(level[e & 15]) | bf16(level[e >> 4]) << 16,
   // one copy per lane%32 (entry stride 128 bytes)
@@ -332,14 +337,32 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
   }
   __syncthreads();
 
+  // LoRA-down partials this thread sums later: first read issued after the
+  // first batch is multiplied, so it travels while the rest is computed
+  constexpr int kHPer = 16 * 128 / kThreads;   // up to M*r = 2048 sums per tile
+  const int r16 = (p.r + 15) & ~15;
+  uint64_t hp[kHSplit];                         // early read of this thread's first sum
+  bool hp_issued = false;
+  auto issue_poll = [&]() {
+    const int i = threadIdx.x;
+    if (i < p.M * p.r) {
+      const int m = i / p.r, j = i - m * p.r;
+#pragma unroll
+      for (int ks = 0; ks < kHSplit; ++ks) hp[ks] = ld_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j]);
+    }
+    hp_issued = true;
+  };
+
   if (work) {
     for (int b0 = b_beg; b0 < c.b_end; b0 += 2 * kBatch) {
       if (b0 != b_beg && b0 + kBatch < c.b_end) load_blocks(c, Lb, b0 + kBatch);
       mul_blocks(c, La, b0, mu, lutb, cb, acc);
+      if (!hp_issued) issue_poll();
       if (b0 + 2 * kBatch < c.b_end) load_blocks(c, La, b0 + 2 * kBatch);
       if (b0 + kBatch < c.b_end) mul_blocks(c, Lb, b0 + kBatch, mu, lutb, cb, acc);
     }
   }
+  if (!hp_issued) issue_poll();
   // acc[v] = partial Y0[m = 4g + v][n0 + nl]
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave * 256 + (4 * g + v) * 16 + nl] = acc[v];
@@ -365,17 +388,18 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
   if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
   __syncthreads();
   const uint32_t tag = *tag_lds;
-  {
-    const int r16 = (p.r + 15) & ~15;
-    for (int i = threadIdx.x; i < p.M * p.r; i += kThreads) {
+#pragma unroll
+  for (int u = 0; u < kHPer; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i < p.M * p.r) {
       const int m = i / p.r, j = i - m * p.r;
       float h = 0.f;
 #pragma unroll
       for (int ks = 0; ks < kHSplit; ++ks) {
         const uint64_t* src = &p.Hpart[((size_t)ks * p.M + m) * r16 + j];
-        uint64_t v = ld_tagged(src);
+        uint64_t v = u == 0 ? hp[ks] : ld_tagged(src);
         unsigned spins = 0;
-        while ((uint32_t)(v >> 32) != tag) {
+        while ((uint32_t)(v >> 32) != tag) {   // not yet published: poll
           __builtin_amdgcn_s_sleep(2);
           if (++spins > kSpinLimit) {
             __hip_atomic_store(reinterpret_cast<unsigned*>(p.ws + 128 * 9), 1u, __ATOMIC_RELAXED,
@@ -392,24 +416,31 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
   }
   __syncthreads();
 
-  if (threadIdx.x < 256) {
-    const int m = threadIdx.x >> 4, nn = threadIdx.x & 15;
-    float y = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) y += red[w * 256 + threadIdx.x];
-    const int n = n0 + nn;
-    if (m < p.M && n < p.N) {
+  // epilogue: output o = m*16 + nn gets G threads (G = 512 / (16 M), capped at
+  // 32); each sums a share of the wave partials and of the r-long LoRA dot
+  // product, then the G lanes combine with xor shuffles
+  {
+    const int G = p.epi_group;
+    const int o = threadIdx.x / G, sub = threadIdx.x - o * G;
+    const bool valid = o < 16 * p.M;
+    float part = 0.f;
+    if (valid) {
+      const int m = o >> 4, nn = o & 15;
+      for (int w = sub; w < kWaves; w += G) part += red[w * 256 + o];
       const float* brow = bs + nn * bs_ld;
       const float* hrow = hs + m * p.r;
       float lora = 0.f;
-      for (int j = 0; j < p.r; ++j) lora = __builtin_fmaf(hrow[j], brow[j], lora);
-      y = __builtin_fmaf(p.scale, lora, y);
-      p.Y[(size_t)m * p.N + n] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
+      for (int j = sub; j < p.r; j += G) lora = __builtin_fmaf(hrow[j], brow[j], lora);
+      part = __builtin_fmaf(p.scale, lora, part);
+    }
+    for (int off = G >> 1; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    if (valid && sub == 0) {
+      const int m = o >> 4, n = n0 + (o & 15);
+      if (n < p.N) p.Y[(size_t)m * p.N + n] = (uint16_t)(pack_bf16x2(part, 0.f) & 0xFFFFu);
     }
   }
 }
 
-// Two 512-thread workgroups per CU (4 waves per SIMD): at most 128 VGPRs.
 template <bool kXLds>
 __global__ void __launch_bounds__(kThreads, 4) qlora_decode_kernel(DecodeParams p) {
   __shared__ uint32_t lut[256 * kLutCopies];    // 32 KiB
@@ -478,6 +509,9 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   const int64_t r16 = (a.r + 15) & ~15;
   p.n_htiles = (int)(r16 / kRows) * kHSplit;
   p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
+  int G = kThreads / (16 * (int)a.M);
+  G = G >= 32 ? 32 : (G >= 16 ? 16 : (G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1))));
+  p.epi_group = G;
   p.c2_vec = (a.K % 256 == 0) && (reinterpret_cast<uintptr_t>(a.w.c2) % 4 == 0);
   p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
   const Nf4HiLo& hl = nf4_hilo();
