@@ -47,9 +47,9 @@ __device__ __forceinline__ uint32_t hi16(uint32_t a, uint32_t b) { return (a >> 
 // ---------------------------------------------------------------- loaders
 
 // bf16 source, rows contiguous in the reduction index.
-template <int R>
+template <int R, int T = NT>
 struct RowsBf16 {
-  static constexpr int kChunks = R * BK / 8 / NT;  // 16-byte chunks per thread
+  static constexpr int kChunks = R * BK / 8 / T;  // 16-byte chunks per thread
   const uint16_t* src;
   int64_t ld;       // elements between rows
   int rows;         // valid rows from row0
@@ -58,10 +58,10 @@ struct RowsBf16 {
   bool vec;         // ld % 8 == 0 and 16-byte aligned base
   u32x4 reg[kChunks];
 
-  __device__ void load(int kt) {
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int idx = threadIdx.x + c * NT;
+      const int idx = threadIdx.x + c * T;
       const int rr = idx >> 3, ch = idx & 7;
       const int k = kt * BK + ch * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -79,19 +79,19 @@ struct RowsBf16 {
       reg[c] = v;
     }
   }
-  __device__ void store(lds_t* t) const {
+  __device__ __forceinline__ void store(lds_t* t) const {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int idx = threadIdx.x + c * NT;
+      const int idx = threadIdx.x + c * T;
       st_lds16(t + (idx >> 3) * PITCH + (idx & 7) * 8, reg[c]);
     }
   }
 };
 
 // fp32 source with rows contiguous in the reduction index, scaled and rounded to bf16.
-template <int R>
+template <int R, int T = NT>
 struct RowsF32 {
-  static constexpr int kChunks = R * BK / 8 / NT;
+  static constexpr int kChunks = R * BK / 8 / T;
   const float* src;
   int64_t ld;
   int rows;
@@ -100,10 +100,10 @@ struct RowsF32 {
   float scale;
   u32x4 reg[kChunks];
 
-  __device__ void load(int kt) {
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int idx = threadIdx.x + c * NT;
+      const int idx = threadIdx.x + c * T;
       const int rr = idx >> 3, ch = idx & 7;
       const int k = kt * BK + ch * 8;
       float f[8];
@@ -119,69 +119,74 @@ struct RowsF32 {
                      pack_bf16x2(f[6], f[7])};
     }
   }
-  __device__ void store(lds_t* t) const {
+  __device__ __forceinline__ void store(lds_t* t) const {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int idx = threadIdx.x + c * NT;
+      const int idx = threadIdx.x + c * T;
       st_lds16(t + (idx >> 3) * PITCH + (idx & 7) * 8, reg[c]);
     }
   }
 };
 
 // bf16 source stored [red][rows]: tile row i is source column col0 + i.
-template <int R>
+template <int R, int T = NT>
 struct ColsBf16 {
   static constexpr int kPatches = 2 * R;  // (BK/4) x (R/8) patches of 4 red x 8 cols
+  static constexpr int kPer = (kPatches + T - 1) / T;
   const uint16_t* src;
   int64_t ld;    // elements between source rows (reduction steps)
   int cols;      // valid tile rows (source columns) from col0
   int red;       // valid reduction length
   int64_t col0;
   bool vec;
-  u32x4 reg[4];
-  bool active;
+  u32x4 reg[kPer][4];
 
-  __device__ void load(int kt) {
-    const int pid = threadIdx.x;
-    active = pid < kPatches;
-    if (!active) return;
-    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
-    const int c = pc * 8;
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = kt * BK + pr * 4 + q;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k < red) {
-        const uint16_t* p = src + (int64_t)k * ld + col0 + c;
-        if (vec && c + 8 <= cols) {
-          v = ld16(p);
-        } else {
-          uint32_t e[8];
+    for (int u = 0; u < kPer; ++u) {
+      const int pid = threadIdx.x + u * T;
+      if (pid >= kPatches) break;
+      const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+      const int c = pc * 8;
 #pragma unroll
-          for (int z = 0; z < 8; ++z) e[z] = (c + z < cols) ? p[z] : 0u;
-          v = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+      for (int q = 0; q < 4; ++q) {
+        const int k = kt * BK + pr * 4 + q;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (k < red) {
+          const uint16_t* p = src + (int64_t)k * ld + col0 + c;
+          if (vec && c + 8 <= cols) {
+            v = ld16(p);
+          } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int z = 0; z < 8; ++z) e[z] = (c + z < cols) ? p[z] : 0u;
+            v = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+          }
         }
+        reg[u][q] = v;
       }
-      reg[q] = v;
     }
   }
-  __device__ void store(lds_t* t) const {
-    if (!active) return;
-    const int pid = threadIdx.x;
-    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+  __device__ __forceinline__ void store(lds_t* t) const {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // columns 2w (low halves) and 2w+1 (high halves)
-      const u32x2 a = {lo16(reg[0][w], reg[1][w]), lo16(reg[2][w], reg[3][w])};
-      const u32x2 b = {hi16(reg[0][w], reg[1][w]), hi16(reg[2][w], reg[3][w])};
-      st_lds8(t + (pc * 8 + 2 * w) * PITCH + pr * 4, a);
-      st_lds8(t + (pc * 8 + 2 * w + 1) * PITCH + pr * 4, b);
+    for (int u = 0; u < kPer; ++u) {
+      const int pid = threadIdx.x + u * T;
+      if (pid >= kPatches) break;
+      const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // columns 2w (low halves) and 2w+1 (high halves)
+        const u32x2 a = {lo16(reg[u][0][w], reg[u][1][w]), lo16(reg[u][2][w], reg[u][3][w])};
+        const u32x2 b = {hi16(reg[u][0][w], reg[u][1][w]), hi16(reg[u][2][w], reg[u][3][w])};
+        st_lds8(t + (pc * 8 + 2 * w) * PITCH + pr * 4, a);
+        st_lds8(t + (pc * 8 + 2 * w + 1) * PITCH + pr * 4, b);
+      }
     }
   }
 };
 
 // fp32 source stored [red][rows], rounded to bf16 (optionally scaled).
-template <int R>
+template <int R, int T = NT>
 struct ColsF32 {
   static constexpr int kPatches = 2 * R;
   const float* src;
@@ -193,7 +198,7 @@ struct ColsF32 {
   uint32_t reg[8][2];
   bool active;
 
-  __device__ void load(int kt) {
+  __device__ __forceinline__ void load(int kt) {
     const int pid = threadIdx.x;
     active = pid < kPatches;
     if (!active) return;
@@ -213,7 +218,7 @@ struct ColsF32 {
       reg[z][1] = pack_bf16x2(f[2][z], f[3][z]);
     }
   }
-  __device__ void store(lds_t* t) const {
+  __device__ __forceinline__ void store(lds_t* t) const {
     if (!active) return;
     const int pid = threadIdx.x;
     const int pr = pid % (BK / 4), pc = pid / (BK / 4);
@@ -226,9 +231,9 @@ struct ColsF32 {
 // 64-wide reduction step is exactly one NF4 block per row, so every thread
 // needs a single constant: thread t dequantizes half a block (32 codes) of row
 // t/2 (for R = 128) to bf16( fp32(level * c_hat) ).
-template <int R>
+template <int R, int T = NT>
 struct Nf4Rows {
-  static constexpr int kUnits = R * 2 / NT;  // half-blocks per thread
+  static constexpr int kUnits = R * 2 / T;  // half-blocks per thread
   const uint8_t* codes;
   const uint8_t* c2;
   const float* c1;
@@ -240,10 +245,10 @@ struct Nf4Rows {
   u32x4 q[kUnits];
   float chat[kUnits];
 
-  __device__ void load(int kt) {
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
-      const int idx = threadIdx.x + u * NT;
+      const int idx = threadIdx.x + u * T;
       const int rr = idx >> 1, h = idx & 1;
       if (rr < rows) {
         const int64_t n = row0 + rr;
@@ -256,10 +261,10 @@ struct Nf4Rows {
       }
     }
   }
-  __device__ void store(lds_t* t) const {
+  __device__ __forceinline__ void store(lds_t* t) const {
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
-      const int idx = threadIdx.x + u * NT;
+      const int idx = threadIdx.x + u * T;
       const int rr = idx >> 1, h = idx & 1;
       lds_t* dst = t + rr * PITCH + h * 32;
 #pragma unroll
@@ -279,11 +284,12 @@ struct Nf4Rows {
 };
 
 // NF4 weight read transposed: tile row i = weight column k0 + i, reduction =
-// weight row n.  A thread takes a patch of 4 rows (n) x 8 columns (k); the 8
-// columns lie in one block of each row, so it needs 4 constants.
-template <int R>
+// weight row n.  A thread takes patches of 4 rows (n) x 8 columns (k); the 8
+// columns lie in one block of each row, so a patch needs 4 constants.
+template <int R, int T = NT>
 struct Nf4Cols {
   static constexpr int kPatches = 2 * R;
+  static constexpr int kPer = (kPatches + T - 1) / T;
   const uint8_t* codes;
   const uint8_t* c2;
   const float* c1;
@@ -291,58 +297,65 @@ struct Nf4Cols {
   int64_t N, K;
   int64_t col0;
   const float* lut;
-  uint32_t word[4];
-  float chat[4];
-  bool active;
+  uint32_t word[kPer][4];
+  float chat[kPer][4];
 
-  __device__ void load(int kt) {
-    const int pid = threadIdx.x;
-    active = pid < kPatches;
-    if (!active) return;
-    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
-    const int64_t k = col0 + pc * 8;
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n = (int64_t)kt * BK + pr * 4 + q;
-      if (n < N && k < K) {
-        word[q] = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + k / 2);
-        const int64_t bi = n * (K / 64) + k / 64;
-        chat[q] = dequant_constant(c2[bi], c1[bi >> 8], mean);
-      } else {
-        word[q] = 0u;
-        chat[q] = 0.f;
+    for (int u = 0; u < kPer; ++u) {
+      const int pid = threadIdx.x + u * T;
+      if (pid >= kPatches) break;
+      const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+      const int64_t k = col0 + pc * 8;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = (int64_t)kt * BK + pr * 4 + q;
+        if (n < N && k < K) {
+          word[u][q] = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + k / 2);
+          const int64_t bi = n * (K / 64) + k / 64;
+          chat[u][q] = dequant_constant(c2[bi], c1[bi >> 8], mean);
+        } else {
+          word[u][q] = 0u;
+          chat[u][q] = 0.f;
+        }
       }
     }
   }
-  __device__ void store(lds_t* t) const {
-    if (!active) return;
-    const int pid = threadIdx.x;
-    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
+  __device__ __forceinline__ void store(lds_t* t) const {
 #pragma unroll
-    for (int z = 0; z < 8; ++z) {
-      float v[4];
+    for (int u = 0; u < kPer; ++u) {
+      const int pid = threadIdx.x + u * T;
+      if (pid >= kPatches) break;
+      const int pr = pid % (BK / 4), pc = pid / (BK / 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = __fmul_rn(lut[(word[q] >> (4 * z)) & 15u], chat[q]);
-      st_lds8(t + (pc * 8 + z) * PITCH + pr * 4, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+      for (int z = 0; z < 8; ++z) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __fmul_rn(lut[(word[u][q] >> (4 * z)) & 15u], chat[u][q]);
+        st_lds8(t + (pc * 8 + z) * PITCH + pr * 4, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+      }
     }
   }
 };
 
 // ---------------------------------------------------------------- engine
 
-template <int BM, int BN>
+// A BM x BN tile computed by 2 x WN waves, each (BM/2) x (BN/WN) as 32x32 MFMA tiles.
+template <int BM, int BN, int WN = 2>
 struct Acc {
-  static constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32;
+  static constexpr int TM = BM / 2 / 32, TN = BN / WN / 32;
   f32x16 c[TM][TN];
 };
 
-template <int BM, int BN>
-__device__ __forceinline__ void mma_tile(const lds_t* sa, const lds_t* sb, Acc<BM, BN>& acc) {
-  constexpr int TM = Acc<BM, BN>::TM, TN = Acc<BM, BN>::TN;
+template <int BM, int BN, int WN>
+__device__ __forceinline__ void mma_tile(const lds_t* sa, const lds_t* sb, Acc<BM, BN, WN>& acc) {
+  constexpr int TM = Acc<BM, BN, WN>::TM, TN = Acc<BM, BN, WN>::TN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int r = lane & 31, kq = (lane >> 5) * 8;
-#pragma unroll
+  // big wave tiles keep their accumulators in the 256 AGPRs; load fragments
+  // one 16-deep step at a time so they fit the VGPRs next to the prefetch
+#pragma unroll(TM * TN >= 16 ? 1 : 4)
   for (int kk = 0; kk < BK; kk += 16) {
     bf16x8 fa[TM], fb[TN];
 #pragma unroll
@@ -350,7 +363,7 @@ __device__ __forceinline__ void mma_tile(const lds_t* sa, const lds_t* sb, Acc<B
       fa[i] = __builtin_bit_cast(bf16x8, ld16(sa + (wm * (BM / 2) + i * 32 + r) * PITCH + kk + kq));
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      fb[j] = __builtin_bit_cast(bf16x8, ld16(sb + (wn * (BN / 2) + j * 32 + r) * PITCH + kk + kq));
+      fb[j] = __builtin_bit_cast(bf16x8, ld16(sb + (wn * (BN / WN) + j * 32 + r) * PITCH + kk + kq));
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -359,8 +372,8 @@ __device__ __forceinline__ void mma_tile(const lds_t* sa, const lds_t* sb, Acc<B
   }
 }
 
-template <int BM, int BN, class LA, class LB>
-__device__ void run_phase(LA& la, LB& lb, int kt0, int kt1, lds_t* sa, lds_t* sb, Acc<BM, BN>& acc) {
+template <int BM, int BN, int WN, class LA, class LB>
+__device__ __forceinline__ void run_phase(LA& la, LB& lb, int kt0, int kt1, lds_t* sa, lds_t* sb, Acc<BM, BN, WN>& acc) {
   if (kt0 >= kt1) return;
   constexpr int SA = BM * PITCH, SB = BN * PITCH;
   la.load(kt0);
@@ -375,7 +388,7 @@ __device__ void run_phase(LA& la, LB& lb, int kt0, int kt1, lds_t* sa, lds_t* sb
       la.load(kt + 1);
       lb.load(kt + 1);
     }
-    mma_tile<BM, BN>(sa + cur * SA, sb + cur * SB, acc);
+    mma_tile<BM, BN, WN>(sa + cur * SA, sb + cur * SB, acc);
     if (more) {
       la.store(sa + (cur ^ 1) * SA);
       lb.store(sb + (cur ^ 1) * SB);
@@ -385,11 +398,11 @@ __device__ void run_phase(LA& la, LB& lb, int kt0, int kt1, lds_t* sa, lds_t* sb
 }
 
 // Lane l of a 32x32 accumulator holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4.
-template <int BM, int BN, class F>
-__device__ __forceinline__ void for_each_out(const Acc<BM, BN>& acc, F f) {
-  constexpr int TM = Acc<BM, BN>::TM, TN = Acc<BM, BN>::TN;
+template <int BM, int BN, int WN, class F>
+__device__ __forceinline__ void for_each_out(const Acc<BM, BN, WN>& acc, F f) {
+  constexpr int TM = Acc<BM, BN, WN>::TM, TN = Acc<BM, BN, WN>::TN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -397,17 +410,17 @@ __device__ __forceinline__ void for_each_out(const Acc<BM, BN>& acc, F f) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = wn * (BN / 2) + j * 32 + (lane & 31);
+        const int col = wn * (BN / WN) + j * 32 + (lane & 31);
         f(row, col, acc.c[i][j][v]);
       }
 }
 
-template <int BM, int BN>
-__device__ __forceinline__ void zero(Acc<BM, BN>& acc) {
+template <int BM, int BN, int WN>
+__device__ __forceinline__ void zero(Acc<BM, BN, WN>& acc) {
 #pragma unroll
-  for (int i = 0; i < Acc<BM, BN>::TM; ++i)
+  for (int i = 0; i < Acc<BM, BN, WN>::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < Acc<BM, BN>::TN; ++j)
+    for (int j = 0; j < Acc<BM, BN, WN>::TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.f;
 }
@@ -418,9 +431,83 @@ __device__ __forceinline__ void load_lut(float* lut, const Nf4Table& tab) {
 
 __device__ __forceinline__ uint16_t to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xFFFFu); }
 
+// LoRA term appended to a tile's accumulators straight from global memory:
+// acc[i][j] += sum_k Aop(i, k) * Bop(j, k) over k < kr (kr <= 128), with the
+// operands small and cache-resident.  fa(row, k0) / fb(row, k0) return the
+// 8 bf16 values at k0 .. k0+7 of one operand row (zeros past the extents).
+template <int BM, int BN, int WN, class FA, class FB>
+__device__ __forceinline__ void lora_tail(Acc<BM, BN, WN>& acc, int kr, FA fa, FB fb) {
+  constexpr int TM = Acc<BM, BN, WN>::TM, TN = Acc<BM, BN, WN>::TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r = lane & 31, kq = (lane >> 5) * 8;
+#pragma unroll 1
+  for (int kk = 0; kk < kr; kk += 16) {
+    bf16x8 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = __builtin_bit_cast(bf16x8, fa(wm * (BM / 2) + i * 32 + r, kk + kq));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = __builtin_bit_cast(bf16x8, fb(wn * (BN / WN) + j * 32 + r, kk + kq));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+// 8 fp32 values of row `row` (k0 .. k0+7, zero past rows/kr), scaled, as bf16x8 bits
+__device__ __forceinline__ u32x4 frag_f32_row(const float* src, int64_t ld, int64_t row, int64_t rows, int k0,
+                                              int kr, float scale) {
+  float f[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f[q] = (row < rows && k0 + q < kr) ? src[row * ld + k0 + q] * scale : 0.f;
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
+// 8 bf16 values of row `row` of a row-major bf16 matrix (k0 .. k0+7)
+__device__ __forceinline__ u32x4 frag_bf16_row(const uint16_t* src, int64_t ld, int64_t row, int64_t rows, int k0,
+                                               int kr, bool vec) {
+  if (row < rows && vec && k0 + 8 <= kr) return ld16(src + row * ld + k0);
+  uint32_t e[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) e[q] = (row < rows && k0 + q < kr) ? src[row * ld + k0 + q] : 0u;
+  return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
+// 8 bf16 values of column `col` of a row-major bf16 matrix [kr][ld] (rows k0 .. k0+7)
+__device__ __forceinline__ u32x4 frag_bf16_col(const uint16_t* src, int64_t ld, int64_t col, int64_t cols, int k0,
+                                               int kr) {
+  uint32_t e[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) e[q] = (col < cols && k0 + q < kr) ? src[(int64_t)(k0 + q) * ld + col] : 0u;
+  return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
 // ---------------------------------------------------------------- kernels
 
-constexpr int FBM = 128, FBN = 128;
+// Tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each
+// with its own L2.  Workgroup L runs on XCD L % 8; give XCD x a contiguous
+// range of logical tiles (a bijection of [0, T)), and walk logical tiles in
+// grouped-raster order (gm row tiles by every column tile), so the CUs of one
+// XCD work on a compact block of tiles and share X and W slices in their L2.
+__device__ __forceinline__ void tile_of(int L, int mtiles, int ntiles, int gm, int& mi, int& ni) {
+  const int T = mtiles * ntiles;
+  const int x = L & 7, j = L >> 3;
+  const int q = T >> 3, rem = T & 7;
+  const int logical = x * q + min(x, rem) + j;
+  const int per_group = gm * ntiles;
+  const int group = logical / per_group;
+  const int first_m = group * gm;
+  const int gm_eff = min(gm, mtiles - first_m);
+  const int in_group = logical - group * per_group;
+  mi = first_m + in_group % gm_eff;
+  ni = in_group / gm_eff;
+}
+
+__host__ __device__ constexpr size_t gemm_lds_bytes(int bm, int bn) {
+  return (size_t)2 * (bm + bn) * PITCH * sizeof(lds_t) + 16 * sizeof(float);
+}
 
 // Forward, M > 16: Y = bf16( X W_deq^T + (s H) B^T ).  Phase 1 streams X and
 // the NF4 weight over K; phase 2 appends the LoRA product as r more reduction
@@ -438,28 +525,33 @@ struct FwdGemmParams {
   bool b_vec;
   float scale;
   uint16_t* Y;
+  int mtiles, ntiles, gm;
   Nf4Table tab;
 };
 
-__global__ void __launch_bounds__(NT) fwd_gemm_kernel(FwdGemmParams p) {
-  __shared__ __attribute__((aligned(16))) lds_t sa[2 * FBM * PITCH];
-  __shared__ __attribute__((aligned(16))) lds_t sb[2 * FBN * PITCH];
-  __shared__ float lut[16];
+template <int BM, int BN, int WN>
+__global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
+  constexpr int T = 128 * WN;
+  extern __shared__ __attribute__((aligned(16))) lds_t smem[];
+  lds_t* sa = smem;
+  lds_t* sb = smem + 2 * BM * PITCH;
+  float* lut = reinterpret_cast<float*>(sb + 2 * BN * PITCH);
   load_lut(lut, p.tab);
-  const int64_t m0 = (int64_t)blockIdx.y * FBM, n0 = (int64_t)blockIdx.x * FBN;
-  Acc<FBM, FBN> acc;
+  int mi, ni;
+  tile_of((int)blockIdx.x, p.mtiles, p.ntiles, p.gm, mi, ni);
+  const int64_t m0 = (int64_t)mi * BM, n0 = (int64_t)ni * BN;
+  Acc<BM, BN, WN> acc;
   zero(acc);
   __syncthreads();
   {
-    RowsBf16<FBM> la{p.X, p.K, (int)min<int64_t>(FBM, p.M - m0), (int)p.K, m0, true};
-    Nf4Rows<FBN> lb{p.codes, p.c2, p.c1, *p.mean, p.K, (int)min<int64_t>(FBN, p.N - n0), n0, lut};
-    run_phase<FBM, FBN>(la, lb, 0, (int)(p.K / BK), sa, sb, acc);
+    RowsBf16<BM, T> la{p.X, p.K, (int)min<int64_t>(BM, p.M - m0), (int)p.K, m0, true};
+    Nf4Rows<BN, T> lb{p.codes, p.c2, p.c1, *p.mean, p.K, (int)min<int64_t>(BN, p.N - n0), n0, lut};
+    run_phase<BM, BN, WN>(la, lb, 0, (int)(p.K / BK), sa, sb, acc);
   }
-  {
-    RowsF32<FBM> la{p.H, p.r, (int)min<int64_t>(FBM, p.M - m0), p.r, m0, p.scale};
-    RowsBf16<FBN> lb{p.B, p.r, (int)min<int64_t>(FBN, p.N - n0), p.r, n0, p.b_vec};
-    run_phase<FBM, FBN>(la, lb, 0, (p.r + BK - 1) / BK, sa, sb, acc);
-  }
+  lora_tail<BM, BN, WN>(
+      acc, p.r,
+      [&](int i, int k0) { return frag_f32_row(p.H, p.r, m0 + i, p.M, k0, p.r, p.scale); },
+      [&](int j, int k0) { return frag_bf16_row(p.B, p.r, n0 + j, p.N, k0, p.r, p.b_vec); });
   for_each_out(acc, [&](int i, int j, float v) {
     const int64_t m = m0 + i, n = n0 + j;
     if (m < p.M && n < p.N) p.Y[m * p.N + n] = to_bf16(v);
@@ -487,11 +579,11 @@ __global__ void __launch_bounds__(NT) skinny_kernel(SkinnyParams<BM, BN, LA, LB>
   LB lb = p.lb;
   la.row_origin(i0, p.rows);
   lb.row_origin(j0, p.cols);
-  Acc<BM, BN> acc;
+  Acc<BM, BN, 2> acc;
   zero(acc);
   const int kt0 = blockIdx.z * p.steps_per_split;
   const int kt1 = min(p.ksteps, kt0 + p.steps_per_split);
-  run_phase<BM, BN>(la, lb, kt0, kt1, sa, sb, acc);
+  run_phase<BM, BN, 2>(la, lb, kt0, kt1, sa, sb, acc);
   float* out = p.out + (int64_t)blockIdx.z * p.rows * p.cols;
   for_each_out(acc, [&](int i, int j, float v) {
     const int64_t a = i0 + i, b = j0 + j;
@@ -527,28 +619,33 @@ struct DxParams {
   const float* dH;
   const uint16_t* A;
   uint16_t* dX;
+  int mtiles, ntiles, gm;
   Nf4Table tab;
 };
 
-__global__ void __launch_bounds__(NT) dx_gemm_kernel(DxParams p) {
-  __shared__ __attribute__((aligned(16))) lds_t sa[2 * FBM * PITCH];
-  __shared__ __attribute__((aligned(16))) lds_t sb[2 * FBN * PITCH];
-  __shared__ float lut[16];
+template <int BM, int BN, int WN>
+__global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
+  constexpr int T = 128 * WN;
+  extern __shared__ __attribute__((aligned(16))) lds_t smem[];
+  lds_t* sa = smem;
+  lds_t* sb = smem + 2 * BM * PITCH;
+  float* lut = reinterpret_cast<float*>(sb + 2 * BN * PITCH);
   load_lut(lut, p.tab);
-  const int64_t m0 = (int64_t)blockIdx.y * FBM, k0 = (int64_t)blockIdx.x * FBN;
-  Acc<FBM, FBN> acc;
+  int mi, ki;
+  tile_of((int)blockIdx.x, p.mtiles, p.ntiles, p.gm, mi, ki);
+  const int64_t m0 = (int64_t)mi * BM, k0 = (int64_t)ki * BN;
+  Acc<BM, BN, WN> acc;
   zero(acc);
   __syncthreads();
   {
-    RowsBf16<FBM> la{p.dY, p.N, (int)min<int64_t>(FBM, p.M - m0), (int)p.N, m0, (p.N % 8) == 0};
-    Nf4Cols<FBN> lb{p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut};
-    run_phase<FBM, FBN>(la, lb, 0, (int)((p.N + BK - 1) / BK), sa, sb, acc);
+    RowsBf16<BM, T> la{p.dY, p.N, (int)min<int64_t>(BM, p.M - m0), (int)p.N, m0, (p.N % 8) == 0};
+    Nf4Cols<BN, T> lb{p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut};
+    run_phase<BM, BN, WN>(la, lb, 0, (int)((p.N + BK - 1) / BK), sa, sb, acc);
   }
-  {
-    RowsF32<FBM> la{p.dH, p.r, (int)min<int64_t>(FBM, p.M - m0), p.r, m0, 1.0f};
-    ColsBf16<FBN> lb{p.A, p.K, (int)min<int64_t>(FBN, p.K - k0), p.r, k0, true};
-    run_phase<FBM, FBN>(la, lb, 0, (p.r + BK - 1) / BK, sa, sb, acc);
-  }
+  lora_tail<BM, BN, WN>(
+      acc, p.r,
+      [&](int i, int kk) { return frag_f32_row(p.dH, p.r, m0 + i, p.M, kk, p.r, 1.0f); },
+      [&](int j, int kk) { return frag_bf16_col(p.A, p.K, k0 + j, p.K, kk, p.r); });
   for_each_out(acc, [&](int i, int j, float v) {
     const int64_t m = m0 + i, k = k0 + j;
     if (m < p.M && k < p.K) p.dX[m * p.K + k] = to_bf16(v);
@@ -557,22 +654,22 @@ __global__ void __launch_bounds__(NT) dx_gemm_kernel(DxParams p) {
 
 // Skinny-product loaders with a per-tile origin, built on the loaders above.
 template <int R>
-struct SRowsBf16 : RowsBf16<R> {
-  __device__ void row_origin(int64_t o, int64_t total) {
+struct SRowsBf16 : RowsBf16<R, NT> {
+  __device__ __forceinline__ void row_origin(int64_t o, int64_t total) {
     this->row0 = o;
     this->rows = (int)min<int64_t>(R, total - o);
   }
 };
 template <int R>
-struct SColsBf16 : ColsBf16<R> {
-  __device__ void row_origin(int64_t o, int64_t total) {
+struct SColsBf16 : ColsBf16<R, NT> {
+  __device__ __forceinline__ void row_origin(int64_t o, int64_t total) {
     this->col0 = o;
     this->cols = (int)min<int64_t>(R, total - o);
   }
 };
 template <int R>
-struct SColsF32 : ColsF32<R> {
-  __device__ void row_origin(int64_t o, int64_t total) {
+struct SColsF32 : ColsF32<R, NT> {
+  __device__ __forceinline__ void row_origin(int64_t o, int64_t total) {
     this->col0 = o;
     this->cols = (int)min<int64_t>(R, total - o);
   }
@@ -625,6 +722,23 @@ size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r) {
   return splits == 1 ? 0 : (size_t)splits * M * r * sizeof(float);
 }
 
+// Launch a tiled kernel with dynamic LDS (raising the per-kernel limit once).
+template <class Kern, class P>
+hipError_t launch_tiled(Kern kern, int threads, size_t lds, int mtiles, int ntiles, P& p, hipStream_t s) {
+  static bool attr_set = false;  // per instantiation; setting it twice is harmless
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  p.mtiles = mtiles;
+  p.ntiles = ntiles;
+  p.gm = mtiles >= 8 ? mtiles / 8 : 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(mtiles * ntiles)), dim3(threads), lds, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   FwdGemmParams p;
   p.X = a.X;
@@ -642,8 +756,11 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   p.scale = a.scale;
   p.Y = a.Y;
   p.tab = nf4_table();
-  hipLaunchKernelGGL(fwd_gemm_kernel, dim3(cdiv(a.N, FBN), cdiv(a.M, FBM)), dim3(NT), 0, s, p);
-  return hipGetLastError();
+  if (a.M >= 256)
+    return launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), (int)cdiv(a.M, 256),
+                        (int)cdiv(a.N, 256), p, s);
+  return launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), (int)cdiv(a.M, 128),
+                      (int)cdiv(a.N, 128), p, s);
 }
 
 // Backward workspace: H (if recomputed), dH, and split-K partials.
@@ -730,7 +847,13 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     p.A = a.A;
     p.dX = a.dX;
     p.tab = nf4_table();
-    hipLaunchKernelGGL(dx_gemm_kernel, dim3(cdiv(a.K, FBN), cdiv(a.M, FBM)), dim3(NT), 0, s, p);
+    if (a.M >= 256)
+      e = launch_tiled(dx_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), (int)cdiv(a.M, 256),
+                       (int)cdiv(a.K, 256), p, s);
+    else
+      e = launch_tiled(dx_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), (int)cdiv(a.M, 128),
+                       (int)cdiv(a.K, 128), p, s);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

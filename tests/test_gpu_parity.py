@@ -151,6 +151,7 @@ FWD_CASES = [
     (2, 300, 1024, 16), (7, 129, 512, 24), (1, 1000, 2048, 64), (5, 77, 768, 12), (16, 64, 4096, 64),
     (1, 96, 11008, 64), (12, 40, 1280, 40),
     (17, 130, 192, 16), (33, 257, 128, 1), (130, 300, 448, 72), (256, 512, 1024, 64), (64, 64, 64, 64),
+    (600, 700, 1536, 16), (513, 2304, 512, 64),
 ]
 
 
@@ -246,7 +247,8 @@ def test_forward_decode_layer_full_size(shape):
 
 # ------------------------------------------------------------------ backward
 
-BWD_CASES = [(16, 256, 256, 8), (3, 100, 320, 5), (70, 130, 192, 16), (257, 300, 448, 72), (1, 64, 64, 1)]
+BWD_CASES = [(16, 256, 256, 8), (3, 100, 320, 5), (70, 130, 192, 16), (257, 300, 448, 72), (1, 64, 64, 1),
+             (520, 600, 1280, 32)]
 
 
 @pytest.mark.parametrize("M,N,K,r", BWD_CASES)
