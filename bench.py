@@ -14,7 +14,7 @@ decode layer, the Llama-7B MLP shapes at M = 1, the 65B-scale training layer
 double quant throughput.  The CPU oracle is timed on a bounded sample of the
 headline workload (`cpu_baseline`).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--eager] [--no-cpu]
 """
 
 from __future__ import annotations
@@ -257,6 +257,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the headline steps one by one instead of replaying a graph "
+                         "(for per-dispatch counter collection)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -276,7 +279,7 @@ def main():
     N, K, r = 4096, 4096, 64
     copies = max(2, int(2 * MALL_BYTES / fwd_bytes(1, N, K, r)) + 1)
     log(f"[bench] decode fwd M=1 {N}x{K} r={r}: {copies} weight copies, {args.steps} steps")
-    head = bench_fwd(torch, qa, 1, N, K, r, args.steps, args.warmup, copies)
+    head = bench_fwd(torch, qa, 1, N, K, r, args.steps, args.warmup, copies, graph=not args.eager)
     log(f"[bench] M=1: {head['ms'] * 1e3:.2f} us/call, {head['GBps']:.0f} GB/s")
 
     if args.copy_calibration:
