@@ -12,8 +12,10 @@
 // output tile: both operands are staged in LDS as [rows][64 + 8] bf16 tiles
 // (reduction contiguous, 16-byte pad so that 16-byte fragment reads of eight
 // consecutive rows hit distinct banks), double-buffered with one barrier per
-// 64-wide reduction step.  Four waves in a 2 x 2 grid each own
-// (BM/2) x (BN/2) of the tile as 32x32x16 MFMA accumulators.
+// 64-wide reduction step.  2 x WN waves each own (BM/2) x (BN/WN) of the
+// tile as 32x32x16 MFMA accumulators: 4 waves for 128 x 128 tiles, 8 waves
+// (two per SIMD, so one wave's dequantization overlaps the other's MFMAs)
+// for 256 x 256 tiles.
 //
 // Loaders turn every source layout into that LDS form:
 //   RowsBf16  bf16 [rows][red] (X, dY, A, B)
