@@ -62,12 +62,14 @@ def fwd_workspace(M: int, N: int, K: int, r: int, device):
 
 
 def linear_fwd(X, q: QuantizedWeight, A, B, alpha: float, workspace=None, want_h: bool = True, stream=None):
-    """Y = X W_deq^T + (alpha/r) (X A^T) B^T.  X, A, B bf16; returns (Y bf16 [M,N], H fp32 [M,r] or None)."""
+    """Y = X W_deq^T + (alpha/r) (X A^T) B^T.  X, A, B bf16; returns (Y bf16 [M,N], H fp32 [M,r] or None).
+
+    A = B = None means no adapter (r = 0): Y = X W_deq^T."""
     import torch
     M = X.shape[0]
-    r = A.shape[0]
+    r = 0 if A is None else A.shape[0]
     Y = torch.empty((M, q.N), dtype=torch.bfloat16, device=X.device)
-    H = torch.empty((M, r), dtype=torch.float32, device=X.device) if want_h else None
+    H = torch.empty((M, r), dtype=torch.float32, device=X.device) if want_h and r > 0 else None
     if workspace is None:
         workspace = fwd_workspace(M, q.N, q.K, r, X.device)
     qlora_linear_fwd(X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, Y, H, workspace, q.N, stream)
@@ -75,13 +77,15 @@ def linear_fwd(X, q: QuantizedWeight, A, B, alpha: float, workspace=None, want_h
 
 
 def linear_bwd(dY, X, q: QuantizedWeight, A, B, alpha: float, H=None, want_dx: bool = True, stream=None):
-    """Gradients (dX or None, dA, dB) of the QLoRA linear; the NF4 weight gets none."""
+    """Gradients (dX or None, dA, dB) of the QLoRA linear; the NF4 weight gets none.
+
+    A = B = None means no adapter (r = 0): only dX, and dA = dB = None."""
     import torch
     M, K = X.shape
-    r = A.shape[0]
+    r = 0 if A is None else A.shape[0]
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device) if want_dx else None
-    dA = torch.empty((r, K), dtype=torch.bfloat16, device=X.device)
-    dB = torch.empty((q.N, r), dtype=torch.bfloat16, device=X.device)
+    dA = torch.empty((r, K), dtype=torch.bfloat16, device=X.device) if r > 0 else None
+    dB = torch.empty((q.N, r), dtype=torch.bfloat16, device=X.device) if r > 0 else None
     ws = torch.empty(max(qlora_linear_bwd_workspace(M, q.N, K, r), 256), dtype=torch.uint8, device=X.device)
     qlora_linear_bwd(dY, X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, H, dX, dA, dB, ws, stream)
     return dX, dA, dB

@@ -136,7 +136,7 @@ def qlora_linear_fwd(X, codes, c2, c1, mean, A, B, alpha: float, Y, H_out, works
                      stream=None):
     _need_cuda(X, codes, c2, c1, mean, A, B, Y, H_out, workspace)
     M, K = X.shape
-    r = A.shape[0]
+    r = 0 if A is None else A.shape[0]
     _check(lib().qlora_linear_fwd(_ptr(X), M, N, K, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), _ptr(A),
                                   _ptr(B), r, float(alpha), _ptr(Y), _ptr(H_out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
@@ -152,7 +152,7 @@ def qlora_linear_bwd(dY, X, codes, c2, c1, mean, A, B, alpha: float, H, dX, dA, 
     _need_cuda(dY, X, codes, c2, c1, mean, A, B, H, dX, dA, dB, workspace)
     M, K = X.shape
     N = dY.shape[1]
-    r = A.shape[0]
+    r = 0 if A is None else A.shape[0]
     _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), M, N, K, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean),
                                   _ptr(A), _ptr(B), r, float(alpha), _ptr(H), _ptr(dX), _ptr(dA), _ptr(dB),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),

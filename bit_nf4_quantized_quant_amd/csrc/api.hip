@@ -36,7 +36,7 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 int check_layer(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M < 0 || N < 0 || K < 0 || r < 0) return QLORA_EINVAL;
   if (K % 64 != 0) return QLORA_ESHAPE;
-  if (r < 1 || r > 128) return QLORA_ESHAPE;
+  if (r > 128) return QLORA_ESHAPE;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return QLORA_ESHAPE;
   if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return QLORA_ESHAPE;
   return QLORA_OK;
@@ -70,7 +70,7 @@ const char* qlora_status_str(int status) {
   switch (status) {
     case QLORA_OK: return "QLORA_OK";
     case QLORA_EINVAL: return "QLORA_EINVAL: null, negative, misaligned argument or workspace too small";
-    case QLORA_ESHAPE: return "QLORA_ESHAPE: unsupported shape (K % 64, r outside [1,128], size limit)";
+    case QLORA_ESHAPE: return "QLORA_ESHAPE: unsupported shape (K % 64, r above 128, size limit)";
     case QLORA_EHIP: return "QLORA_EHIP: the HIP runtime rejected a kernel launch";
     default: return "QLORA: unknown status";
   }
@@ -142,7 +142,8 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
   if (K == 0) return QLORA_ESHAPE;
   if (M == 0 || N == 0) return QLORA_OK;
   if ((st = check_weight(codes, c2, c1, mean))) return st;
-  if (!X || !A || !B || !Y || !workspace) return QLORA_EINVAL;
+  if (!X || !Y || !workspace) return QLORA_EINVAL;
+  if (r > 0 && (!A || !B)) return QLORA_EINVAL;
   if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(Y, 2) || !aligned(workspace, 256))
     return QLORA_EINVAL;
   if (H_out && !aligned(H_out, 4)) return QLORA_EINVAL;
@@ -157,18 +158,19 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
   a.w = Nf4Weight{codes, c2, c1, mean};
   a.A = A;
   a.B = B;
-  a.scale = alpha / (float)r;
+  a.scale = r > 0 ? alpha / (float)r : 0.f;
   a.Y = Y;
-  a.H = H_out;
+  a.H = r > 0 ? H_out : nullptr;
   a.workspace = workspace;
   hipStream_t s = (hipStream_t)stream;
   if (use_decode(M, N, K)) return status_of(launch_decode_fwd(a, s));
   char* ws = reinterpret_cast<char*>(workspace) + kFwdReserved;
-  float* H = H_out ? H_out : reinterpret_cast<float*>(ws);
-  float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
-  a.H = H;
-  hipError_t e = launch_lora_down(X, M, K, A, r, H, scratch, s);
-  if (e != hipSuccess) return QLORA_EHIP;
+  if (r > 0) {
+    float* H = H_out ? H_out : reinterpret_cast<float*>(ws);
+    float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
+    a.H = H;
+    if (launch_lora_down(X, M, K, A, r, H, scratch, s) != hipSuccess) return QLORA_EHIP;
+  }
   return status_of(launch_gemm_fwd(a, s));
 }
 
@@ -185,7 +187,8 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N
   if (st) return st;
   if (K == 0) return QLORA_ESHAPE;
   if ((st = check_weight(codes, c2, c1, mean))) return st;
-  if (!A || !B || !dA || !dB || !workspace) return QLORA_EINVAL;
+  if (!workspace) return QLORA_EINVAL;
+  if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_EINVAL;
   if (M > 0 && (!dY || !X)) return QLORA_EINVAL;
   if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(dA, 16) ||
       !aligned(dB, 2) || !aligned(workspace, 256))
@@ -205,7 +208,7 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N
   a.w = Nf4Weight{codes, c2, c1, mean};
   a.A = A;
   a.B = B;
-  a.scale = alpha / (float)r;
+  a.scale = r > 0 ? alpha / (float)r : 0.f;
   a.H = H;
   a.dX = dX;
   a.dA = dA;

@@ -265,6 +265,7 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
   // chunks, parked in LDS after the weight stream (row stride r+1: no bank
   // conflicts when the 16 rows are read together)
   const int bs_ld = p.r + 1;
+  const int rdiv = p.r > 0 ? p.r : 1;   // r = 0 (no adapter): every B/H loop is empty
   const int b_chunks = p.b_vec ? (16 * p.r) / 8 : 0;
   const rsrc_t rb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
   u32x4 bchunk = {0u, 0u, 0u, 0u};
@@ -276,7 +277,7 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
       const int e = threadIdx.x + i * kThreads;
-      const int br = e / p.r, bc = e - br * p.r;
+      const int br = e / rdiv, bc = e - br * p.r;
       bv[i] = (e < 16 * p.r && n0 + br < p.N) ? p.B[(size_t)(n0 + br) * p.r + bc] : 0u;
     }
   }
@@ -378,7 +379,7 @@ __device__ void weight_tile(const DecodeParams& p, int tile, uint32_t* lut, char
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
       const int e = threadIdx.x + i * kThreads;
-      const int br = e / p.r, bc = e - br * p.r;
+      const int br = e / rdiv, bc = e - br * p.r;
       if (e < 16 * p.r) bs[br * bs_ld + bc] = __uint_as_float(bv[i] << 16);
     }
   }

@@ -797,41 +797,43 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
   float* dH = reinterpret_cast<float*>(ws + plan.off_dH);
   float* part = reinterpret_cast<float*>(ws + plan.off_part);
   hipError_t e;
-  if (a.M > 0 && !H) {
-    H = reinterpret_cast<float*>(ws + plan.off_H);
-    if ((e = launch_lora_down(a.X, a.M, a.K, a.A, a.r, H, part, s)) != hipSuccess) return e;
-  }
-  const bool n_vec = (a.N % 8) == 0;
-  const bool r_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
-  // dH = s dY B : rows m, cols j, reduction n
-  if (a.M > 0) {
-    SRowsBf16<128> la;
-    la.src = a.dY; la.ld = a.N; la.red = (int)a.N; la.vec = n_vec;
-    SColsBf16<64> lb;
-    lb.src = a.B; lb.ld = a.r; lb.red = (int)a.N; lb.vec = r_vec;
-    if ((e = launch_skinny<128, 64>(la, lb, a.M, a.r, a.N, plan.s_dh, part, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.M * a.r, 256)), dim3(256), 0, s, part, plan.s_dh,
-                       (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
-  }
-  // dB = s dY^T H : rows n, cols j, reduction m
-  {
-    SColsBf16<128> la;
-    la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
-    SColsF32<64> lb;
-    lb.src = H; lb.ld = a.r; lb.red = (int)a.M; lb.scale = 1.0f;
-    if ((e = launch_skinny<128, 64>(la, lb, a.N, a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, part, plan.s_db,
-                       (int64_t)(a.N * a.r), a.scale, a.dB, (float*)nullptr);
-  }
-  // dA = dH^T X : rows j, cols k, reduction m
-  {
-    SColsF32<64> la;
-    la.src = dH; la.ld = a.r; la.red = (int)a.M; la.scale = 1.0f;
-    SColsBf16<128> lb;
-    lb.src = a.X; lb.ld = a.K; lb.red = (int)a.M; lb.vec = true;
-    if ((e = launch_skinny<64, 128>(la, lb, a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.r * a.K, 256)), dim3(256), 0, s, part, plan.s_da,
-                       (int64_t)(a.r * a.K), 1.0f, a.dA, (float*)nullptr);
+  if (a.r > 0) {  // no adapter (r = 0): only the input gradient
+    if (a.M > 0 && !H) {
+      H = reinterpret_cast<float*>(ws + plan.off_H);
+      if ((e = launch_lora_down(a.X, a.M, a.K, a.A, a.r, H, part, s)) != hipSuccess) return e;
+    }
+    const bool n_vec = (a.N % 8) == 0;
+    const bool r_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
+    // dH = s dY B : rows m, cols j, reduction n
+    if (a.M > 0) {
+      SRowsBf16<128> la;
+      la.src = a.dY; la.ld = a.N; la.red = (int)a.N; la.vec = n_vec;
+      SColsBf16<64> lb;
+      lb.src = a.B; lb.ld = a.r; lb.red = (int)a.N; lb.vec = r_vec;
+      if ((e = launch_skinny<128, 64>(la, lb, a.M, a.r, a.N, plan.s_dh, part, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.M * a.r, 256)), dim3(256), 0, s, part, plan.s_dh,
+                         (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
+    }
+    // dB = s dY^T H : rows n, cols j, reduction m
+    {
+      SColsBf16<128> la;
+      la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
+      SColsF32<64> lb;
+      lb.src = H; lb.ld = a.r; lb.red = (int)a.M; lb.scale = 1.0f;
+      if ((e = launch_skinny<128, 64>(la, lb, a.N, a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, part, plan.s_db,
+                         (int64_t)(a.N * a.r), a.scale, a.dB, (float*)nullptr);
+    }
+    // dA = dH^T X : rows j, cols k, reduction m
+    {
+      SColsF32<64> la;
+      la.src = dH; la.ld = a.r; la.red = (int)a.M; la.scale = 1.0f;
+      SColsBf16<128> lb;
+      lb.src = a.X; lb.ld = a.K; lb.red = (int)a.M; lb.vec = true;
+      if ((e = launch_skinny<64, 128>(la, lb, a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.r * a.K, 256)), dim3(256), 0, s, part, plan.s_da,
+                         (int64_t)(a.r * a.K), 1.0f, a.dA, (float*)nullptr);
+    }
   }
   // dX = dY W_deq + dH A
   if (a.dX && a.M > 0) {

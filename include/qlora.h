@@ -58,7 +58,7 @@ extern "C" {
 
 #define QLORA_OK 0
 #define QLORA_EINVAL 1  /* null pointer, negative size, misaligned pointer, workspace too small */
-#define QLORA_ESHAPE 2  /* K % 64 != 0, r outside [1,128], sizes past the supported range */
+#define QLORA_ESHAPE 2  /* K % 64 != 0, r above 128, sizes past the supported range */
 #define QLORA_EHIP 3    /* the HIP runtime rejected a launch (hipGetLastError) */
 
 /* Human-readable name of a status code (static string). */
@@ -132,7 +132,9 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  *   codes, c2, c1, mean          the quantized weight W [N,K] (see above)
  *   A      in   bf16 [r,K]       LoRA down factor (16-B aligned)
  *   B      in   bf16 [N,r]       LoRA up factor
- *   r, alpha                     rank (1..128) and LoRA alpha; s = alpha / r in fp32
+ *   r, alpha                     rank (0..128) and LoRA alpha; s = alpha / r in fp32.
+ *                                r = 0 is a layer without adapter: Y = bf16(X W_deq^T);
+ *                                A, B and H_out may then be NULL and are not accessed
  *   Y      out  bf16 [M,N]       Y = bf16( X W_deq^T + s H B^T ), fp32 accumulation
  *   H_out  out  fp32 [M,r]       H = X A^T (may be NULL; keep it for the backward)
  *   workspace                    qlora_linear_fwd_workspace(M,N,K,r) bytes,
@@ -161,6 +163,7 @@ size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  *   H   in   fp32 [M,r] from the forward, or NULL to recompute it
  *   dX  out  bf16 [M,K] (may be NULL to skip the input gradient)
  *   dA  out  bf16 [r,K];  dB out bf16 [N,r]
+ *   r = 0 (no adapter): only dX = dY W_deq; A, B, H, dA, dB may be NULL
  *   workspace  qlora_linear_bwd_workspace(M,N,K,r) bytes, 256-B aligned
  *              (contents on entry do not matter)
  */

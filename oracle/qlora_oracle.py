@@ -313,7 +313,20 @@ def dequant_weight(codes_packed: np.ndarray, c2: np.ndarray, c1: np.ndarray, mu,
     c1r = np.asarray(c1, dtype=F32)[blk // DQ_BLOCK]
     prod = f32(e4m3_value(c2r) * c1r.astype(F64))
     chat = f32(prod.astype(F64) + F64(F32(mu)))                     # [rows, K/64]
-    chat_e = np.repeat(chat, BLOCK, axis=1)
+    return dequant_codes(codes, chat, L)
+
+
+def dequant_codes(codes: np.ndarray, chat: np.ndarray, levels32: np.ndarray | None = None) -> np.ndarray:
+    """W_deq = bf16( fp32( L[code] * c_hat ) ) for unpacked codes [R, nb*64] whose
+    64-element blocks have the dequantized constants chat [R, nb]; bf16 bits [R, nb*64].
+
+    Any set of whole blocks can be expanded this way (rows of W, or a 64-column
+    slice of every row), since each block carries its own constant.
+    """
+    L = nf4_levels_f32() if levels32 is None else np.asarray(levels32, dtype=F32)
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, n = codes.shape
+    chat_e = np.repeat(np.asarray(chat, dtype=F32).reshape(R, n // BLOCK), BLOCK, axis=1)
     w = f32(L[codes].astype(F64) * chat_e.astype(F64))
     return bf16_round(w)
 

@@ -15,45 +15,57 @@ of N(., .) is read as a standard deviation throughout, as numpy's
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
-from typing import Iterator
+import os
 
 import numpy as np
 
 # Seeds per tensor role: W uses seed 0 as in the pages' worked example.
 SEED_W, SEED_X, SEED_A, SEED_B, SEED_DY = 0, 1, 2, 3, 4
 
-_CHUNK = 1 << 22  # draw in chunks so huge tensors never hold a full fp64 copy
-
-
-def _normal_f64_chunks(rng: np.random.Generator, std: float, count: int) -> Iterator[np.ndarray]:
-    done = 0
-    while done < count:
-        n = min(_CHUNK, count - done)
-        yield rng.normal(0.0, std, size=n)
-        done += n
+_CHUNK = 1 << 22  # elements per independent sub-stream (and per worker task)
+_WORKERS = min(16, os.cpu_count() or 1)
 
 
 def normal_f32(seed, shape, std: float) -> np.ndarray:
-    """fp64 normal draws rounded to fp32 (round to nearest even)."""
+    """fp64 normal draws rounded to fp32 (round to nearest even).
+
+    Element i belongs to chunk i // 2^22; chunk c is drawn from the PCG64
+    stream of ``seed`` advanced by c jumps, so chunks are independent and are
+    filled in parallel.  A tensor of at most one chunk is exactly the first
+    ``count`` draws of ``np.random.default_rng(seed).normal(0, std)``.
+    """
     count = int(np.prod(shape))
     out = np.empty(count, dtype=np.float32)
-    rng = np.random.default_rng(seed)
-    pos = 0
-    for chunk in _normal_f64_chunks(rng, std, count):
-        out[pos:pos + chunk.size] = chunk.astype(np.float32)
-        pos += chunk.size
+    nchunks = -(-count // _CHUNK)
+    base = np.random.PCG64(seed)
+
+    def fill(c):
+        n = min(_CHUNK, count - c * _CHUNK)
+        rng = np.random.Generator(base.jumped(c) if c else np.random.PCG64(seed))
+        out[c * _CHUNK:c * _CHUNK + n] = rng.normal(0.0, std, size=n)
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(min(_WORKERS, nchunks)) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Store fp32 values as bf16 bit patterns (uint16), round to nearest even.
 
-    Inputs are finite; this is only the storage conversion of synthetic data.
+    Inputs are finite (so the 32-bit sum below cannot wrap); this is only the
+    storage conversion of synthetic data.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = u + np.uint32(0x7FFF)
+    out += (u >> 16) & np.uint32(1)
+    out >>= 16
+    return out.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

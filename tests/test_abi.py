@@ -98,7 +98,7 @@ def _fwd(L, **kw):
     a.update(kw)
     if a["wsb"] is None:
         a["wsb"] = L.qlora_linear_fwd_workspace(max(a["M"], 0), max(a["N"], 0), max(a["K"], 0),
-                                                min(max(a["r"], 1), 128))
+                                                min(max(a["r"], 0), 128))
     return L.qlora_linear_fwd(a["X"], a["M"], a["N"], a["K"], a["codes"], a["c2"], a["c1"], a["mean"],
                               a["A"], a["B"], a["r"], a["alpha"], a["Y"], a["H"], a["ws"], a["wsb"], None)
 
@@ -107,8 +107,12 @@ def test_fwd_validation():
     L = _lib.lib()
     assert _fwd(L, K=96) == _lib.QLORA_ESHAPE
     assert _fwd(L, K=0) == _lib.QLORA_ESHAPE
-    assert _fwd(L, r=0) == _lib.QLORA_ESHAPE
+    assert _fwd(L, r=-1) == _lib.QLORA_EINVAL
     assert _fwd(L, r=129) == _lib.QLORA_ESHAPE
+    assert _fwd(L, A=None) == _lib.QLORA_EINVAL              # an adapter needs A and B
+    assert _fwd(L, B=None) == _lib.QLORA_EINVAL
+    # r = 0: no adapter, A and B may be NULL (empty batch: nothing is queued)
+    assert _fwd(L, r=0, A=None, B=None, M=0, X=None, Y=None) == _lib.QLORA_OK
     assert _fwd(L, M=-1) == _lib.QLORA_EINVAL
     assert _fwd(L, X=None) == _lib.QLORA_EINVAL
     assert _fwd(L, X=MIS) == _lib.QLORA_EINVAL
@@ -147,6 +151,8 @@ def test_bwd_validation():
     assert call(dX=MIS) == _lib.QLORA_EINVAL
     assert call(wsb=need - 1) == _lib.QLORA_EINVAL
     assert call(N=0) == _lib.QLORA_OK
+    assert call(A=None) == _lib.QLORA_EINVAL
+    assert call(r=0, A=None, B=None, dA=None, dB=None, N=0) == _lib.QLORA_OK
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):

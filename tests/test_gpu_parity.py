@@ -285,3 +285,149 @@ def test_backward_empty_batch_gives_zero_lora_grads():
     torch.cuda.synchronize()
     assert dX.numel() == 0
     assert float(dA.float().abs().sum()) == 0.0 and float(dB.float().abs().sum()) == 0.0
+
+
+# ------------------------------------------------------------------ no adapter (r = 0)
+
+NOADAPTER_CASES = [(1, 256, 256), (16, 300, 512), (40, 130, 192), (300, 257, 320)]
+
+
+@pytest.mark.parametrize("M,N,K", NOADAPTER_CASES)
+def test_no_adapter_forward_and_backward(M, N, K):
+    """r = 0: Y = X W_deq^T and dX = dY W_deq, with A and B passed as NULL."""
+    say(f"[r=0] M={M} N={N} K={K}")
+    d = synth.make_layer(synth.LayerShape("t", M=M, N=N, K=K, r=1, seed_offset=7 * M + N + K), with_dy=True)
+    _, wd = oracle_layer(d, 16.0, 1)
+    q = gpu_quantize(d["W"])
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    Y, H = qa.linear_fwd(X, q, None, None, 16.0)
+    dX, dA, dB = qa.linear_bwd(dY, X, q, None, None, 16.0)
+    torch.cuda.synchronize()
+    assert H is None and dA is None and dB is None
+    Xf, Wf, dYf = bf16_f64(d["X"]), bf16_f64(wd), bf16_f64(d["dY"])
+    no_a, no_b = np.zeros((0, K)), np.zeros((N, 0))
+    Yr, _ = oracle.linear_fwd_f64(Xf, Wf, no_a, no_b, 0.0)
+    g = oracle.linear_bwd_f64(dYf, Xf, Wf, no_a, no_b, 0.0)
+    check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (r=0)")
+    check_close(bf16_f64(host_bf16_bits(dX)), g["dX"], "dX (r=0)")
+
+
+# ------------------------------------------------------------------ full-size layers, sampled outputs
+
+def oracle_sampled(W, rows, col_block=None):
+    """The oracle's quantization of a full-size weight: every constant (absmax,
+    c2, c1, mean) in full, codes and W_deq only for the sampled rows and, if
+    asked, for one 64-column block of every row."""
+    N, K = W.shape
+    absmax = oracle.blockwise_absmax(W)
+    c2, c1, mu = oracle.double_quant(absmax)
+    chat = oracle.dequant_constants(c2, c1, mu).reshape(N, K // 64)
+    codes_r, _ = oracle.quantize_codes(W[rows])
+    out = {"absmax": absmax, "c2": c2, "c1": c1, "mu": mu,
+           "codes": oracle.pack_nibbles(codes_r).reshape(len(rows), K // 2),
+           "wd_rows": oracle.dequant_codes(codes_r.reshape(len(rows), K), chat[rows])}
+    if col_block is not None:
+        kb = col_block
+        codes_c, _ = oracle.quantize_codes(np.ascontiguousarray(W[:, 64 * kb:64 * kb + 64]))
+        out["wd_cols"] = oracle.dequant_codes(codes_c.reshape(N, 64), chat[:, kb:kb + 1])
+    return out
+
+
+def adapter(d, r):
+    return (dev_bf16(d["A"]), dev_bf16(d["B"])) if r > 0 else (None, None)
+
+
+def check_fwd_sampled(d, ref, rows, Y, H, alpha, r, name, msel=None):
+    X = d["X"] if msel is None else d["X"][msel]
+    Yg = bf16_f64(host_bf16_bits(Y))[:, rows] if msel is None else bf16_f64(host_bf16_bits(Y))[msel][:, rows]
+    if r > 0:
+        Yr, Hr = oracle.linear_fwd(X, ref["wd_rows"], d["A"], d["B"][rows], alpha, r)
+        Hg = host(H) if msel is None else host(H)[msel]
+        check_close(Hg, Hr, f"H {name}")
+    else:
+        Yr, _ = oracle.linear_fwd_f64(bf16_f64(X), bf16_f64(ref["wd_rows"]), np.zeros((0, X.shape[1])),
+                                      np.zeros((len(rows), 0)), 0.0)
+    check_close(Yg, Yr, f"Y {name}")
+
+
+MLP_SHAPES = [("gate_up_11008x4096", 11008, 4096), ("down_4096x11008", 4096, 11008)]
+
+
+@pytest.mark.parametrize("name,N,K", MLP_SHAPES, ids=[s[0] for s in MLP_SHAPES])
+def test_forward_mlp_layer_full_size_sampled(name, N, K):
+    """Llama-7B-shaped MLP projections at M = 1, 16, 256 (decode and tiled
+    paths) in the launch configuration the benchmark uses; all constants and
+    512 sampled output columns against the oracle."""
+    shapes = [sh for sh in synth.MLP if sh.N == N and sh.K == K]
+    rows = np.sort(np.random.default_rng(N + K).choice(N, 512, replace=False))
+    d0 = synth.make_layer(shapes[0])
+    ref = oracle_sampled(d0["W"], rows)
+    q = gpu_quantize(d0["W"])
+    check_quantized(q, ref, rows)
+    for sh in shapes:
+        say(f"[mlp full] {sh.name}")
+        d = synth.make_layer(sh)
+        assert np.array_equal(d["W"], d0["W"])
+        A, B = adapter(d, sh.r)
+        Y, H = qa.linear_fwd(dev_bf16(d["X"]), q, A, B, sh.alpha)
+        torch.cuda.synchronize()
+        check_fwd_sampled(d, ref, rows, Y, H, sh.alpha, sh.r, sh.name)
+
+
+def test_train65b_layer_full_size_sampled():
+    """The 65B-scale training layer (W 22016 x 8192, M = 4096, r = 64) forward
+    and backward: all constants, sampled rows of W_deq, sampled outputs of Y,
+    dX (one 64-column block of every row), dA (the same columns) and dB (sampled
+    rows) against the oracle."""
+    sh = synth.TRAIN65B
+    M, N, K, r, alpha = sh.M, sh.N, sh.K, sh.r, sh.alpha
+    say(f"[65b] generating {sh.name}")
+    d = synth.make_layer(sh, with_dy=True)
+    rng = np.random.default_rng(65)
+    rows = np.sort(rng.choice(N, 128, replace=False))
+    kb = int(rng.integers(K // 64))
+    msel = np.sort(rng.choice(M, 256, replace=False))
+    ref = oracle_sampled(d["W"], rows, kb)
+    say("[65b] gpu")
+    q = gpu_quantize(d["W"])
+    check_quantized(q, ref, rows)
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    A, B = adapter(d, r)
+    Y, H = qa.linear_fwd(X, q, A, B, alpha)
+    dX, dA, dB = qa.linear_bwd(dY, X, q, A, B, alpha, H=H)
+    torch.cuda.synchronize()
+    del X, dY
+    say("[65b] forward check")
+    check_fwd_sampled(d, ref, rows, Y, H, alpha, r, "65b", msel=msel)
+    say("[65b] backward check")
+    cols = slice(64 * kb, 64 * kb + 64)
+    g1 = oracle.linear_bwd(d["dY"], np.ascontiguousarray(d["X"][:, cols]), ref["wd_cols"],
+                           np.ascontiguousarray(d["A"][:, cols]), d["B"], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(dX))[:, cols], g1["dX"], "dX (64-column block)")
+    check_close(bf16_f64(host_bf16_bits(dA))[:, cols], g1["dA"], "dA (64-column block)")
+    g2 = oracle.linear_bwd(np.ascontiguousarray(d["dY"][:, rows]), d["X"], ref["wd_rows"], d["A"],
+                           d["B"][rows], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(dB))[rows], g2["dB"], "dB (sampled rows)")
+
+
+@pytest.mark.parametrize("layer", [0, synth.DECODER_LAYERS - 1])
+def test_decoder_layer_full_size_sampled(layer):
+    """One layer of the 7B-shaped decoder (q, k, v, o, gate, up, down; LoRA
+    r = 16 on q and v only) at M = 1 and M = 512: all constants and 256 sampled
+    output columns per linear against the oracle."""
+    for mi, (mod, N, K, r) in enumerate(synth.DECODER_MODULES):
+        seed = synth.decoder_seed(layer, mi)
+        rows = np.sort(np.random.default_rng(seed).choice(N, 256, replace=False))
+        q = ref = None
+        for M in (1, 512):
+            sh = synth.LayerShape(f"decoder_l{layer}_{mod}_m{M}", M=M, N=N, K=K, r=r, seed_offset=seed)
+            say(f"[decoder] {sh.name}")
+            d = synth.make_layer(sh)
+            if q is None:
+                ref = oracle_sampled(d["W"], rows)
+                q = gpu_quantize(d["W"])
+                check_quantized(q, ref, rows)
+            A, B = adapter(d, r)
+            Y, H = qa.linear_fwd(dev_bf16(d["X"]), q, A, B, sh.alpha)
+            torch.cuda.synchronize()
+            check_fwd_sampled(d, ref, rows, Y, H, sh.alpha, r, sh.name)

@@ -370,6 +370,14 @@ def test_dequant_weight_definition():
             assert wd[n, k] == expect
     rows = np.array([3, 0, 11])
     assert np.array_equal(o.dequant_weight(q["codes"], q["c2"], q["c1"], q["mu"], 12, 512, rows=rows), wd[rows])
+    # a 64-column slice quantized on its own has the same blocks, codes and W_deq columns
+    for kb in (0, 5):
+        sl = np.ascontiguousarray(W[:, 64 * kb:64 * kb + 64])
+        codes_c, absmax_c = o.quantize_codes(sl)
+        assert np.array_equal(absmax_c, q["absmax"].reshape(12, 8)[:, kb])
+        assert np.array_equal(codes_c.reshape(12, 64), codes[:, 64 * kb:64 * kb + 64])
+        cols = o.dequant_codes(codes_c.reshape(12, 64), chat[:, kb:kb + 1])
+        assert np.array_equal(cols, wd[:, 64 * kb:64 * kb + 64])
 
 
 # ---------------------------------------------------------------- forward / backward
