@@ -9,9 +9,10 @@ layer (one kernel launch); the timed steps are captured in a HIP graph and
 replayed once between HIP events, so host launch cost stays out of the figure.
 
 Also measured in the same run and reported under "extra": M = 4 and 16 on the
-decode layer, the Llama-7B MLP shapes at M = 1, the 65B-scale training layer
-(22016 x 8192, M = 4096) forward and backward in TFLOP/s, and quantize +
-double quant throughput.  The CPU oracle is timed on a bounded sample of the
+decode layer, the Llama-7B MLP shapes at M = 1, 16 and 256, the 65B-scale
+training layer (22016 x 8192, M = 4096) forward and backward in TFLOP/s,
+quantize + double quant throughput, and the 7B-shaped decoder's 224 linears
+(quantize all, then one forward pass at M = 1 and at M = 512).  The CPU oracle is timed on a bounded sample of the
 headline workload (`cpu_baseline`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--eager] [--no-cpu]
@@ -184,6 +185,56 @@ def bench_quantize(torch, qa, N, K, steps, warmup):
             "double_quant_GBps": (5 * n_c2 + 4 * n_c1) / ms_dq / 1e6}
 
 
+def bench_decoder(torch, qa, reps, seed=5):
+    """The 7B-shaped decoder's linears (32 layers x q, k, v, o, gate, up, down;
+    LoRA r = 16 on q and v): quantize + double quant all of them, then one
+    forward pass over all 224 linears at M = 1 and at M = 512."""
+    import synth
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    layers = []
+    ms_quant = 0.0
+    params = 0
+    for _ in range(synth.DECODER_LAYERS):
+        for mod, N, K, r in synth.DECODER_MODULES:
+            W = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            q = qa.quantize(W)
+            e1.record()
+            torch.cuda.synchronize()
+            ms_quant += e0.elapsed_time(e1)
+            params += N * K
+            del W
+            A = B = None
+            if r:
+                A = (torch.randn((r, K), generator=gen, device="cuda") / K).to(torch.bfloat16)
+                B = (torch.randn((N, r), generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+            layers.append((q, A, B, N, K, r))
+    log(f"[bench] decoder: {len(layers)} linears quantized, {ms_quant:.1f} ms")
+    res = {"params": params, "quantize_ms": ms_quant,
+           "quantize_GBps": params * (4 + 0.5 + 4 / 64) / ms_quant / 1e6}
+    for M in (1, 512):
+        xs = {K: torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16) for K in (4096, 11008)}
+        ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N in (4096, 11008)}
+        ws = qa.fwd_workspace(M, 11008, 11008, 16, "cuda")
+
+        def one_pass(i):
+            for q, A, B, N, K, r in layers:
+                qa.qlora_linear_fwd(xs[K], q.codes, q.c2, q.c1, q.mean, A, B, 16.0, ys[N], None, ws, N)
+
+        ms = (timed_graph if M == 1 else timed_eager)(torch, one_pass, reps, 1)
+        byts = sum(fwd_bytes(M, N, K, r) for _, _, _, N, K, r in layers)
+        fl = sum(fwd_flops(M, N, K, r) for _, _, _, N, K, r in layers)
+        res[f"m{M}"] = {"ms": ms, "GBps": byts / ms / 1e6, "TFLOPs": fl / ms / 1e9,
+                        "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS,
+                        "mfma_frac": fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, "bytes": byts, "flops": fl}
+        log(f"[bench] decoder pass M={M}: {ms:.3f} ms")
+        del xs, ys, ws
+    del layers
+    return res
+
+
 # ----------------------------------------------------------------------------- traffic from counters
 
 def kernel_source_hash(name):
@@ -296,10 +347,12 @@ def main():
             extra[f"decode_4096x4096_m{M}"] = res
             log(f"[bench] M={M}: {res['ms'] * 1e3:.2f} us/call, {res['GBps']:.0f} GB/s")
         for nm, n, k in (("mlp_gate_up_11008x4096", 11008, 4096), ("mlp_down_4096x11008", 4096, 11008)):
-            cp = max(2, int(2 * MALL_BYTES / fwd_bytes(1, n, k, r)) + 1)
-            res = bench_fwd(torch, qa, 1, n, k, r, args.steps, args.warmup, cp)
-            extra[f"{nm}_m1"] = res
-            log(f"[bench] {nm} M=1: {res['ms'] * 1e3:.2f} us/call, {res['GBps']:.0f} GB/s")
+            for M in (1, 16, 256):
+                cp = max(2, int(2 * MALL_BYTES / fwd_bytes(M, n, k, r)) + 1)
+                res = bench_fwd(torch, qa, M, n, k, r, args.steps, args.warmup, cp)
+                extra[f"{nm}_m{M}"] = res
+                log(f"[bench] {nm} M={M}: {res['ms'] * 1e3:.2f} us/call, {res['GBps']:.0f} GB/s, "
+                    f"{res['TFLOPs']:.1f} TFLOP/s")
         Ml, Nl, Kl = 4096, 22016, 8192
         res = bench_fwd(torch, qa, Ml, Nl, Kl, r, 10, 2, 3, graph=False)
         extra["train65b_22016x8192_m4096_fwd"] = res
@@ -310,6 +363,12 @@ def main():
         res = bench_quantize(torch, qa, Nl, Kl, 5, 1)
         extra["quantize_22016x8192"] = res
         log(f"[bench] quantize: {res['quantize_GBps']:.0f} GB/s, double quant {res['double_quant_ms'] * 1e3:.1f} us")
+        torch.cuda.empty_cache()
+        res = bench_decoder(torch, qa, 20)
+        extra["decoder_7b_224_linears"] = res
+        log(f"[bench] 7B decoder: quantize {res['params'] / 1e9:.2f}B params in {res['quantize_ms']:.1f} ms; "
+            f"fwd M=1 {res['m1']['ms']:.3f} ms ({res['m1']['GBps']:.0f} GB/s), "
+            f"M=512 {res['m512']['ms']:.3f} ms ({res['m512']['TFLOPs']:.0f} TFLOP/s)")
         torch.cuda.empty_cache()
 
     traffic = recorded_traffic("qlora_decode_kernel_decode_4096x4096_m1.md", "decode.hip")

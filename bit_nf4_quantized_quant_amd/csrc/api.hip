@@ -11,7 +11,8 @@
 namespace qlora {
 size_t decode_workspace_bytes(int64_t M, int64_t r);
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s);
-hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s);
+size_t gemm_fwd_scratch_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int64_t r, float* H,
                             float* scratch, hipStream_t s);
 size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r);
@@ -59,7 +60,10 @@ bool use_decode(int64_t M, int64_t N, int64_t K) {
 
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (use_decode(M, N, K)) return round256(decode_workspace_bytes(M, r));
-  return kFwdReserved + round256((size_t)M * r * sizeof(float)) + round256(lora_down_scratch_bytes(M, K, r));
+  // H, then one scratch region used first by the LoRA-down split-K partials
+  // and then by the main product's split-K partials
+  const size_t scratch = std::max(lora_down_scratch_bytes(M, K, r), gemm_fwd_scratch_bytes(M, N, K));
+  return kFwdReserved + round256((size_t)M * r * sizeof(float)) + round256(scratch);
 }
 
 }  // namespace
@@ -165,13 +169,13 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
   hipStream_t s = (hipStream_t)stream;
   if (use_decode(M, N, K)) return status_of(launch_decode_fwd(a, s));
   char* ws = reinterpret_cast<char*>(workspace) + kFwdReserved;
+  float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
   if (r > 0) {
     float* H = H_out ? H_out : reinterpret_cast<float*>(ws);
-    float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
     a.H = H;
     if (launch_lora_down(X, M, K, A, r, H, scratch, s) != hipSuccess) return QLORA_EHIP;
   }
-  return status_of(launch_gemm_fwd(a, s));
+  return status_of(launch_gemm_fwd(a, scratch, s));
 }
 
 size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -188,15 +192,17 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N
   if (K == 0) return QLORA_ESHAPE;
   if ((st = check_weight(codes, c2, c1, mean))) return st;
   if (!workspace) return QLORA_EINVAL;
-  if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_EINVAL;
-  if (M > 0 && (!dY || !X)) return QLORA_EINVAL;
+  // pointers to empty tensors may be NULL (dY, B, dB when N == 0; dY, X when M == 0)
+  if (r > 0 && (!A || !dA || (N > 0 && (!B || !dB)))) return QLORA_EINVAL;
+  if (M > 0 && (!X || (N > 0 && !dY))) return QLORA_EINVAL;
   if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(dA, 16) ||
       !aligned(dB, 2) || !aligned(workspace, 256))
     return QLORA_EINVAL;
   if (H && !aligned(H, 4)) return QLORA_EINVAL;
   if (dX && !aligned(dX, 16)) return QLORA_EINVAL;
   if (workspace_bytes < gemm_bwd_workspace_bytes(M, N, K, r)) return QLORA_EINVAL;
-  if (N == 0) return QLORA_OK;
+  // N == 0 still runs: the sums over N are empty, so dX and dA are written as zeros
+  if (r == 0 && (M == 0 || !dX)) return QLORA_OK;  // no adapter and no input gradient to write
 
   BwdArgs a;
   a.dY = dY;

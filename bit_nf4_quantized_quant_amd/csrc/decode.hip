@@ -27,9 +27,11 @@
 //     stores bf16 Y.  Workgroups are dispatched in index order, so the
 //     LoRA-down tiles are running or done before any weight tile waits.
 //
-// Launch epochs: every launch adds exactly 2^20 to each counter it uses,
-// however many workgroups share the counter, so a workgroup's own counter
-// update returns (epoch << 20) + something < 2^20, which names the launch.
+// Launch epochs: every launch adds exactly 2^20 to each of the 9 counters,
+// however many workgroups share a counter, so a workgroup's own counter
+// update returns (epoch << 20) + something < 2^20, which names the launch
+// (the same epoch on every counter, whatever mix of shapes and ranks, with or
+// without adapter, used the workspace before).
 // LoRA-down tiles store each partial as one 64-bit word (epoch tag, value),
 // so a partial is valid exactly when its tag is this launch's; nothing has to
 // be reset or waited for on the producer side.  Weight tiles spread their
@@ -476,6 +478,9 @@ __global__ void __launch_bounds__(kThreads, 4) qlora_decode_kernel(DecodeParams 
       for (uint32_t s = (uint32_t)wt + nw; s < (uint32_t)kSlots; s += nw)
         add_ctr(reinterpret_cast<uint64_t*>(p.ws + 128 * (1 + s)), kEpoch);
     }
+    // without an adapter there are no LoRA-down tiles: advance their counter
+    // here so that every launch moves every counter by one epoch
+    if (p.n_htiles == 0 && wt == 0) add_ctr(reinterpret_cast<uint64_t*>(p.ws), kEpoch);
   }
 
   __shared__ uint32_t wtag;

@@ -527,6 +527,8 @@ struct FwdGemmParams {
   bool b_vec;
   float scale;
   uint16_t* Y;
+  float* part;          // split-K partials [splits][M][N] (splits > 1)
+  int splits, steps_per_split;
   int mtiles, ntiles, gm;
   Nf4Table tab;
 };
@@ -539,25 +541,38 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
   lds_t* sb = smem + 2 * BM * PITCH;
   float* lut = reinterpret_cast<float*>(sb + 2 * BN * PITCH);
   load_lut(lut, p.tab);
+  const int tiles = p.mtiles * p.ntiles;
+  const int split = (int)blockIdx.x / tiles;
   int mi, ni;
-  tile_of((int)blockIdx.x, p.mtiles, p.ntiles, p.gm, mi, ni);
+  tile_of((int)blockIdx.x - split * tiles, p.mtiles, p.ntiles, p.gm, mi, ni);
   const int64_t m0 = (int64_t)mi * BM, n0 = (int64_t)ni * BN;
+  const int ksteps = (int)(p.K / BK);
+  const int kt0 = split * p.steps_per_split, kt1 = min(ksteps, kt0 + p.steps_per_split);
   Acc<BM, BN, WN> acc;
   zero(acc);
   __syncthreads();
   {
     RowsBf16<BM, T> la{p.X, p.K, (int)min<int64_t>(BM, p.M - m0), (int)p.K, m0, true};
     Nf4Rows<BN, T> lb{p.codes, p.c2, p.c1, *p.mean, p.K, (int)min<int64_t>(BN, p.N - n0), n0, lut};
-    run_phase<BM, BN, WN>(la, lb, 0, (int)(p.K / BK), sa, sb, acc);
+    run_phase<BM, BN, WN>(la, lb, kt0, kt1, sa, sb, acc);
   }
-  lora_tail<BM, BN, WN>(
-      acc, p.r,
-      [&](int i, int k0) { return frag_f32_row(p.H, p.r, m0 + i, p.M, k0, p.r, p.scale); },
-      [&](int j, int k0) { return frag_bf16_row(p.B, p.r, n0 + j, p.N, k0, p.r, p.b_vec); });
-  for_each_out(acc, [&](int i, int j, float v) {
-    const int64_t m = m0 + i, n = n0 + j;
-    if (m < p.M && n < p.N) p.Y[m * p.N + n] = to_bf16(v);
-  });
+  if (split == 0)
+    lora_tail<BM, BN, WN>(
+        acc, p.r,
+        [&](int i, int k0) { return frag_f32_row(p.H, p.r, m0 + i, p.M, k0, p.r, p.scale); },
+        [&](int j, int k0) { return frag_bf16_row(p.B, p.r, n0 + j, p.N, k0, p.r, p.b_vec); });
+  if (p.splits == 1) {
+    for_each_out(acc, [&](int i, int j, float v) {
+      const int64_t m = m0 + i, n = n0 + j;
+      if (m < p.M && n < p.N) p.Y[m * p.N + n] = to_bf16(v);
+    });
+  } else {
+    float* out = p.part + (int64_t)split * p.M * p.N;
+    for_each_out(acc, [&](int i, int j, float v) {
+      const int64_t m = m0 + i, n = n0 + j;
+      if (m < p.M && n < p.N) out[m * p.N + n] = v;
+    });
+  }
 }
 
 // Generic bf16 x bf16 product with fp32 output (split-K partials or final):
@@ -621,6 +636,8 @@ struct DxParams {
   const float* dH;
   const uint16_t* A;
   uint16_t* dX;
+  float* part;          // split-K partials [splits][M][K] (splits > 1)
+  int splits, steps_per_split;
   int mtiles, ntiles, gm;
   Nf4Table tab;
 };
@@ -633,25 +650,38 @@ __global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
   lds_t* sb = smem + 2 * BM * PITCH;
   float* lut = reinterpret_cast<float*>(sb + 2 * BN * PITCH);
   load_lut(lut, p.tab);
+  const int tiles = p.mtiles * p.ntiles;
+  const int split = (int)blockIdx.x / tiles;
   int mi, ki;
-  tile_of((int)blockIdx.x, p.mtiles, p.ntiles, p.gm, mi, ki);
+  tile_of((int)blockIdx.x - split * tiles, p.mtiles, p.ntiles, p.gm, mi, ki);
   const int64_t m0 = (int64_t)mi * BM, k0 = (int64_t)ki * BN;
+  const int nsteps = (int)((p.N + BK - 1) / BK);
+  const int nt0 = split * p.steps_per_split, nt1 = min(nsteps, nt0 + p.steps_per_split);
   Acc<BM, BN, WN> acc;
   zero(acc);
   __syncthreads();
   {
     RowsBf16<BM, T> la{p.dY, p.N, (int)min<int64_t>(BM, p.M - m0), (int)p.N, m0, (p.N % 8) == 0};
     Nf4Cols<BN, T> lb{p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut};
-    run_phase<BM, BN, WN>(la, lb, 0, (int)((p.N + BK - 1) / BK), sa, sb, acc);
+    run_phase<BM, BN, WN>(la, lb, nt0, nt1, sa, sb, acc);
   }
-  lora_tail<BM, BN, WN>(
-      acc, p.r,
-      [&](int i, int kk) { return frag_f32_row(p.dH, p.r, m0 + i, p.M, kk, p.r, 1.0f); },
-      [&](int j, int kk) { return frag_bf16_col(p.A, p.K, k0 + j, p.K, kk, p.r); });
-  for_each_out(acc, [&](int i, int j, float v) {
-    const int64_t m = m0 + i, k = k0 + j;
-    if (m < p.M && k < p.K) p.dX[m * p.K + k] = to_bf16(v);
-  });
+  if (split == 0)
+    lora_tail<BM, BN, WN>(
+        acc, p.r,
+        [&](int i, int kk) { return frag_f32_row(p.dH, p.r, m0 + i, p.M, kk, p.r, 1.0f); },
+        [&](int j, int kk) { return frag_bf16_col(p.A, p.K, k0 + j, p.K, kk, p.r); });
+  if (p.splits == 1) {
+    for_each_out(acc, [&](int i, int j, float v) {
+      const int64_t m = m0 + i, k = k0 + j;
+      if (m < p.M && k < p.K) p.dX[m * p.K + k] = to_bf16(v);
+    });
+  } else {
+    float* out = p.part + (int64_t)split * p.M * p.K;
+    for_each_out(acc, [&](int i, int j, float v) {
+      const int64_t m = m0 + i, k = k0 + j;
+      if (m < p.M && k < p.K) out[m * p.K + k] = v;
+    });
+  }
 }
 
 // Skinny-product loaders with a per-tile origin, built on the loaders above.
@@ -726,7 +756,8 @@ size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r) {
 
 // Launch a tiled kernel with dynamic LDS (raising the per-kernel limit once).
 template <class Kern, class P>
-hipError_t launch_tiled(Kern kern, int threads, size_t lds, int mtiles, int ntiles, P& p, hipStream_t s) {
+hipError_t launch_tiled(Kern kern, int threads, size_t lds, int mtiles, int ntiles, int splits, P& p,
+                        hipStream_t s) {
   static bool attr_set = false;  // per instantiation; setting it twice is harmless
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -737,11 +768,41 @@ hipError_t launch_tiled(Kern kern, int threads, size_t lds, int mtiles, int ntil
   p.mtiles = mtiles;
   p.ntiles = ntiles;
   p.gm = mtiles >= 8 ? mtiles / 8 : 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(mtiles * ntiles)), dim3(threads), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(mtiles * ntiles * splits)), dim3(threads), lds, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
+// Tile size and split-K for an M x N output over `steps` 64-deep steps:
+// 256 x 256 tiles (8 waves, one workgroup per CU) when they alone give every
+// CU a tile, else 128 x 128 tiles (4 waves, two workgroups per CU), split
+// along the reduction until about 512 workgroups run, keeping at least 8
+// steps per split.
+struct GemmPlan {
+  int tile, mtiles, ntiles, splits, steps_per_split;
+};
+
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t steps) {
+  GemmPlan g;
+  const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
+  g.tile = (M >= 256 && t256 >= 256) ? 256 : 128;
+  g.mtiles = (int)cdiv(M, g.tile);
+  g.ntiles = (int)cdiv(N, g.tile);
+  const int64_t tiles = (int64_t)g.mtiles * g.ntiles;
+  int sp = 1;
+  if (g.tile == 128)
+    while (tiles * sp < 512 && steps / (sp * 2) >= 8 && sp < 16) sp *= 2;
+  g.steps_per_split = std::max(1, (int)cdiv(steps, sp));   // an empty reduction is one empty split
+  g.splits = std::max(1, (int)cdiv(steps, g.steps_per_split));
+  return g;
+}
+
+size_t gemm_fwd_scratch_bytes(int64_t M, int64_t N, int64_t K) {
+  const GemmPlan g = gemm_plan(M, N, K / BK);
+  return g.splits > 1 ? (size_t)g.splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
+  const GemmPlan g = gemm_plan(a.M, a.N, a.K / BK);
   FwdGemmParams p;
   p.X = a.X;
   p.M = a.M;
@@ -757,12 +818,21 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   p.b_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
   p.scale = a.scale;
   p.Y = a.Y;
+  p.part = scratch;
+  p.splits = g.splits;
+  p.steps_per_split = g.steps_per_split;
   p.tab = nf4_table();
-  if (a.M >= 256)
-    return launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), (int)cdiv(a.M, 256),
-                        (int)cdiv(a.N, 256), p, s);
-  return launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), (int)cdiv(a.M, 128),
-                      (int)cdiv(a.N, 128), p, s);
+  hipError_t e;
+  if (g.tile == 256)
+    e = launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits,
+                     p, s);
+  else
+    e = launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits,
+                     p, s);
+  if (e != hipSuccess || g.splits == 1) return e;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.N, 256), 4096)),
+                     dim3(256), 0, s, scratch, g.splits, (int64_t)(a.M * a.N), 1.0f, a.Y, (float*)nullptr);
+  return hipGetLastError();
 }
 
 // Backward workspace: H (if recomputed), dH, and split-K partials.
@@ -782,6 +852,8 @@ static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   b.off_part = b.off_dH + al((size_t)M * r * 4);
   size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * r, (size_t)b.s_da * r * K}) * 4;
   part = std::max(part, lora_down_scratch_bytes(M, K, r));
+  const GemmPlan g = gemm_plan(M, K, (N + BK - 1) / BK);
+  if (g.splits > 1) part = std::max(part, (size_t)g.splits * M * K * sizeof(float));
   b.bytes = b.off_part + al(part);
   return b;
 }
@@ -815,7 +887,7 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
                          (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
     }
     // dB = s dY^T H : rows n, cols j, reduction m
-    {
+    if (a.N > 0) {
       SColsBf16<128> la;
       la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
       SColsF32<64> lb;
@@ -850,14 +922,21 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     p.dH = dH;
     p.A = a.A;
     p.dX = a.dX;
+    const GemmPlan g = gemm_plan(a.M, a.K, (a.N + BK - 1) / BK);
+    p.part = part;
+    p.splits = g.splits;
+    p.steps_per_split = g.steps_per_split;
     p.tab = nf4_table();
-    if (a.M >= 256)
-      e = launch_tiled(dx_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), (int)cdiv(a.M, 256),
-                       (int)cdiv(a.K, 256), p, s);
+    if (g.tile == 256)
+      e = launch_tiled(dx_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits,
+                       p, s);
     else
-      e = launch_tiled(dx_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), (int)cdiv(a.M, 128),
-                       (int)cdiv(a.K, 128), p, s);
+      e = launch_tiled(dx_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits,
+                       p, s);
     if (e != hipSuccess) return e;
+    if (g.splits > 1)
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.K, 256), 4096)),
+                         dim3(256), 0, s, part, g.splits, (int64_t)(a.M * a.K), 1.0f, a.dX, (float*)nullptr);
   }
   return hipGetLastError();
 }

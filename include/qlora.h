@@ -28,7 +28,8 @@
  *     synchronization, as for any HIP kernel.
  *   - Inputs must be finite; non-finite inputs give unspecified results.
  *   - Zero-sized problems (N, M or K equal to 0, as allowed per entry point)
- *     are accepted and queue nothing.
+ *     are accepted; they queue nothing except where an output is a sum over
+ *     the empty extent (the backward's gradients), which is then written as 0.
  *   - Alignment: pointers to fp32/bf16 matrices and to the packed codes must be
  *     16-byte aligned; absmax, c1, mean and H need 4-byte alignment; c2 and B
  *     need only their natural alignment.
@@ -164,6 +165,7 @@ size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  *   dX  out  bf16 [M,K] (may be NULL to skip the input gradient)
  *   dA  out  bf16 [r,K];  dB out bf16 [N,r]
  *   r = 0 (no adapter): only dX = dY W_deq; A, B, H, dA, dB may be NULL
+ *   Empty sums give zeros: M = 0 writes dA = dB = 0; N = 0 writes dX = dA = 0
  *   workspace  qlora_linear_bwd_workspace(M,N,K,r) bytes, 256-B aligned
  *              (contents on entry do not matter)
  */

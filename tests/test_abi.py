@@ -150,9 +150,9 @@ def test_bwd_validation():
     assert call(dB=None) == _lib.QLORA_EINVAL
     assert call(dX=MIS) == _lib.QLORA_EINVAL
     assert call(wsb=need - 1) == _lib.QLORA_EINVAL
-    assert call(N=0) == _lib.QLORA_OK
     assert call(A=None) == _lib.QLORA_EINVAL
-    assert call(r=0, A=None, B=None, dA=None, dB=None, N=0) == _lib.QLORA_OK
+    # no adapter and an empty batch: nothing to compute, nothing queued
+    assert call(r=0, A=None, B=None, dA=None, dB=None, M=0, dY=None, X=None) == _lib.QLORA_OK
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -208,25 +208,35 @@ def test_forward_one_hot_rows_select_weight_columns():
 
 
 def test_forward_deterministic_and_workspace_reusable():
-    """Repeated calls give identical bits, and one workspace serves any mix of shapes."""
+    """Repeated calls give identical bits, and one workspace serves any mix of
+    shapes, ranks and layers without adapter (r = 0)."""
     ws = qa.fwd_workspace(64, 2048, 1024, 72, "cuda")
     layers = {}
     for M, N, K, r in ((1, 512, 512, 16), (16, 512, 512, 16), (64, 512, 512, 16), (3, 2048, 1024, 72),
-                       (1, 100, 128, 8), (16, 2048, 1024, 72)):
+                       (1, 100, 128, 8), (2, 512, 512, 0), (16, 2048, 1024, 72), (5, 300, 256, 0)):
         d = synth.make_layer(synth.LayerShape("t", M=M, N=N, K=K, r=r, seed_offset=900 + M + N + r))
         layers[(M, N, K, r)] = (d, gpu_quantize(d["W"]))
     first = {}
     for rep in range(3):
         for key, (d, q) in layers.items():
-            Y, H = run_fwd(d, q, 16.0, key[3], ws)
+            r = key[3]
+            A, B = adapter(d, r)
+            Y, H = qa.linear_fwd(dev_bf16(d["X"]), q, A, B, 16.0, workspace=ws)
+            torch.cuda.synchronize()
             if rep == 0:
                 first[key] = (Y, H)
-                _, wd = oracle_layer(d, 16.0, key[3])
-                Yr, _ = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], 16.0, key[3])
+                _, wd = oracle_layer(d, 16.0, max(r, 1))
+                if r:
+                    Yr, _ = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], 16.0, r)
+                else:
+                    Yr, _ = oracle.linear_fwd_f64(bf16_f64(d["X"]), bf16_f64(wd), np.zeros((0, key[2])),
+                                                  np.zeros((key[1], 0)), 0.0)
                 check_close(bf16_f64(host_bf16_bits(Y)), Yr, f"Y {key}")
             else:
                 assert torch.equal(Y.view(torch.int16), first[key][0].view(torch.int16)), key
-                assert torch.equal(H, first[key][1]), key
+                assert (H is None) == (r == 0)
+                if r:
+                    assert torch.equal(H, first[key][1]), key
     # the decode kernel's bounded wait never timed out
     assert int(ws[128 * 9:128 * 9 + 4].view(torch.int32)[0]) == 0
 
@@ -272,6 +282,24 @@ def test_backward_parity(M, N, K, r):
     torch.cuda.synchronize()
     assert torch.equal(dA2.view(torch.int16), dA.view(torch.int16))
     assert torch.equal(dB2.view(torch.int16), dB.view(torch.int16))
+
+
+def test_backward_no_outputs_gives_zero_input_grads():
+    """N = 0: the sums over the output dimension are empty, so dX = 0 and dA = 0."""
+    M, K, r = 40, 128, 8
+    d = synth.make_layer(synth.LayerShape("t", M=M, N=1, K=K, r=r, seed_offset=4343))
+    q = qa.QuantizedWeight(0, K, torch.zeros((1, K // 2), dtype=torch.uint8, device="cuda"), None,
+                           torch.zeros(1, dtype=torch.uint8, device="cuda"),
+                           torch.zeros(1, dtype=torch.float32, device="cuda"),
+                           torch.zeros(1, dtype=torch.float32, device="cuda"))
+    X = dev_bf16(d["X"])
+    dY = torch.zeros((M, 0), dtype=torch.bfloat16, device="cuda")
+    A = dev_bf16(d["A"])
+    B = torch.zeros((0, r), dtype=torch.bfloat16, device="cuda")
+    dX, dA, dB = qa.linear_bwd(dY, X, q, A, B, 16.0)
+    torch.cuda.synchronize()
+    assert dB.numel() == 0
+    assert float(dX.float().abs().sum()) == 0.0 and float(dA.float().abs().sum()) == 0.0
 
 
 def test_backward_empty_batch_gives_zero_lora_grads():
