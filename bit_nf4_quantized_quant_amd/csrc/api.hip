@@ -26,6 +26,8 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 31;       // every extent must fit a 32-bit grid index
 constexpr int64_t kMaxElems = int64_t(1) << 40;     // elements of any one tensor
 constexpr int64_t kDecodeMaxM = 16;
+constexpr int64_t kMaxRowLen = int64_t(1) << 23;        // K, N: 256 rows of a tile within 4 GiB
+constexpr int64_t kMaxWeightBytes = int64_t(1) << 32;   // packed codes of one weight
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -40,6 +42,8 @@ int check_layer(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (r > 128) return QLORA_ESHAPE;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return QLORA_ESHAPE;
   if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return QLORA_ESHAPE;
+  // the products address a tile's rows and the packed weight with 32-bit offsets
+  if (K >= kMaxRowLen || N >= kMaxRowLen || N * K / 2 >= kMaxWeightBytes) return QLORA_ESHAPE;
   return QLORA_OK;
 }
 

@@ -18,6 +18,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 64;     // weights per first-level constant
 constexpr int kDqBlock = 256;  // constants per second-level constant
 
+// --------------------------------------------------------------- buffer resources
+
+// A raw buffer over `bytes` bytes at `base`: loads take a 32-bit byte offset
+// (vector part + scalar part + immediate) and return zero past the end.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // --------------------------------------------------------------- bf16
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -26,6 +26,7 @@
 // A transposed source is read as 4 x 8 patches (4 rows of 8 contiguous
 // elements) and written to LDS as 8 rows of 4 reduction elements.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -42,6 +43,14 @@ typedef uint16_t lds_t;
 __device__ __forceinline__ void st_lds16(lds_t* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st_lds8(lds_t* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Byte b of w (b a constant): one instruction each.
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int b) {
+  return __builtin_amdgcn_perm(0u, w, 0x0C0C0C00u | (uint32_t)b);   // v_perm_b32: byte b, zeros above
+}
+
+// 64-bit integer minimum (integer instructions only)
+__device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
 __device__ __forceinline__ uint32_t lo16(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
@@ -285,6 +294,190 @@ struct Nf4Rows {
   }
 };
 
+// ---------------------------------------------------------------- branch-free loaders
+
+// Loaders of the main products read through buffer resources based at the
+// tile's first row, so offsets stay 32-bit for any tensor and the loops carry
+// no bounds branches: tile rows past the valid ones repeat the last valid row
+// (their outputs are never stored) and reads past a resource's end return 0.
+// (Arguments are wave-uniform; readfirstlane states it so that the resource
+// lives in scalar registers.)
+__device__ __forceinline__ rsrc_t tile_rsrc(const void* base, int64_t off_bytes, int64_t total_bytes) {
+  const int64_t rem = total_bytes - off_bytes;
+  const uint64_t a = reinterpret_cast<uint64_t>(static_cast<const char*>(base) + off_bytes);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)lmin(rem, 0xFFFFFFFFll));
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
+}
+
+// Fragment-major LDS tiles (the pipelined products): an R x 64 operand tile
+// is a set of 1 KB blocks, block (s, g) for 16-deep sub-step s (0..3) and
+// row group g (32 rows).  A block holds the 64 bf16x8 operands that the lanes
+// of a 32x32x16 MFMA take: lane l's operand (row 32 g + l % 32, reduction
+// 16 s + 8 h .. +7 with h = l / 32) sits in 16-byte slot
+// 32 h + (l % 32 + 2 s + h) % 32.  A fragment read is two contiguous
+// (rotated) 512-byte halves; the rotation also spreads the writes over all
+// banks when 8 lanes store the 8 chunks of one row (the coalesced order of the
+// global loads) or 2 lanes per row store one chunk each.  No padding is
+// needed.
+template <int R>
+__device__ __forceinline__ int frag_slot(int row, int c8) {   // c8: 8-element chunk 0..7 of the step
+  const int s = c8 >> 1, half = c8 & 1;
+  const int pos = 32 * half + (((row & 31) + 2 * s + half) & 31);
+  return ((s * (R / 32) + (row >> 5)) * 64 + pos) * 8;   // in bf16 elements
+}
+// the slot lane l reads in sub-step s
+__device__ __forceinline__ int frag_read_slot(int lane, int s) {
+  return 32 * (lane >> 5) + (((lane & 31) + 2 * s + (lane >> 5)) & 31);
+}
+
+// bf16 rows [rows][ld], reduction contiguous (X, dY).  kVec: ld % 8 == 0, so a
+// row's 8-element chunks are 16-byte aligned.  A reduction tail past the row
+// end reads the next row (or zero past the tensor): finite values that the
+// other operand's zeros cancel.  kDepth: steps in flight in registers.
+template <int R, int T, bool kVec, int kDepth = 2>
+struct XRows {
+  static constexpr int kChunks = R * BK / 8 / T;   // 16-byte chunks per thread: chunk c is
+  static_assert(kChunks % 4 == 0, "whole chunks per quarter step");   // row (tid + c T) / 8, part (tid + c T) % 8
+  rsrc_t rs;
+  uint32_t off[kChunks];
+  u32x4 reg[kDepth][kChunks];
+
+  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld, int64_t total_rows, int64_t row0) {
+    const int rows = (int)lmin(R, total_rows - row0);
+    rs = tile_rsrc(src, row0 * ld * 2, total_rows * ld * 2);
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = threadIdx.x + c * T;
+      off[c] = (uint32_t)(((int64_t)min(idx >> 3, rows - 1) * ld + (idx & 7) * 8) * 2);
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void load(int kt) {
+    const int sof = kt * BK * 2;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      if (kVec) {
+        reg[S][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[c], sof, 0));
+      } else {
+        uint32_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, off[c] + 2 * q, sof, 0);
+        reg[S][c] = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+      }
+    }
+  }
+  // quarter P of the next step (register slot S when two steps are in flight)
+  template <int S, int P>
+  __device__ __forceinline__ void store_part(lds_t* t) const {
+    constexpr int s = kDepth == 2 ? S : 0;
+#pragma unroll
+    for (int c = P; c < kChunks; c += 4) {
+      const int idx = threadIdx.x + c * T;
+      st_lds16(t + frag_slot<R>(idx >> 3, idx & 7), reg[s][c]);
+    }
+  }
+  // pipeline hooks: step kt0 into LDS buffer t (and the following step in flight)
+  __device__ __forceinline__ void prologue(int kt0, int last, lds_t* t) {
+    load<0>(kt0);
+    store_part<0, 0>(t);
+    store_part<0, 1>(t);
+    store_part<0, 2>(t);
+    store_part<0, 3>(t);
+    if (kDepth == 2) load<kDepth - 1>(min(kt0 + 1, last));
+  }
+  // at the start of step kt: issue the loads of the step kDepth ahead into slot S
+  template <int S>
+  __device__ __forceinline__ void ahead(int kt, int last) {
+    load<kDepth == 2 ? S : 0>(min(kt + kDepth, last));
+  }
+};
+
+// NF4 weight rows [n][k] (forward): unit u of a thread is half a block (32
+// codes, one constant) of row (tid + u T) / 2, expanded to
+// bf16( fp32(level * c_hat) ), bit-exact with W_deq.
+template <int R, int T>
+struct WRows {
+  static constexpr int kUnits = R * 2 / T;
+  rsrc_t rc, r2, r1;
+  uint32_t coff[kUnits];   // code bytes of this half-block at kt = 0 (tile-relative)
+  uint32_t boff[kUnits];   // its block index at kt = 0 (tile-relative)
+  uint32_t bglob[kUnits];  // its global block index at kt = 0
+  float mean;
+  const float* lut;
+  u32x4 q[2][kUnits];      // two steps in flight
+  uint32_t c2v[2][kUnits];
+  float c1v[2][kUnits];
+  float chat[kUnits];      // constants of the step being stored
+
+  __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* c2, const float* c1, float mu,
+                                       int64_t N, int64_t K, int64_t row0, const float* lut_) {
+    const int rows = (int)lmin(R, N - row0);
+    const int64_t nb = K / BK;
+    rc = tile_rsrc(codes, row0 * (K / 2), N * (K / 2));
+    r2 = tile_rsrc(c2, row0 * nb, N * nb);
+    r1 = tile_rsrc(c1, 0, ((N * nb + 255) / 256) * 4);
+    mean = mu;
+    lut = lut_;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int idx = threadIdx.x + u * T;
+      const int rr = min(idx >> 1, rows - 1), h = idx & 1;
+      coff[u] = (uint32_t)(rr * (K / 2) + h * 16);
+      boff[u] = (uint32_t)(rr * nb);
+      bglob[u] = (uint32_t)((row0 + rr) * nb);
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void load(int kt) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      q[S][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff[u], kt * 32, 0));
+      c2v[S][u] = __builtin_amdgcn_raw_buffer_load_b8(r2, boff[u], kt, 0);
+      c1v[S][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ((bglob[u] + kt) >> 8) * 4, 0, 0));
+    }
+  }
+  // chunk P (8 codes) of every unit of the step held in slot S; the level
+  // table lives in static LDS, so a code's byte address (code * 4) is its
+  // whole ds_read address
+  template <int S, int P>
+  __device__ __forceinline__ void store_part(lds_t* t) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) store_unit<S, P>(t, u);
+  }
+  template <int S, int P>
+  __device__ __forceinline__ void store_unit(lds_t* t, int u) {
+    if (P == 0) chat[u] = dequant_constant(c2v[S][u], c1v[S][u], mean);
+    const int idx = threadIdx.x + u * T;
+    const int row = idx >> 1, h = idx & 1;
+    const uint32_t word = q[S][u][P];
+    const uint32_t lo4 = (word << 2) & 0x3C3C3C3Cu;   // 4 * low nibble of each byte
+    const uint32_t hi4 = (word >> 2) & 0x3C3C3C3Cu;   // 4 * high nibble of each byte
+    u32x4 o;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t al = byte_of(lo4, b), ah = byte_of(hi4, b);
+      const float lo = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + al), chat[u]);
+      const float hi = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + ah), chat[u]);
+      o[b] = pack_bf16x2(lo, hi);
+    }
+    st_lds16(t + frag_slot<R>(row, 4 * h + P), o);
+  }
+  __device__ __forceinline__ void prologue(int kt0, int last, lds_t* t) {
+    load<0>(kt0);
+    store_part<0, 0>(t);
+    store_part<0, 1>(t);
+    store_part<0, 2>(t);
+    store_part<0, 3>(t);
+    load<1>(min(kt0 + 1, last));
+  }
+  template <int S>
+  __device__ __forceinline__ void ahead(int kt, int last) {
+    load<S>(min(kt + 2, last));
+  }
+};
+
 // NF4 weight read transposed: tile row i = weight column k0 + i, reduction =
 // weight row n.  A thread takes patches of 4 rows (n) x 8 columns (k); the 8
 // columns lie in one block of each row, so a patch needs 4 constants.
@@ -383,19 +576,88 @@ __device__ __forceinline__ void run_phase(LA& la, LB& lb, int kt0, int kt1, lds_
   la.store(sa);
   lb.store(sb);
   __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
+  // the last step is peeled so that the loop body has no branches
+  int kt = kt0;
+  for (; kt + 1 < kt1; ++kt) {
     const int cur = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) {
-      la.load(kt + 1);
-      lb.load(kt + 1);
-    }
+    la.load(kt + 1);
+    lb.load(kt + 1);
     mma_tile<BM, BN, WN>(sa + cur * SA, sb + cur * SB, acc);
-    if (more) {
-      la.store(sa + (cur ^ 1) * SA);
-      lb.store(sb + (cur ^ 1) * SB);
-    }
+    la.store(sa + (cur ^ 1) * SA);
+    lb.store(sb + (cur ^ 1) * SB);
     __syncthreads();
+  }
+  const int cur = (kt - kt0) & 1;
+  mma_tile<BM, BN, WN>(sa + cur * SA, sb + cur * SB, acc);
+}
+
+// One 64-deep step on LDS buffers (sa, sb), with the expansion of the next
+// step (register slot S -> LDS buffers da, db) spread over its four 16-deep
+// sub-steps, so that the dequantization VALU work issues between MFMAs.
+template <int BM, int BN, int WN, int S, class LA, class LB>
+__device__ __forceinline__ void mma_step_store(const lds_t* sa, const lds_t* sb, Acc<BM, BN, WN>& acc, LA& la,
+                                               LB& lb, lds_t* da, lds_t* db) {
+  constexpr int TM = Acc<BM, BN, WN>::TM, TN = Acc<BM, BN, WN>::TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  // fragments of sub-step P+1 are read while sub-step P multiplies
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto read = [&](int buf, int ps) {   // fragment-major tiles: one contiguous 1 KB per fragment
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[buf][i] = __builtin_bit_cast(
+          bf16x8, ld16(sa + ((ps * (BM / 32) + (wm * (BM / 2) + i * 32) / 32) * 64 + frag_read_slot(lane, ps)) * 8));
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[buf][j] = __builtin_bit_cast(
+          bf16x8, ld16(sb + ((ps * (BN / 32) + (wn * (BN / WN) + j * 32) / 32) * 64 + frag_read_slot(lane, ps)) * 8));
+  };
+  auto sub = [&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (p < 3) read((p + 1) & 1, p + 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p & 1][i], fb[p & 1][j], acc.c[i][j], 0, 0, 0);
+    la.template store_part<S, p>(da);
+    lb.template store_part<S, p>(db);
+  };
+  read(0, 0);
+  sub(std::integral_constant<int, 0>{});
+  sub(std::integral_constant<int, 1>{});
+  sub(std::integral_constant<int, 2>{});
+  sub(std::integral_constant<int, 3>{});
+}
+
+// The X/W product over steps [kt0, kt1) on fragment-major tiles (SA, SB bf16
+// elements per buffer): LDS double buffer, and global loads
+// two steps ahead in two register slots, so the loads of step kt+2 travel
+// while step kt is multiplied and step kt+1 is expanded.  Loads past the end
+// repeat the last step (harmless) and the final expansion lands in the
+// buffer nobody reads, which keeps the loop free of branches.
+template <int BM, int BN, int WN, class LA, class LB>
+__device__ __forceinline__ void run_pipelined(LA& la, LB& lb, int kt0, int kt1, lds_t* sa, lds_t* sb,
+                                              Acc<BM, BN, WN>& acc) {
+  if (kt0 >= kt1) return;
+  constexpr int SA = BM * BK, SB = BN * BK;
+  const int last = kt1 - 1;
+  la.prologue(kt0, last, sa);
+  lb.prologue(kt0, last, sb);
+  __syncthreads();
+  for (int kt = kt0;; kt += 2) {
+    // step kt in buffer 0; register slot 1 holds step kt+1; slot 0 is free
+    la.template ahead<0>(kt, last);
+    lb.template ahead<0>(kt, last);
+    mma_step_store<BM, BN, WN, 1>(sa, sb, acc, la, lb, sa + SA, sb + SB);
+    __syncthreads();
+    if (kt + 1 > last) break;
+    // step kt+1 in buffer 1; slot 0 holds step kt+2; slot 1 is free
+    la.template ahead<1>(kt + 1, last);
+    lb.template ahead<1>(kt + 1, last);
+    mma_step_store<BM, BN, WN, 0>(sa + SA, sb + SB, acc, la, lb, sa, sb);
+    __syncthreads();
+    if (kt + 2 > last) break;
   }
 }
 
@@ -507,6 +769,11 @@ __device__ __forceinline__ void tile_of(int L, int mtiles, int ntiles, int gm, i
   ni = in_group / gm_eff;
 }
 
+// dynamic LDS of the pipelined products (fragment-major tiles, two buffers)
+__host__ __device__ constexpr size_t frag_lds_bytes(int bm, int bn) {
+  return (size_t)2 * (bm + bn) * BK * sizeof(lds_t);
+}
+
 __host__ __device__ constexpr size_t gemm_lds_bytes(int bm, int bn) {
   return (size_t)2 * (bm + bn) * PITCH * sizeof(lds_t) + 16 * sizeof(float);
 }
@@ -537,9 +804,9 @@ template <int BM, int BN, int WN>
 __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
   constexpr int T = 128 * WN;
   extern __shared__ __attribute__((aligned(16))) lds_t smem[];
+  __shared__ float lut[16];
   lds_t* sa = smem;
-  lds_t* sb = smem + 2 * BM * PITCH;
-  float* lut = reinterpret_cast<float*>(sb + 2 * BN * PITCH);
+  lds_t* sb = smem + 2 * BM * BK;   // fragment-major tiles, double-buffered
   load_lut(lut, p.tab);
   const int tiles = p.mtiles * p.ntiles;
   const int split = (int)blockIdx.x / tiles;
@@ -552,9 +819,11 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
   zero(acc);
   __syncthreads();
   {
-    RowsBf16<BM, T> la{p.X, p.K, (int)min<int64_t>(BM, p.M - m0), (int)p.K, m0, true};
-    Nf4Rows<BN, T> lb{p.codes, p.c2, p.c1, *p.mean, p.K, (int)min<int64_t>(BN, p.N - n0), n0, lut};
-    run_phase<BM, BN, WN>(la, lb, kt0, kt1, sa, sb, acc);
+    XRows<BM, T, true, (WN == 4 ? 2 : 1)> la;
+    la.init(p.X, p.K, p.M, m0);
+    WRows<BN, T> lb;
+    lb.init(p.codes, p.c2, p.c1, *p.mean, p.N, p.K, n0, lut);
+    run_pipelined<BM, BN, WN>(la, lb, kt0, kt1, sa, sb, acc);
   }
   if (split == 0)
     lora_tail<BM, BN, WN>(
@@ -661,7 +930,7 @@ __global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
   zero(acc);
   __syncthreads();
   {
-    RowsBf16<BM, T> la{p.dY, p.N, (int)min<int64_t>(BM, p.M - m0), (int)p.N, m0, (p.N % 8) == 0};
+    RowsBf16<BM, T> la{p.dY, p.N, (int)lmin(BM, p.M - m0), (int)p.N, m0, (p.N % 8) == 0};
     Nf4Cols<BN, T> lb{p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut};
     run_phase<BM, BN, WN>(la, lb, nt0, nt1, sa, sb, acc);
   }
@@ -689,21 +958,21 @@ template <int R>
 struct SRowsBf16 : RowsBf16<R, NT> {
   __device__ __forceinline__ void row_origin(int64_t o, int64_t total) {
     this->row0 = o;
-    this->rows = (int)min<int64_t>(R, total - o);
+    this->rows = (int)lmin(R, total - o);
   }
 };
 template <int R>
 struct SColsBf16 : ColsBf16<R, NT> {
   __device__ __forceinline__ void row_origin(int64_t o, int64_t total) {
     this->col0 = o;
-    this->cols = (int)min<int64_t>(R, total - o);
+    this->cols = (int)lmin(R, total - o);
   }
 };
 template <int R>
 struct SColsF32 : ColsF32<R, NT> {
   __device__ __forceinline__ void row_origin(int64_t o, int64_t total) {
     this->col0 = o;
-    this->cols = (int)min<int64_t>(R, total - o);
+    this->cols = (int)lmin(R, total - o);
   }
 };
 
@@ -824,10 +1093,10 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
   p.tab = nf4_table();
   hipError_t e;
   if (g.tile == 256)
-    e = launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits,
+    e = launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, frag_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits,
                      p, s);
   else
-    e = launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits,
+    e = launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, frag_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits,
                      p, s);
   if (e != hipSuccess || g.splits == 1) return e;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.N, 256), 4096)),
