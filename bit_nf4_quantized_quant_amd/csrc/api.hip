@@ -55,7 +55,7 @@ int check_weight(const uint8_t* codes, const uint8_t* c2, const float* c1, const
 
 // Forward workspace: the decode kernel keeps its launch counters in the first
 // kFwdReserved bytes whatever M is, so one workspace can serve both paths.
-constexpr size_t kFwdReserved = 2048;
+constexpr size_t kFwdReserved = 4096;
 
 bool use_decode(int64_t M, int64_t N, int64_t K) {
   // the decode kernel addresses the codes with 32-bit byte offsets

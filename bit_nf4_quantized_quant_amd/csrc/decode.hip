@@ -53,10 +53,11 @@ constexpr uint64_t kEpoch = uint64_t(1) << 20;
 constexpr unsigned kSpinLimit = 1u << 20;  // ~50 ms per polled word, a safety net only
 constexpr int kXLdsBytes = 16384;  // X staged in LDS when M*K*2 fits
 
-// Workspace layout (bytes): [0] LoRA-down counter (u64), [128*(1+s)] weight
-// counter s (u64), [128*9] timeout flag (u32), [kHpartOff..] tagged partial
-// sums (u64: tag << 32 | fp32 bits).
-constexpr size_t kHpartOff = 2048;
+// Workspace layout (bytes): [128*(1+s)] weight counter s (u64, s < 8),
+// [128*9] timeout flag (u32), [128*(10+s)] LoRA-down counter s (u64, s < 8),
+// [kHpartOff..] tagged partial sums (u64: tag << 32 | fp32 bits).  Counters
+// sit 128 bytes apart so that their atomics do not queue on one cache line.
+constexpr size_t kHpartOff = 4096;
 
 struct DecodeParams {
   const uint16_t* X;
@@ -81,6 +82,7 @@ struct DecodeParams {
   int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
   int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
   uint32_t hi[16]; // bf16(level) per code
+  uint32_t pair[256];  // code byte e -> bf16(level[e & 15]) | bf16(level[e >> 4]) << 16
 };
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -110,6 +112,41 @@ __device__ __forceinline__ uint64_t add_ctr(uint64_t* p, uint64_t v) {
 // i-th of n equal integer shares of 2^20 (the shares add up to exactly 2^20)
 __device__ __forceinline__ uint64_t epoch_share(uint32_t i, uint32_t n) {
   return kEpoch / n + ((i < kEpoch % n) ? 1u : 0u);
+}
+
+// Tile i of n takes its share of one launch epoch from a group of kSlots
+// counters (byte offset base + 128 s): the tiles of counter s together add
+// exactly 2^20.  With fewer tiles than counters a tile advances every counter
+// it owns.  Returns the tile's own counter update.
+__device__ __forceinline__ uint64_t take_slot_ticket(char* ws, int base, uint32_t i, uint32_t n) {
+  uint64_t ticket;
+  if (n >= (uint32_t)kSlots) {
+    const uint32_t s = i % kSlots;
+    const uint32_t cnt = n / kSlots + ((s < n % kSlots) ? 1u : 0u);
+    ticket = add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * s), epoch_share(i / kSlots, cnt));
+  } else {
+    ticket = add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * i), kEpoch);
+    for (uint32_t s = i + n; s < (uint32_t)kSlots; s += n)
+      add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * s), kEpoch);
+  }
+  return ticket;
+}
+
+constexpr int kWeightCtr = 128;        // weight counters at 128 (1 + s)
+constexpr int kDownCtr = 128 * 10;     // LoRA-down counters at 128 (10 + s)
+
+// Weight tile wt's ticket (one thread per tile).  Without an adapter there
+// are no LoRA-down tiles: tile 0 advances their counters too, so that every
+// launch moves every counter by one epoch.
+__device__ __forceinline__ uint64_t take_weight_ticket(const DecodeParams& p, int wt) {
+  const uint64_t ticket = take_slot_ticket(p.ws, kWeightCtr, (uint32_t)wt, (uint32_t)p.n_wtiles);
+  if (p.n_htiles == 0 && wt == 0)
+    for (int s = 0; s < kSlots; ++s) add_ctr(reinterpret_cast<uint64_t*>(p.ws + kDownCtr + 128 * s), kEpoch);
+  return ticket;
+}
+
+__device__ __forceinline__ uint64_t take_down_ticket(const DecodeParams& p, int tile) {
+  return take_slot_ticket(p.ws, kDownCtr, (uint32_t)tile, (uint32_t)p.n_htiles);
 }
 
 // ---------------------------------------------------------------- LoRA-down tile
@@ -451,8 +488,7 @@ __global__ void __launch_bounds__(kThreads, 4) qlora_decode_kernel(DecodeParams 
   if (tile < p.n_htiles) {
     __shared__ uint32_t htag;
     uint64_t hticket = 0;
-    if (threadIdx.x == 0)
-      hticket = add_ctr(reinterpret_cast<uint64_t*>(p.ws), epoch_share((uint32_t)tile, (uint32_t)p.n_htiles));
+    if (threadIdx.x == 0) hticket = take_down_ticket(p, tile);
     lora_down_tile(p, tile, red, &htag, hticket);
     return;
   }
@@ -460,25 +496,256 @@ __global__ void __launch_bounds__(kThreads, 4) qlora_decode_kernel(DecodeParams 
   // weight tile: take the epoch ticket now, use it at the wait
   const int wt = tile - p.n_htiles;
   uint64_t ticket = 0;
-  if (threadIdx.x == 0) {
-    const uint32_t nw = (uint32_t)p.n_wtiles;
-    if (nw >= (uint32_t)kSlots) {
-      const uint32_t s = (uint32_t)wt % kSlots;
-      const uint32_t cnt = nw / kSlots + ((s < nw % kSlots) ? 1u : 0u);
-      ticket = add_ctr(reinterpret_cast<uint64_t*>(p.ws + 128 * (1 + s)), epoch_share((uint32_t)wt / kSlots, cnt));
-    } else {
-      // fewer tiles than counters: this tile advances every counter it owns
-      ticket = add_ctr(reinterpret_cast<uint64_t*>(p.ws + 128 * (1 + wt)), kEpoch);
-      for (uint32_t s = (uint32_t)wt + nw; s < (uint32_t)kSlots; s += nw)
-        add_ctr(reinterpret_cast<uint64_t*>(p.ws + 128 * (1 + s)), kEpoch);
-    }
-    // without an adapter there are no LoRA-down tiles: advance their counter
-    // here so that every launch moves every counter by one epoch
-    if (p.n_htiles == 0 && wt == 0) add_ctr(reinterpret_cast<uint64_t*>(p.ws), kEpoch);
-  }
+  if (threadIdx.x == 0) ticket = take_weight_ticket(p, wt);
 
   __shared__ uint32_t wtag;
   weight_tile<kXLds>(p, wt, lut, xs, words, red, hs, bs, &wtag, ticket);
+}
+
+// ---------------------------------------------------------------- GEMV path (M <= 2)
+// 16 output rows per workgroup, two per wave.  A wave streams each of its
+// rows in 1 KB pieces: lane l takes 16 bytes (32 codes, inside one NF4 block),
+// so every load instruction reads 1 KB of contiguous codes.  The lane forms
+// bf16 pair products with the matching 32 X values (v_dot2_f32_bf16; a code
+// byte indexes the pair table of bf16 levels), scales its sum by the block's
+// fp32 constant, adds its share of the LoRA term and the wave sums its lanes.
+// The level enters as bf16(level) and the block constant in fp32 after the
+// sum, as in the matrix-core path above.  X sits in LDS, loaded once per
+// workgroup.  The LoRA-down products come from one workgroup per row of A,
+// each publishing H[m][j] as one tagged word.
+constexpr int kGemvRows = 2;                 // output rows per wave
+constexpr int kGemvXBytes = 24576;           // X in LDS (M * K * 2 bytes at most)
+
+// bf16 pairs as the dot-product builtin takes them (raw 16-bit lanes)
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+struct GemvLoads {
+  u32x4 w[kGemvRows];     // 16 bytes of codes per row
+  uint32_t c2[kGemvRows];
+  float c1[kGemvRows];
+};
+
+__device__ __forceinline__ void gemv_load(const DecodeParams& p, const rsrc_t& rc, const rsrc_t& r2, const rsrc_t& r1,
+                                          const uint32_t (&row)[kGemvRows], int i, GemvLoads& L) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t nblk = (uint32_t)p.K / 64, rb = (uint32_t)p.K / 2;
+  const uint32_t c = (uint32_t)(lane + 64 * i);    // piece index within the row
+#pragma unroll
+  for (int rr = 0; rr < kGemvRows; ++rr) {
+    const uint32_t blk = row[rr] * nblk + (c >> 1);
+    L.w[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, row[rr] * rb + 16 * c, 0, 0));
+    L.c2[rr] = __builtin_amdgcn_raw_buffer_load_b8(r2, blk, 0, 0);
+    L.c1[rr] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (blk >> 8) * 4, 0, 0));
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void gemv_mul(const DecodeParams& p, const GemvLoads& L, int i, int nch, float mu,
+                                         const char* lutb, uint32_t cb, const char* xs, float (&acc)[kGemvRows][M]) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane + 64 * i;
+  if (c >= nch) return;   // past the row end
+  u32x4 xv[M][4];         // the piece's 32 X values per batch row
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[m][q] = *reinterpret_cast<const u32x4*>(xs + ((size_t)m * p.K + 32 * c) * 2 + 16 * q);
+#pragma unroll
+  for (int rr = 0; rr < kGemvRows; ++rr) {
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t word = L.w[rr][q];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t byte = (word >> (8 * b)) & 0xFFu;
+        const uint32_t wp = *reinterpret_cast<const uint32_t*>(lutb + ((byte << 7) | cb));
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          // copy the vector element out first: a bit_cast applied to the
+          // element expression itself reads element 0
+          const uint32_t xp = xv[m][q][b];
+          part[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, wp), __builtin_bit_cast(s16x2, xp),
+                                                    part[m], false);
+        }
+      }
+    }
+    const float chat = dequant_constant(L.c2[rr], L.c1[rr], mu);
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[rr][m] = __builtin_fmaf(chat, part[m], acc[rr][m]);
+  }
+}
+
+// X [M, K] for LDS, in 16-byte chunks (K % 64 == 0 keeps them whole)
+constexpr int kGemvXPer = kGemvXBytes / 16 / kThreads;
+
+// LoRA-down row j = tile: H[m][j] = sum_k X[m][k] A[j][k] for m < M, published
+// as tagged words Hpart[m * r16 + j].
+template <int M>
+__device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_t* tag_lds, uint64_t ticket) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const rsrc_t ra = make_rsrc(p.A + (size_t)j * p.K, (uint32_t)p.K * 2);
+  const rsrc_t rx = make_rsrc(p.X, (uint32_t)M * p.K * 2);
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  for (int c = threadIdx.x; c < p.K / 8; c += kThreads) {   // 8 elements per chunk
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 16 * c, 0, 0));
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ((uint32_t)m * p.K + 8 * c) * 2, 0, 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t aq = a[q], xq = x[q];
+        acc[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, aq), __builtin_bit_cast(s16x2, xq), acc[m],
+                                                 false);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float v = acc[m];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) red[wave * M + m] = v;
+  }
+  if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
+  __syncthreads();
+  if (threadIdx.x < M) {
+    float h = 0.f;
+    for (int w = 0; w < kWaves; ++w) h += red[w * M + threadIdx.x];
+    const int r16 = (p.r + 15) & ~15;
+    st_tagged(&p.Hpart[(size_t)threadIdx.x * r16 + j], *tag_lds, h);
+  }
+}
+
+template <int M>
+__device__ void gemv_tile(const DecodeParams& p, int tile, uint32_t* lut, char* xs, uint32_t* tag_lds, uint64_t ticket) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t row[kGemvRows];
+#pragma unroll
+  for (int rr = 0; rr < kGemvRows; ++rr) row[rr] = (uint32_t)(tile * kRows + kGemvRows * wave + rr);
+  const uint32_t n_c2 = (uint32_t)p.N * (uint32_t)(p.K / 64);
+  const rsrc_t rc = make_rsrc(p.codes, n_c2 * 32u);   // rows >= N read as zero codes
+  const rsrc_t r2 = make_rsrc(p.c2, n_c2);
+  const rsrc_t r1 = make_rsrc(p.c1, ((n_c2 + 255u) / 256u) * 4u);
+  const int nch = p.K / 32;                            // 16-byte pieces per row
+  const int npl = (nch + 63) / 64;                     // pieces per lane
+
+  // loads complete in issue order: X and the pair-table entry first, so that
+  // X and the table reach LDS while the codes stream in
+  const int n16 = M * p.K / 8;
+  u32x4 xv[kGemvXPer];
+#pragma unroll
+  for (int i = 0; i < kGemvXPer; ++i) {
+    const int j = threadIdx.x + i * kThreads;
+    if (j < n16) xv[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * j);
+  }
+  const uint32_t pv = threadIdx.x < 256 ? p.pair[threadIdx.x] : 0u;
+  GemvLoads La, Lb;
+  gemv_load(p, rc, r2, r1, row, 0, La);
+  if (1 < npl) gemv_load(p, rc, r2, r1, row, 1, Lb);
+  // B entries of this lane (j = lane, lane + 64) for the LoRA epilogue
+  const rsrc_t rbb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
+  uint32_t bv[kGemvRows][2];
+#pragma unroll
+  for (int rr = 0; rr < kGemvRows; ++rr)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      bv[rr][h] = (lane + 64 * h < p.r) ? __builtin_amdgcn_raw_buffer_load_b16(rbb, (row[rr] * p.r + lane + 64 * h) * 2, 0, 0) : 0u;
+  if (threadIdx.x < 256) {   // 32 copies of entry e = tid (one per lane % 32)
+    u32x4* dst = reinterpret_cast<u32x4*>(lut + threadIdx.x * kLutCopies);
+#pragma unroll
+    for (int i = 0; i < kLutCopies / 4; ++i) dst[i] = u32x4{pv, pv, pv, pv};
+  }
+#pragma unroll
+  for (int i = 0; i < kGemvXPer; ++i) {
+    const int j = threadIdx.x + i * kThreads;
+    if (j < n16) reinterpret_cast<u32x4*>(xs)[j] = xv[i];
+  }
+  __syncthreads();
+
+  const float mu = *p.mean;
+  const uint32_t cb = (uint32_t)(lane & 31) * 4u;
+  const char* lutb = reinterpret_cast<const char*>(lut);
+  float acc[kGemvRows][M];
+#pragma unroll
+  for (int rr = 0; rr < kGemvRows; ++rr)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[rr][m] = 0.f;
+  for (int i = 0; i < npl; i += 2) {
+    if (i != 0 && i + 1 < npl) gemv_load(p, rc, r2, r1, row, i + 1, Lb);
+    gemv_mul<M>(p, La, i, nch, mu, lutb, cb, xs, acc);
+    if (i + 2 < npl) gemv_load(p, rc, r2, r1, row, i + 2, La);
+    if (i + 1 < npl) gemv_mul<M>(p, Lb, i + 1, nch, mu, lutb, cb, xs, acc);
+  }
+
+  // LoRA: s H B^T, this lane's share j = lane, lane + 64, from this launch's
+  // published H (tag = epoch + 1), polling until present.  Thread 0 holds
+  // the epoch; the barrier also ends the use of the table and of X.
+  if (p.r > 0) {
+    if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
+    __syncthreads();
+    const uint32_t tag = *tag_lds;
+    const int r16 = (p.r + 15) & ~15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = lane + 64 * h;
+      if (j >= p.r) continue;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint64_t* src = &p.Hpart[(size_t)m * r16 + j];
+        uint64_t v = ld_tagged(src);
+        unsigned spins = 0;
+        while ((uint32_t)(v >> 32) != tag) {   // not yet published: poll
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            __hip_atomic_store(reinterpret_cast<unsigned*>(p.ws + 128 * 9), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          v = ld_tagged(src);
+        }
+        const float hv = __uint_as_float((uint32_t)v);
+        if (tile == 0 && wave == 0 && p.H) p.H[m * p.r + j] = hv;
+        const float sh = p.scale * hv;
+#pragma unroll
+        for (int rr = 0; rr < kGemvRows; ++rr)
+          acc[rr][m] = __builtin_fmaf(sh, __uint_as_float(bv[rr][h] << 16), acc[rr][m]);
+      }
+    }
+  }
+  // sum over the wave's lanes
+#pragma unroll
+  for (int rr = 0; rr < kGemvRows; ++rr)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = acc[rr][m];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0 && row[rr] < (uint32_t)p.N) p.Y[(size_t)m * p.N + row[rr]] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+    }
+}
+
+template <int M>
+__global__ void __launch_bounds__(kThreads, 2) qlora_gemv_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutCopies];   // 32 KiB
+  __shared__ __attribute__((aligned(16))) char xs[kGemvXBytes];
+  __shared__ float red[kWaves * M];
+  __shared__ uint32_t tag;
+  const int tile = (int)blockIdx.x;
+  if (tile < p.n_htiles) {
+    uint64_t hticket = 0;
+    if (threadIdx.x == 0) hticket = take_down_ticket(p, tile);
+    gemv_down_tile<M>(p, tile, red, &tag, hticket);
+    return;
+  }
+  const int wt = tile - p.n_htiles;
+  uint64_t ticket = 0;
+  if (threadIdx.x == 0) ticket = take_weight_ticket(p, wt);
+  gemv_tile<M>(p, wt, lut, xs, &tag, ticket);
 }
 
 }  // namespace
@@ -507,7 +774,8 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   p.Hpart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff);
   p.H = a.H;
   const int64_t r16 = (a.r + 15) & ~15;
-  p.n_htiles = (int)(r16 / kRows) * kHSplit;
+  const bool gemv = a.M <= 2 && (size_t)a.M * a.K * 2 <= (size_t)kGemvXBytes;
+  p.n_htiles = gemv ? (int)a.r : (int)(r16 / kRows) * kHSplit;
   p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
   int G = kThreads / (16 * (int)a.M);
   G = G >= 32 ? 32 : (G >= 16 ? 16 : (G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1))));
@@ -516,8 +784,13 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
   const Nf4HiLo& hl = nf4_hilo();
   for (int i = 0; i < 16; ++i) p.hi[i] = hl.word[i] & 0xFFFFu;
+  for (int e = 0; e < 256; ++e) p.pair[e] = p.hi[e & 15] | (p.hi[e >> 4] << 16);
   const dim3 grid(p.n_htiles + p.n_wtiles);
-  if ((size_t)a.M * a.K * 2 <= (size_t)kXLdsBytes)
+  if (gemv && a.M == 1)
+    hipLaunchKernelGGL(qlora_gemv_kernel<1>, grid, dim3(kThreads), 0, s, p);
+  else if (gemv)
+    hipLaunchKernelGGL(qlora_gemv_kernel<2>, grid, dim3(kThreads), 0, s, p);
+  else if ((size_t)a.M * a.K * 2 <= (size_t)kXLdsBytes)
     hipLaunchKernelGGL(qlora_decode_kernel<true>, grid, dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL(qlora_decode_kernel<false>, grid, dim3(kThreads), 0, s, p);
