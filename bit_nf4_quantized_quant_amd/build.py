@@ -22,11 +22,14 @@ SOURCES = ["api.hip", "quant.hip", "decode.hip", "gemm.hip", "nf4_table.cpp"]
 
 # -ffp-contract=off: the dequantization arithmetic is specified as separate
 # fp32 roundings; fused multiply-adds are written explicitly where wanted.
-# Packed fp32 instructions are disabled on the device.
+# Packed fp32 instructions are disabled on the device.  The atomic optimizer
+# is off: every device atomic here is issued by one lane, and the optimizer's
+# wave-wide rewrite waits for each reply as soon as it is issued.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

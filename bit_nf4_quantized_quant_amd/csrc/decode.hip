@@ -82,7 +82,6 @@ struct DecodeParams {
   int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
   int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
   uint32_t hi[16]; // bf16(level) per code
-  uint32_t pair[256];  // code byte e -> bf16(level[e & 15]) | bf16(level[e >> 4]) << 16
 };
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -118,17 +117,18 @@ __device__ __forceinline__ uint64_t epoch_share(uint32_t i, uint32_t n) {
 // counters (byte offset base + 128 s): the tiles of counter s together add
 // exactly 2^20.  With fewer tiles than counters a tile advances every counter
 // it owns.  Returns the tile's own counter update.
+// (One returning atomic on a computed address, no branch around it, so that
+// nothing waits for its result before the result is used.)
 __device__ __forceinline__ uint64_t take_slot_ticket(char* ws, int base, uint32_t i, uint32_t n) {
-  uint64_t ticket;
-  if (n >= (uint32_t)kSlots) {
-    const uint32_t s = i % kSlots;
-    const uint32_t cnt = n / kSlots + ((s < n % kSlots) ? 1u : 0u);
-    ticket = add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * s), epoch_share(i / kSlots, cnt));
-  } else {
-    ticket = add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * i), kEpoch);
-    for (uint32_t s = i + n; s < (uint32_t)kSlots; s += n)
-      add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * s), kEpoch);
-  }
+  const bool shared = n >= (uint32_t)kSlots;
+  const uint32_t s = shared ? i % kSlots : i;
+  const uint32_t cnt = n / kSlots + ((s < n % kSlots) ? 1u : 0u);
+  const uint64_t share = shared ? epoch_share(i / kSlots, cnt) : kEpoch;
+  const uint64_t ticket = add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * s), share);
+  if (!shared)
+    for (uint32_t t = i + n; t < (uint32_t)kSlots; t += n)
+      __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(ws + base + 128 * t), kEpoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   return ticket;
 }
 
@@ -503,55 +503,65 @@ __global__ void __launch_bounds__(kThreads, 4) qlora_decode_kernel(DecodeParams 
 }
 
 // ---------------------------------------------------------------- GEMV path (M <= 2)
-// 16 output rows per workgroup, two per wave.  A wave streams each of its
-// rows in 1 KB pieces: lane l takes 16 bytes (32 codes, inside one NF4 block),
-// so every load instruction reads 1 KB of contiguous codes.  The lane forms
-// bf16 pair products with the matching 32 X values (v_dot2_f32_bf16; a code
-// byte indexes the pair table of bf16 levels), scales its sum by the block's
-// fp32 constant, adds its share of the LoRA term and the wave sums its lanes.
-// The level enters as bf16(level) and the block constant in fp32 after the
-// sum, as in the matrix-core path above.  X sits in LDS, loaded once per
-// workgroup.  The LoRA-down products come from one workgroup per row of A,
-// each publishing H[m][j] as one tagged word.
-constexpr int kGemvRows = 2;                 // output rows per wave
-constexpr int kGemvXBytes = 24576;           // X in LDS (M * K * 2 bytes at most)
+// 16 output rows per workgroup.  Wave w takes rows 4 (w % 4) .. +3 of the
+// tile over one half of K (w / 4).  Per row, lane l reads 16 bytes of codes
+// (32 codes inside one NF4 block), so a load instruction covers 1 KB of one
+// row.  Each wave loads the X values of its own pieces into registers, so no
+// wave waits for another before its dot products: they run while the rest
+// of the weight stream is still arriving.  A code byte indexes a table of
+// bf16 level pairs in LDS (entry e at 256 e, one 4-byte copy per lane % 32:
+// the address 256 byte + 4 (lane % 32) is one byte permute, and the lanes of
+// a half-wave always hit distinct banks); v_dot2_f32_bf16 multiplies the
+// pair with two X values in fp32.  The level enters as bf16(level) and the
+// block's fp32 constant scales the block's sum afterwards, as in the
+// matrix-core path above.  The two halves of K meet in LDS at the end.  The
+// LoRA-down products come from one workgroup per row of A, each publishing
+// H[m][j] as one tagged word.
+constexpr int kGvRowsPerWave = 4;
+constexpr int kGvStride = 256;   // bytes per pair-table entry
 
 // bf16 pairs as the dot-product builtin takes them (raw 16-bit lanes)
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-struct GemvLoads {
-  u32x4 w[kGemvRows];     // 16 bytes of codes per row
-  uint32_t c2[kGemvRows];
-  float c1[kGemvRows];
+template <int M>
+struct GvPiece {
+  u32x4 x[M][4];               // the piece's 32 X values per batch row
+  u32x4 w[kGvRowsPerWave];     // 16 bytes of codes per row
+  uint8_t c2[kGvRowsPerWave];    // (bytes: widened where used, not ahead of a loop)
+  float c1[kGvRowsPerWave];
 };
 
-__device__ __forceinline__ void gemv_load(const DecodeParams& p, const rsrc_t& rc, const rsrc_t& r2, const rsrc_t& r1,
-                                          const uint32_t (&row)[kGemvRows], int i, GemvLoads& L) {
-  const int lane = threadIdx.x & 63;
+// piece c of each of the wave's rows (c < K / 32), X first: it is used first
+template <int M>
+__device__ __forceinline__ void gv_load(const DecodeParams& p, const rsrc_t& rc, const rsrc_t& r2, const rsrc_t& r1,
+                                        const rsrc_t& rx, const uint32_t (&row)[kGvRowsPerWave], uint32_t c,
+                                        GvPiece<M>& L) {
   const uint32_t nblk = (uint32_t)p.K / 64, rb = (uint32_t)p.K / 2;
-  const uint32_t c = (uint32_t)(lane + 64 * i);    // piece index within the row
 #pragma unroll
-  for (int rr = 0; rr < kGemvRows; ++rr) {
-    const uint32_t blk = row[rr] * nblk + (c >> 1);
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      L.x[m][q] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ((uint32_t)m * p.K + 32 * c) * 2 + 16 * q, 0, 0));
+  // (constants through plain byte loads, which widen for free, on a row
+  // clamped to N - 1; the buffer form's byte result costs a separate
+  // widening instruction, which the compiler places early)
+  const uint32_t last = (uint32_t)p.N - 1u, n_c2 = (uint32_t)p.N * nblk;
+#pragma unroll
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr) {
+    const uint32_t rowc = row[rr] < last ? row[rr] : last;
+    const uint32_t blk = rowc * nblk + (c >> 1);
     L.w[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, row[rr] * rb + 16 * c, 0, 0));
-    L.c2[rr] = __builtin_amdgcn_raw_buffer_load_b8(r2, blk, 0, 0);
+    L.c2[rr] = p.c2[blk < n_c2 ? blk : n_c2 - 1u];
     L.c1[rr] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (blk >> 8) * 4, 0, 0));
   }
 }
 
 template <int M>
-__device__ __forceinline__ void gemv_mul(const DecodeParams& p, const GemvLoads& L, int i, int nch, float mu,
-                                         const char* lutb, uint32_t cb, const char* xs, float (&acc)[kGemvRows][M]) {
-  const int lane = threadIdx.x & 63;
-  const int c = lane + 64 * i;
-  if (c >= nch) return;   // past the row end
-  u32x4 xv[M][4];         // the piece's 32 X values per batch row
+__device__ __forceinline__ void gv_mul(const GvPiece<M>& L, float mu, const char* lut, uint32_t lane4,
+                                       float (&acc)[kGvRowsPerWave][M]) {
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xv[m][q] = *reinterpret_cast<const u32x4*>(xs + ((size_t)m * p.K + 32 * c) * 2 + 16 * q);
-#pragma unroll
-  for (int rr = 0; rr < kGemvRows; ++rr) {
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr) {
     float part[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) part[m] = 0.f;
@@ -560,13 +570,14 @@ __device__ __forceinline__ void gemv_mul(const DecodeParams& p, const GemvLoads&
       const uint32_t word = L.w[rr][q];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (word >> (8 * b)) & 0xFFu;
-        const uint32_t wp = *reinterpret_cast<const uint32_t*>(lutb + ((byte << 7) | cb));
+        // address bytes: [lane4, code byte b, 0, 0]
+        const uint32_t a = __builtin_amdgcn_perm(word, lane4, 0x0c0c0000u | ((4u + b) << 8));
+        const uint32_t wp = *reinterpret_cast<const uint32_t*>(lut + a);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           // copy the vector element out first: a bit_cast applied to the
           // element expression itself reads element 0
-          const uint32_t xp = xv[m][q][b];
+          const uint32_t xp = L.x[m][q][b];
           part[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, wp), __builtin_bit_cast(s16x2, xp),
                                                     part[m], false);
         }
@@ -578,8 +589,53 @@ __device__ __forceinline__ void gemv_mul(const DecodeParams& p, const GemvLoads&
   }
 }
 
-// X [M, K] for LDS, in 16-byte chunks (K % 64 == 0 keeps them whole)
-constexpr int kGemvXPer = kGemvXBytes / 16 / kThreads;
+// Pair-table entry e = bf16(level[e & 15]) | bf16(level[e >> 4]) << 16 for a
+// lane-varying e < 256: the 16 level words (scalar launch arguments) go into
+// lanes 0..15 of one register and each half is fetched by a lane permute, so
+// no memory is read.
+__device__ __forceinline__ uint32_t pair_entry(const DecodeParams& p, uint32_t e) {
+  int tab = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(tab) : "s"(p.hi[k]), "n"(k));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((e & 15u) * 4u), tab);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((e >> 4) * 4u), tab);
+  return lo | (hi << 16);
+}
+
+// Lane exchanges without LDS: DPP within a row of 16 lanes, and gfx950's
+// permlane swaps between rows (16) and halves (32) of the wave.
+__device__ __forceinline__ float dpp_row_sum(float v) {   // every lane: its row's sum
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));   // row_mirror
+  return v;
+}
+// a + b after swapping a's upper 32 lanes with b's lower 32
+__device__ __forceinline__ float swap32_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// a + b after swapping a's odd 16-lane rows with b's even rows
+__device__ __forceinline__ float swap16_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_sum(float v) {   // every lane: the wave's sum
+  v = dpp_row_sum(v);
+  v = swap16_add(v, v);
+  return swap32_add(v, v);
+}
+
+// Sums of v[0..3] over the wave's 64 lanes: afterwards the lanes of row t
+// (lanes 16 t .. 16 t + 15) hold the sum of v[t].  The swaps halve the values
+// a lane carries, so 4 sums cost 2 + 1 swaps and one row reduction.
+__device__ __forceinline__ float wave_sum4(const float (&v)[kGvRowsPerWave]) {
+  // lower half: v0 (+ upper's v0), upper half: v2 (+ lower's v2); same for 1, 3
+  const float a0 = swap32_add(v[0], v[2]), a1 = swap32_add(v[1], v[3]);
+  // even rows keep a0, odd rows a1
+  return dpp_row_sum(swap16_add(a0, a1));
+}
 
 // LoRA-down row j = tile: H[m][j] = sum_k X[m][k] A[j][k] for m < M, published
 // as tagged words Hpart[m * r16 + j].
@@ -606,9 +662,7 @@ __device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    float v = acc[m];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    const float v = wave_sum(acc[m]);
     if (lane == 0) red[wave * M + m] = v;
   }
   if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
@@ -622,74 +676,115 @@ __device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_
 }
 
 template <int M>
-__device__ void gemv_tile(const DecodeParams& p, int tile, uint32_t* lut, char* xs, uint32_t* tag_lds, uint64_t ticket) {
+__device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red, uint32_t* tag_lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t row[kGemvRows];
+  const int grp = wave & 3, half = wave >> 2;
+  // (read ahead of the counter update: with no write before it, the
+  // compiler may take it through the scalar cache)
+  const float mu = *p.mean;
+  // this launch's epoch: thread 0's counter update goes out first, and its
+  // reply, which comes back ahead of every later load, is used only at the
+  // end (no other thread reads the variable)
+  uint64_t ticket;
+  if (threadIdx.x == 0) ticket = take_weight_ticket(p, tile);
+
+  // pair table: entry e = bf16(level[e & 15]) | bf16(level[e >> 4]) << 16,
+  // 32 copies; thread t writes 4 of the 8 16-byte pieces of entry t % 256,
+  // in a per-entry rotated order (no bank conflicts between the 8 entries a
+  // write instruction serves at once).  It is built before any weight load
+  // is issued: the only barrier then precedes all of them, and no wait for
+  // a load can be placed in front of it.
+  {
+    const uint32_t e = threadIdx.x & 255, part = threadIdx.x >> 8;
+    const uint32_t pv = pair_entry(p, e);
+    u32x4* dst = reinterpret_cast<u32x4*>(lut + e * kGvStride);
 #pragma unroll
-  for (int rr = 0; rr < kGemvRows; ++rr) row[rr] = (uint32_t)(tile * kRows + kGemvRows * wave + rr);
+    for (uint32_t i = 0; i < 4; ++i) dst[(4 * part + i + e) & 7] = u32x4{pv, pv, pv, pv};
+  }
+  __syncthreads();
+
+  uint32_t row[kGvRowsPerWave];
+#pragma unroll
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr)
+    row[rr] = (uint32_t)(tile * kRows + kGvRowsPerWave * grp + rr);
   const uint32_t n_c2 = (uint32_t)p.N * (uint32_t)(p.K / 64);
   const rsrc_t rc = make_rsrc(p.codes, n_c2 * 32u);   // rows >= N read as zero codes
   const rsrc_t r2 = make_rsrc(p.c2, n_c2);
   const rsrc_t r1 = make_rsrc(p.c1, ((n_c2 + 255u) / 256u) * 4u);
-  const int nch = p.K / 32;                            // 16-byte pieces per row
-  const int npl = (nch + 63) / 64;                     // pieces per lane
+  const rsrc_t rx = make_rsrc(p.X, (uint32_t)M * p.K * 2);
+  const int hp = p.K / 64;                 // pieces per row in each half of K
+  const int npl = (hp + 63) / 64;          // pieces per lane
+  const uint32_t c0 = (uint32_t)(half * hp + lane);
+  // two pieces in flight at M = 1; at M = 2 one (registers)
+  constexpr bool kTwo = M == 1;
+  GvPiece<M> La, Lb;
+  gv_load<M>(p, rc, r2, r1, rx, row, c0, La);
+  if (kTwo && 1 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64, Lb);
 
-  // loads complete in issue order: X and the pair-table entry first, so that
-  // X and the table reach LDS while the codes stream in
-  const int n16 = M * p.K / 8;
-  u32x4 xv[kGemvXPer];
+  const uint32_t lane4 = (uint32_t)(lane & 31) * 4u;
+  float acc[kGvRowsPerWave][M];
 #pragma unroll
-  for (int i = 0; i < kGemvXPer; ++i) {
-    const int j = threadIdx.x + i * kThreads;
-    if (j < n16) xv[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * j);
-  }
-  const uint32_t pv = threadIdx.x < 256 ? p.pair[threadIdx.x] : 0u;
-  GemvLoads La, Lb;
-  gemv_load(p, rc, r2, r1, row, 0, La);
-  if (1 < npl) gemv_load(p, rc, r2, r1, row, 1, Lb);
-  // B entries of this lane (j = lane, lane + 64) for the LoRA epilogue
-  const rsrc_t rbb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
-  uint32_t bv[kGemvRows][2];
-#pragma unroll
-  for (int rr = 0; rr < kGemvRows; ++rr)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      bv[rr][h] = (lane + 64 * h < p.r) ? __builtin_amdgcn_raw_buffer_load_b16(rbb, (row[rr] * p.r + lane + 64 * h) * 2, 0, 0) : 0u;
-  if (threadIdx.x < 256) {   // 32 copies of entry e = tid (one per lane % 32)
-    u32x4* dst = reinterpret_cast<u32x4*>(lut + threadIdx.x * kLutCopies);
-#pragma unroll
-    for (int i = 0; i < kLutCopies / 4; ++i) dst[i] = u32x4{pv, pv, pv, pv};
-  }
-#pragma unroll
-  for (int i = 0; i < kGemvXPer; ++i) {
-    const int j = threadIdx.x + i * kThreads;
-    if (j < n16) reinterpret_cast<u32x4*>(xs)[j] = xv[i];
-  }
-  __syncthreads();
-
-  const float mu = *p.mean;
-  const uint32_t cb = (uint32_t)(lane & 31) * 4u;
-  const char* lutb = reinterpret_cast<const char*>(lut);
-  float acc[kGemvRows][M];
-#pragma unroll
-  for (int rr = 0; rr < kGemvRows; ++rr)
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[rr][m] = 0.f;
-  for (int i = 0; i < npl; i += 2) {
-    if (i != 0 && i + 1 < npl) gemv_load(p, rc, r2, r1, row, i + 1, Lb);
-    gemv_mul<M>(p, La, i, nch, mu, lutb, cb, xs, acc);
-    if (i + 2 < npl) gemv_load(p, rc, r2, r1, row, i + 2, La);
-    if (i + 1 < npl) gemv_mul<M>(p, Lb, i + 1, nch, mu, lutb, cb, xs, acc);
+  if constexpr (kTwo) {
+    for (int i = 0; i < npl; i += 2) {
+      if (i != 0 && i + 1 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 1), Lb);
+      if (lane + 64 * i < hp) gv_mul<M>(La, mu, lut, lane4, acc);
+      if (i + 2 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 2), La);
+      if (i + 1 < npl && lane + 64 * (i + 1) < hp) gv_mul<M>(Lb, mu, lut, lane4, acc);
+    }
+  } else {
+    for (int i = 0; i < npl; ++i) {
+      if (i != 0) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * i, La);
+      if (lane + 64 * i < hp) gv_mul<M>(La, mu, lut, lane4, acc);
+    }
   }
 
-  // LoRA: s H B^T, this lane's share j = lane, lane + 64, from this launch's
-  // published H (tag = epoch + 1), polling until present.  Thread 0 holds
-  // the epoch; the barrier also ends the use of the table and of X.
-  if (p.r > 0) {
-    if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
-    __syncthreads();
+  // Epilogue.  Waves of the first half of K reduce their sums and leave them
+  // in LDS, and thread 0 publishes the launch tag there; waves of the second
+  // half add s H B^T (H from this launch's tagged partials, tag = epoch + 1,
+  // polled until present), their own sums and the first half's, and store.
+  // The second half reads B and H before the barrier: the replies come back
+  // while it waits.
+  const bool lora = p.r > 0;
+  uint32_t bv[kGvRowsPerWave][2];
+  uint64_t hv[M][2];
+  const int r16 = (p.r + 15) & ~15;
+  if (half == 1 && lora) {
+    const rsrc_t rbb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = lane + 64 * h;
+      if (j >= p.r) continue;
+#pragma unroll
+      for (int rr = 0; rr < kGvRowsPerWave; ++rr)
+        bv[rr][h] = __builtin_amdgcn_raw_buffer_load_b16(rbb, (row[rr] * p.r + j) * 2, 0, 0);
+#pragma unroll
+      for (int m = 0; m < M; ++m) hv[m][h] = ld_tagged(&p.Hpart[(size_t)m * r16 + j]);
+    }
+  }
+  const int rt = lane >> 4;   // this lane's row in the wave's group, if lane % 16 == 0
+  if (half == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v[kGvRowsPerWave];
+#pragma unroll
+      for (int rr = 0; rr < kGvRowsPerWave; ++rr) v[rr] = acc[rr][m];
+      const float t = wave_sum4(v);
+      if ((lane & 15) == 0) red[(grp * kGvRowsPerWave + rt) * M + m] = t;
+    }
+    if (threadIdx.x == 0) {
+      // (the empty asm keeps the use of the reply here, at the end)
+      asm volatile("" : "+v"(ticket));
+      *tag_lds = (uint32_t)(ticket >> 20) + 1u;
+    }
+  }
+  __syncthreads();
+  if (half == 0) return;
+
+  if (lora) {
     const uint32_t tag = *tag_lds;
-    const int r16 = (p.r + 15) & ~15;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int j = lane + 64 * h;
@@ -697,7 +792,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, uint32_t* lut, char* 
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const uint64_t* src = &p.Hpart[(size_t)m * r16 + j];
-        uint64_t v = ld_tagged(src);
+        uint64_t v = hv[m][h];
         unsigned spins = 0;
         while ((uint32_t)(v >> 32) != tag) {   // not yet published: poll
           __builtin_amdgcn_s_sleep(1);
@@ -708,44 +803,48 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, uint32_t* lut, char* 
           }
           v = ld_tagged(src);
         }
-        const float hv = __uint_as_float((uint32_t)v);
-        if (tile == 0 && wave == 0 && p.H) p.H[m * p.r + j] = hv;
-        const float sh = p.scale * hv;
+        const float hval = __uint_as_float((uint32_t)v);
+        if (tile == 0 && grp == 0 && p.H) p.H[m * p.r + j] = hval;
+        const float sh = p.scale * hval;
 #pragma unroll
-        for (int rr = 0; rr < kGemvRows; ++rr)
+        for (int rr = 0; rr < kGvRowsPerWave; ++rr)
           acc[rr][m] = __builtin_fmaf(sh, __uint_as_float(bv[rr][h] << 16), acc[rr][m]);
       }
     }
   }
-  // sum over the wave's lanes
 #pragma unroll
-  for (int rr = 0; rr < kGemvRows; ++rr)
+  for (int m = 0; m < M; ++m) {
+    float v[kGvRowsPerWave];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float v = acc[rr][m];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0 && row[rr] < (uint32_t)p.N) p.Y[(size_t)m * p.N + row[rr]] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+    for (int rr = 0; rr < kGvRowsPerWave; ++rr) v[rr] = acc[rr][m];
+    const float t = wave_sum4(v);
+    if ((lane & 15) == 0 && row[0] + rt < (uint32_t)p.N) {
+      const float y = t + red[(grp * kGvRowsPerWave + rt) * M + m];
+      p.Y[(size_t)m * p.N + row[0] + rt] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
     }
+  }
 }
 
 template <int M>
 __global__ void __launch_bounds__(kThreads, 2) qlora_gemv_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutCopies];   // 32 KiB
-  __shared__ __attribute__((aligned(16))) char xs[kGemvXBytes];
-  __shared__ float red[kWaves * M];
+  __shared__ __attribute__((aligned(16))) char lut[256 * kGvStride];   // 64 KiB
+  __shared__ float red[kRows * M];
   __shared__ uint32_t tag;
   const int tile = (int)blockIdx.x;
+  // fetch the launch arguments both paths use in one round trip, ahead of
+  // the branches (left alone, each branch would wait for its own fetch)
+  asm volatile("" ::"s"(p.X), "s"(p.codes), "s"(p.c2), "s"(p.c1), "s"(p.mean), "s"(p.B), "s"(p.A), "s"(p.K),
+               "s"(p.N), "s"(p.r), "s"(p.n_htiles), "s"(p.n_wtiles), "s"(p.ws));
+  asm volatile("" ::"s"(p.hi[0]), "s"(p.hi[1]), "s"(p.hi[2]), "s"(p.hi[3]), "s"(p.hi[4]), "s"(p.hi[5]),
+               "s"(p.hi[6]), "s"(p.hi[7]), "s"(p.hi[8]), "s"(p.hi[9]), "s"(p.hi[10]), "s"(p.hi[11]),
+               "s"(p.hi[12]), "s"(p.hi[13]), "s"(p.hi[14]), "s"(p.hi[15]));
   if (tile < p.n_htiles) {
     uint64_t hticket = 0;
     if (threadIdx.x == 0) hticket = take_down_ticket(p, tile);
     gemv_down_tile<M>(p, tile, red, &tag, hticket);
     return;
   }
-  const int wt = tile - p.n_htiles;
-  uint64_t ticket = 0;
-  if (threadIdx.x == 0) ticket = take_weight_ticket(p, wt);
-  gemv_tile<M>(p, wt, lut, xs, &tag, ticket);
+  gemv_tile<M>(p, tile - p.n_htiles, lut, red, &tag);
 }
 
 }  // namespace
@@ -774,7 +873,7 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   p.Hpart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff);
   p.H = a.H;
   const int64_t r16 = (a.r + 15) & ~15;
-  const bool gemv = a.M <= 2 && (size_t)a.M * a.K * 2 <= (size_t)kGemvXBytes;
+  const bool gemv = a.M <= 2;
   p.n_htiles = gemv ? (int)a.r : (int)(r16 / kRows) * kHSplit;
   p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
   int G = kThreads / (16 * (int)a.M);
@@ -784,7 +883,6 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
   const Nf4HiLo& hl = nf4_hilo();
   for (int i = 0; i < 16; ++i) p.hi[i] = hl.word[i] & 0xFFFFu;
-  for (int e = 0; e < 256; ++e) p.pair[e] = p.hi[e & 15] | (p.hi[e >> 4] << 16);
   const dim3 grid(p.n_htiles + p.n_wtiles);
   if (gemv && a.M == 1)
     hipLaunchKernelGGL(qlora_gemv_kernel<1>, grid, dim3(kThreads), 0, s, p);
