@@ -688,21 +688,6 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   uint64_t ticket;
   if (threadIdx.x == 0) ticket = take_weight_ticket(p, tile);
 
-  // pair table: entry e = bf16(level[e & 15]) | bf16(level[e >> 4]) << 16,
-  // 32 copies; thread t writes 4 of the 8 16-byte pieces of entry t % 256,
-  // in a per-entry rotated order (no bank conflicts between the 8 entries a
-  // write instruction serves at once).  It is built before any weight load
-  // is issued: the only barrier then precedes all of them, and no wait for
-  // a load can be placed in front of it.
-  {
-    const uint32_t e = threadIdx.x & 255, part = threadIdx.x >> 8;
-    const uint32_t pv = pair_entry(p, e);
-    u32x4* dst = reinterpret_cast<u32x4*>(lut + e * kGvStride);
-#pragma unroll
-    for (uint32_t i = 0; i < 4; ++i) dst[(4 * part + i + e) & 7] = u32x4{pv, pv, pv, pv};
-  }
-  __syncthreads();
-
   uint32_t row[kGvRowsPerWave];
 #pragma unroll
   for (int rr = 0; rr < kGvRowsPerWave; ++rr)
@@ -720,6 +705,19 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   GvPiece<M> La, Lb;
   gv_load<M>(p, rc, r2, r1, rx, row, c0, La);
   if (kTwo && 1 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64, Lb);
+
+  // pair table: entry e = bf16(level[e & 15]) | bf16(level[e >> 4]) << 16,
+  // 32 copies; thread t writes 4 of the 8 16-byte pieces of entry t % 256,
+  // in a per-entry rotated order (no bank conflicts between the 8 entries a
+  // write instruction serves at once), while the loads are in flight.
+  {
+    const uint32_t e = threadIdx.x & 255, part = threadIdx.x >> 8;
+    const uint32_t pv = pair_entry(p, e);
+    u32x4* dst = reinterpret_cast<u32x4*>(lut + e * kGvStride);
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) dst[(4 * part + i + e) & 7] = u32x4{pv, pv, pv, pv};
+  }
+  __syncthreads();
 
   const uint32_t lane4 = (uint32_t)(lane & 31) * 4u;
   float acc[kGvRowsPerWave][M];
