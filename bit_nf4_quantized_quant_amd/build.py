@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libqlora.so")
 
-SOURCES = ["api.hip", "quant.hip", "decode.hip", "gemm.hip", "nf4_table.cpp"]
+SOURCES = ["api.hip", "quant.hip", "decode.hip", "gemv.hip", "gemm.hip", "nf4_table.cpp"]
 
 # -ffp-contract=off: the dequantization arithmetic is specified as separate
 # fp32 roundings; fused multiply-adds are written explicitly where wanted.

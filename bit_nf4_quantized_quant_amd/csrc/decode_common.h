@@ -1,0 +1,282 @@
+// Shared pieces of the fused decode-size QLoRA forward kernels (gfx950): the
+// launch parameters, the cross-workgroup hand-off of the LoRA-down products,
+// the pair table of bf16 NF4 levels and lane reductions.
+//
+// Y = bf16( X W_deq^T + s (X A^T) B^T )   (itwiki "QLoRA", section on the
+// computation; minnong511 "quantization", y = W x + (alpha/r) B A x).
+//
+// One launch does everything.  Its first workgroups are "LoRA-down" tiles,
+// which compute H = X A^T in parts and publish them; they never wait.  The
+// remaining workgroups are weight tiles, which stream the NF4 codes, wait
+// (bounded spin) for this launch's H, add s H B^T in fp32 and store bf16 Y.
+// Workgroups are dispatched in index order, so the LoRA-down tiles are
+// running or done before any weight tile waits.
+//
+// Launch epochs: every launch adds exactly 2^20 to each of the counters of a
+// group, however many workgroups share a counter, so a workgroup's own
+// counter update returns (epoch << 20) + something < 2^20, which names the
+// launch (the same epoch on every counter, whatever mix of shapes, with or
+// without adapter, used the workspace before).  LoRA-down tiles store each
+// partial as one 64-bit word (epoch tag, value), so a partial is valid
+// exactly when its tag is this launch's; nothing has to be reset or waited
+// for on the producer side.  A weight tile's counter update goes out first
+// and its result is used only at the end, so its latency hides behind the
+// weight stream.
+//
+// Workspace layout (bytes): [128*(1+s)] weight counter s (u64, s < 8),
+// [128*9] timeout flag (u32), [128*(10+s)] LoRA-down counter s (u64, s < 8),
+// [kHpartOff..] tagged partial sums (u64: tag << 32 | fp32 bits).  Counters
+// sit 128 bytes apart so that their atomics do not queue on one cache line.
+#pragma once
+
+#include "common.h"
+#include "launch.h"
+
+namespace qlora {
+namespace dec {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = 16;          // output rows per weight tile
+constexpr int kHSplit = 4;         // K slices per LoRA-down row group
+constexpr int kSlots = 8;          // weight-tile epoch counters
+constexpr uint64_t kEpoch = uint64_t(1) << 20;
+constexpr unsigned kSpinLimit = 1u << 20;  // ~50 ms per polled word, a safety net only
+constexpr size_t kHpartOff = 4096;
+constexpr int kTimeoutFlag = 128 * 9;
+
+struct DecodeParams {
+  const uint16_t* X;
+  int M;
+  int N;
+  int K;
+  int r;
+  const uint8_t* codes;
+  const uint8_t* c2;
+  const float* c1;
+  const float* mean;
+  const uint16_t* A;
+  const uint16_t* B;
+  float scale;
+  uint16_t* Y;
+  float* H;        // H [M, r] for the caller, or null
+  uint64_t* Hpart; // [kHSplit][M][r16] tagged partial sums (r16 = r rounded up to 16)
+  char* ws;
+  int n_htiles;
+  int n_wtiles;
+  int epi_group;   // threads per output in the epilogue (power of two, <= 32)
+  int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
+  int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
+  uint32_t hi[16]; // bf16(level) per code
+};
+
+// Cross-workgroup data (H partials, counters) moves only through relaxed
+// agent-scope atomics, which are coherent across the XCDs' separate L2 caches
+// on their own; each partial carries its launch tag in the same 64-bit word,
+// so no ordering between separate stores is needed and no L2
+// write-back/invalidate fence is ever issued.
+__device__ __forceinline__ void st_tagged(uint64_t* p, uint32_t tag, float v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_ctr(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t add_ctr(uint64_t* p, uint64_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// i-th of n equal integer shares of 2^20 (the shares add up to exactly 2^20)
+__device__ __forceinline__ uint64_t epoch_share(uint32_t i, uint32_t n) {
+  return kEpoch / n + ((i < kEpoch % n) ? 1u : 0u);
+}
+
+// Tile i of n takes its share of one launch epoch from a group of kSlots
+// counters (byte offset base + 128 s): the tiles of counter s together add
+// exactly 2^20.  With fewer tiles than counters a tile advances every counter
+// it owns.  Returns the tile's own counter update.
+// (One returning atomic on a computed address, no branch around it, so that
+// nothing waits for its result before the result is used.)
+__device__ __forceinline__ uint64_t take_slot_ticket(char* ws, int base, uint32_t i, uint32_t n) {
+  const bool shared = n >= (uint32_t)kSlots;
+  const uint32_t s = shared ? i % kSlots : i;
+  const uint32_t cnt = n / kSlots + ((s < n % kSlots) ? 1u : 0u);
+  const uint64_t share = shared ? epoch_share(i / kSlots, cnt) : kEpoch;
+  const uint64_t ticket = add_ctr(reinterpret_cast<uint64_t*>(ws + base + 128 * s), share);
+  if (!shared)
+    for (uint32_t t = i + n; t < (uint32_t)kSlots; t += n)
+      __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(ws + base + 128 * t), kEpoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  return ticket;
+}
+
+constexpr int kWeightCtr = 128;        // weight counters at 128 (1 + s)
+constexpr int kDownCtr = 128 * 10;     // LoRA-down counters at 128 (10 + s)
+
+// Weight tile wt's ticket (one thread per tile).  Without an adapter there
+// are no LoRA-down tiles: tile 0 advances their counters too, so that every
+// launch moves every counter by one epoch.
+__device__ __forceinline__ uint64_t take_weight_ticket(const DecodeParams& p, int wt) {
+  const uint64_t ticket = take_slot_ticket(p.ws, kWeightCtr, (uint32_t)wt, (uint32_t)p.n_wtiles);
+  if (p.n_htiles == 0 && wt == 0)
+    for (int s = 0; s < kSlots; ++s) add_ctr(reinterpret_cast<uint64_t*>(p.ws + kDownCtr + 128 * s), kEpoch);
+  return ticket;
+}
+
+__device__ __forceinline__ uint64_t take_down_ticket(const DecodeParams& p, int tile) {
+  return take_slot_ticket(p.ws, kDownCtr, (uint32_t)tile, (uint32_t)p.n_htiles);
+}
+
+// Polls a tagged partial until it carries `tag` (first: the word already
+// read); returns its value.  The spin is bounded: past the limit the timeout
+// flag is raised and whatever was read last is used.
+__device__ __forceinline__ float poll_tagged(const uint64_t* src, uint64_t first, uint32_t tag, char* ws) {
+  uint64_t v = first;
+  unsigned spins = 0;
+  while ((uint32_t)(v >> 32) != tag) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(reinterpret_cast<unsigned*>(ws + kTimeoutFlag), 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    v = ld_tagged(src);
+  }
+  return __uint_as_float((uint32_t)v);
+}
+
+// The weight's mean (read-only during a launch) through the scalar cache: a
+// read in the constant address space is a scalar load, counted apart from
+// the vector loads, so no wait for it lands behind the weight stream.
+__device__ __forceinline__ float load_mean(const DecodeParams& p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) float*>(
+      reinterpret_cast<uintptr_t>(p.mean));
+}
+
+// bf16 pairs as the dot-product builtin takes them (raw 16-bit lanes)
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Pair table in LDS: entry e (code byte e) = bf16(level[e & 15]) |
+// bf16(level[e >> 4]) << 16 at byte 256 e, 32 copies (one per lane % 32), so
+// that the address 256 byte + 4 (lane % 32) is one byte permute and the
+// lanes of a half-wave always hit distinct banks.
+constexpr int kPairStride = 256;
+
+// Pair-table entry e = bf16(level[e & 15]) | bf16(level[e >> 4]) << 16 for a
+// lane-varying e < 256: the 16 level words (scalar launch arguments) go into
+// lanes 0..15 of one register and each half is fetched by a lane permute, so
+// no memory is read.
+__device__ __forceinline__ uint32_t pair_entry(const DecodeParams& p, uint32_t e) {
+  int tab = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(tab) : "s"(p.hi[k]), "n"(k));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((e & 15u) * 4u), tab);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((e >> 4) * 4u), tab);
+  return lo | (hi << 16);
+}
+
+// Address of code byte b (0..3) of `word` in the pair table, for the lane
+// whose copy offset is lane4 = 4 (lane % 32): bytes [lane4, byte b, 0, 0].
+template <int b>
+__device__ __forceinline__ uint32_t pair_addr(uint32_t word, uint32_t lane4) {
+  return __builtin_amdgcn_perm(word, lane4, 0x0c0c0000u | ((4u + b) << 8));
+}
+
+// Builds the table: thread t of `nthreads` (a multiple of 256) writes its
+// share of entry t % 256's eight 16-byte pieces, in a per-entry rotated order
+// (no bank conflicts between the 8 entries a write instruction serves).
+template <int nthreads>
+__device__ __forceinline__ void build_pair_table(const DecodeParams& p, char* lut) {
+  constexpr uint32_t per = 8 / (nthreads / 256);
+  const uint32_t e = threadIdx.x & 255, part = threadIdx.x >> 8;
+  const uint32_t pv = pair_entry(p, e);
+  u32x4* dst = reinterpret_cast<u32x4*>(lut + e * kPairStride);
+#pragma unroll
+  for (uint32_t i = 0; i < per; ++i) dst[(per * part + i + e) & 7] = u32x4{pv, pv, pv, pv};
+}
+
+// Lane exchanges without LDS: DPP within a row of 16 lanes, and gfx950's
+// permlane swaps between rows (16) and halves (32) of the wave.
+__device__ __forceinline__ float dpp_row_sum(float v) {   // every lane: its row's sum
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));   // row_mirror
+  return v;
+}
+// a + b after swapping a's upper 32 lanes with b's lower 32
+__device__ __forceinline__ float swap32_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// a + b after swapping a's odd 16-lane rows with b's even rows
+__device__ __forceinline__ float swap16_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_sum(float v) {   // every lane: the wave's sum
+  v = dpp_row_sum(v);
+  v = swap16_add(v, v);
+  return swap32_add(v, v);
+}
+
+// Sum over aligned groups of G lanes (G a power of two, 1..32): every lane
+// of a group ends with its group's sum.
+__device__ __forceinline__ float group_sum(float v, int G) {
+  if (G >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if (G >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (G >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  if (G >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  if (G >= 32) v = swap16_add(v, v);
+  return v;
+}
+
+// The launch arguments both paths of a kernel use, fetched in one round trip
+// ahead of the first branch (left alone, each branch waits for its own).
+#define QLORA_FETCH_ARGS(p)                                                                              \
+  do {                                                                                                   \
+    asm volatile("" ::"s"((p).X), "s"((p).codes), "s"((p).c2), "s"((p).c1), "s"((p).mean), "s"((p).B),  \
+                 "s"((p).A), "s"((p).K), "s"((p).N), "s"((p).M), "s"((p).r), "s"((p).n_htiles),          \
+                 "s"((p).n_wtiles), "s"((p).ws));                                                        \
+    asm volatile("" ::"s"((p).hi[0]), "s"((p).hi[1]), "s"((p).hi[2]), "s"((p).hi[3]), "s"((p).hi[4]),    \
+                 "s"((p).hi[5]), "s"((p).hi[6]), "s"((p).hi[7]), "s"((p).hi[8]), "s"((p).hi[9]),        \
+                 "s"((p).hi[10]), "s"((p).hi[11]), "s"((p).hi[12]), "s"((p).hi[13]), "s"((p).hi[14]),   \
+                 "s"((p).hi[15]));                                                                       \
+  } while (0)
+
+// Host side: the parameters every decode path shares (tile counts and the
+// epilogue group are set by the path).
+inline DecodeParams decode_params(const FwdArgs& a) {
+  DecodeParams p;
+  p.X = a.X;
+  p.M = (int)a.M;
+  p.N = (int)a.N;
+  p.K = (int)a.K;
+  p.r = (int)a.r;
+  p.codes = a.w.codes;
+  p.c2 = a.w.c2;
+  p.c1 = a.w.c1;
+  p.mean = a.w.mean;
+  p.A = a.A;
+  p.B = a.B;
+  p.scale = a.scale;
+  p.Y = a.Y;
+  p.ws = reinterpret_cast<char*>(a.workspace);
+  p.Hpart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff);
+  p.H = a.H;
+  p.n_htiles = 0;
+  p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
+  p.epi_group = 1;
+  p.c2_vec = (a.K % 256 == 0) && (reinterpret_cast<uintptr_t>(a.w.c2) % 4 == 0);
+  p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
+  const Nf4HiLo& hl = nf4_hilo();
+  for (int i = 0; i < 16; ++i) p.hi[i] = hl.word[i] & 0xFFFFu;
+  return p;
+}
+
+hipError_t launch_gemv_fwd(const DecodeParams& p, hipStream_t s);
+
+}  // namespace dec
+}  // namespace qlora

@@ -1,0 +1,308 @@
+// Fused QLoRA forward for M <= 2 (decode), gfx950: the GEMV path.
+//
+// Y = bf16( X W_deq^T + s (X A^T) B^T )   (itwiki "QLoRA", section on the
+// computation; minnong511 "quantization", y = W x + (alpha/r) B A x).
+//
+// At M <= 2 the layer is bound by HBM bandwidth on the 4-bit weight.  The
+// pages describe the slow path as a separate dequantization kernel whose bf16
+// output makes a round trip through memory before the matrix product
+// (irregular6612 "QLoRA - Efficient Finetuning of Quantized LLMs", the
+// inference-speed discussion); here the packed codes are streamed once and
+// expanded in registers straight into bf16 dot products.
+//
+#include "decode_common.h"
+
+namespace qlora {
+namespace dec {
+namespace {
+
+// 16 output rows per workgroup.  Wave w takes rows 4 (w % 4) .. +3 of the
+// tile over one half of K (w / 4).  Per row, lane l reads 16 bytes of codes
+// (32 codes inside one NF4 block), so a load instruction covers 1 KB of one
+// row.  Each wave loads the X values of its own pieces into registers, so no
+// wave waits for another before its dot products: they run while the rest
+// of the weight stream is still arriving.  A code byte indexes a table of
+// bf16 level pairs in LDS (entry e at 256 e, one 4-byte copy per lane % 32:
+// the address 256 byte + 4 (lane % 32) is one byte permute, and the lanes of
+// a half-wave always hit distinct banks); v_dot2_f32_bf16 multiplies the
+// pair with two X values in fp32.  Each 64-element NF4 block is one scaling
+// unit: the level enters as bf16(level) and the block's fp32 constant c_hat
+// scales the block's partial sum in fp32 afterwards, i.e. the weight used is
+// bf16(level) * c_hat rather than bf16(level * c_hat): the same size of
+// rounding, one place earlier.  The two halves of K meet in LDS at the end.  The
+// LoRA-down products come from one workgroup per row of A, each publishing
+// H[m][j] as one tagged word.
+constexpr int kGvRowsPerWave = 4;
+
+template <int M>
+struct GvPiece {
+  u32x4 x[M][4];               // the piece's 32 X values per batch row
+  u32x4 w[kGvRowsPerWave];     // 16 bytes of codes per row
+  uint8_t c2[kGvRowsPerWave];  // (bytes: widened where used, not ahead of a loop)
+  float c1[kGvRowsPerWave];
+};
+
+// piece c of each of the wave's rows (c < K / 32), X first: it is used first
+template <int M>
+__device__ __forceinline__ void gv_load(const DecodeParams& p, const rsrc_t& rc, const rsrc_t& r2, const rsrc_t& r1,
+                                        const rsrc_t& rx, const uint32_t (&row)[kGvRowsPerWave], uint32_t c,
+                                        GvPiece<M>& L) {
+  const uint32_t nblk = (uint32_t)p.K / 64, rb = (uint32_t)p.K / 2;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      L.x[m][q] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ((uint32_t)m * p.K + 32 * c) * 2 + 16 * q, 0, 0));
+  // (constants through plain byte loads, which widen for free, on a row
+  // clamped to N - 1; the buffer form's byte result costs a separate
+  // widening instruction, which the compiler places early)
+  const uint32_t last = (uint32_t)p.N - 1u, n_c2 = (uint32_t)p.N * nblk;
+#pragma unroll
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr) {
+    const uint32_t rowc = row[rr] < last ? row[rr] : last;
+    const uint32_t blk = rowc * nblk + (c >> 1);
+    L.w[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, row[rr] * rb + 16 * c, 0, 0));
+    L.c2[rr] = p.c2[blk < n_c2 ? blk : n_c2 - 1u];
+    L.c1[rr] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (blk >> 8) * 4, 0, 0));
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void gv_mul(const GvPiece<M>& L, float mu, const char* lut, uint32_t lane4,
+                                       float (&acc)[kGvRowsPerWave][M]) {
+#pragma unroll
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr) {
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t word = L.w[rr][q];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t a = b == 0 ? pair_addr<0>(word, lane4)
+                         : b == 1 ? pair_addr<1>(word, lane4)
+                         : b == 2 ? pair_addr<2>(word, lane4)
+                                  : pair_addr<3>(word, lane4);
+        const uint32_t wp = *reinterpret_cast<const uint32_t*>(lut + a);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          // copy the vector element out first: a bit_cast applied to the
+          // element expression itself reads element 0
+          const uint32_t xp = L.x[m][q][b];
+          part[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, wp), __builtin_bit_cast(s16x2, xp),
+                                                    part[m], false);
+        }
+      }
+    }
+    const float chat = dequant_constant(L.c2[rr], L.c1[rr], mu);
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[rr][m] = __builtin_fmaf(chat, part[m], acc[rr][m]);
+  }
+}
+
+// Sums of v[0..3] over the wave's 64 lanes: afterwards the lanes of row t
+// (lanes 16 t .. 16 t + 15) hold the sum of v[t].  The swaps halve the values
+// a lane carries, so 4 sums cost 2 + 1 swaps and one row reduction.
+__device__ __forceinline__ float wave_sum4(const float (&v)[kGvRowsPerWave]) {
+  // lower half: v0 (+ upper's v0), upper half: v2 (+ lower's v2); same for 1, 3
+  const float a0 = swap32_add(v[0], v[2]), a1 = swap32_add(v[1], v[3]);
+  // even rows keep a0, odd rows a1
+  return dpp_row_sum(swap16_add(a0, a1));
+}
+
+// LoRA-down row j = tile: H[m][j] = sum_k X[m][k] A[j][k] for m < M, published
+// as tagged words Hpart[m * r16 + j].
+template <int M>
+__device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_t* tag_lds, uint64_t ticket) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const rsrc_t ra = make_rsrc(p.A + (size_t)j * p.K, (uint32_t)p.K * 2);
+  const rsrc_t rx = make_rsrc(p.X, (uint32_t)M * p.K * 2);
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  for (int c = threadIdx.x; c < p.K / 8; c += kThreads) {   // 8 elements per chunk
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 16 * c, 0, 0));
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ((uint32_t)m * p.K + 8 * c) * 2, 0, 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t aq = a[q], xq = x[q];
+        acc[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, aq), __builtin_bit_cast(s16x2, xq), acc[m],
+                                                 false);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const float v = wave_sum(acc[m]);
+    if (lane == 0) red[wave * M + m] = v;
+  }
+  if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
+  __syncthreads();
+  if (threadIdx.x < M) {
+    float h = 0.f;
+    for (int w = 0; w < kWaves; ++w) h += red[w * M + threadIdx.x];
+    const int r16 = (p.r + 15) & ~15;
+    st_tagged(&p.Hpart[(size_t)threadIdx.x * r16 + j], *tag_lds, h);
+  }
+}
+
+template <int M>
+__device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red, uint32_t* tag_lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave & 3, half = wave >> 2;
+  const float mu = load_mean(p);
+  // this launch's epoch: thread 0's counter update goes out first, and its
+  // reply, which comes back ahead of every later load, is used only at the
+  // end (no other thread reads the variable)
+  uint64_t ticket;
+  if (threadIdx.x == 0) ticket = take_weight_ticket(p, tile);
+
+  uint32_t row[kGvRowsPerWave];
+#pragma unroll
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr)
+    row[rr] = (uint32_t)(tile * kRows + kGvRowsPerWave * grp + rr);
+  const uint32_t n_c2 = (uint32_t)p.N * (uint32_t)(p.K / 64);
+  const rsrc_t rc = make_rsrc(p.codes, n_c2 * 32u);   // rows >= N read as zero codes
+  const rsrc_t r2 = make_rsrc(p.c2, n_c2);
+  const rsrc_t r1 = make_rsrc(p.c1, ((n_c2 + 255u) / 256u) * 4u);
+  const rsrc_t rx = make_rsrc(p.X, (uint32_t)M * p.K * 2);
+  const int hp = p.K / 64;                 // pieces per row in each half of K
+  const int npl = (hp + 63) / 64;          // pieces per lane
+  const uint32_t c0 = (uint32_t)(half * hp + lane);
+  // two pieces in flight at M = 1; at M = 2 one (registers)
+  constexpr bool kTwo = M == 1;
+  GvPiece<M> La, Lb;
+  gv_load<M>(p, rc, r2, r1, rx, row, c0, La);
+  if (kTwo && 1 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64, Lb);
+
+  // the pair table, while the loads are in flight
+  build_pair_table<kThreads>(p, lut);
+  __syncthreads();
+
+  const uint32_t lane4 = (uint32_t)(lane & 31) * 4u;
+  float acc[kGvRowsPerWave][M];
+#pragma unroll
+  for (int rr = 0; rr < kGvRowsPerWave; ++rr)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[rr][m] = 0.f;
+  if constexpr (kTwo) {
+    for (int i = 0; i < npl; i += 2) {
+      if (i != 0 && i + 1 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 1), Lb);
+      if (lane + 64 * i < hp) gv_mul<M>(La, mu, lut, lane4, acc);
+      if (i + 2 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 2), La);
+      if (i + 1 < npl && lane + 64 * (i + 1) < hp) gv_mul<M>(Lb, mu, lut, lane4, acc);
+    }
+  } else {
+    for (int i = 0; i < npl; ++i) {
+      if (i != 0) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * i, La);
+      if (lane + 64 * i < hp) gv_mul<M>(La, mu, lut, lane4, acc);
+    }
+  }
+
+  // Epilogue.  Waves of the first half of K reduce their sums and leave them
+  // in LDS, and thread 0 publishes the launch tag there; waves of the second
+  // half add s H B^T (H from this launch's tagged partials, tag = epoch + 1,
+  // polled until present), their own sums and the first half's, and store.
+  // The second half reads B and H before the barrier: the replies come back
+  // while it waits.
+  const bool lora = p.r > 0;
+  uint32_t bv[kGvRowsPerWave][2];
+  uint64_t hv[M][2];
+  const int r16 = (p.r + 15) & ~15;
+  if (half == 1 && lora) {
+    const rsrc_t rbb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = lane + 64 * h;
+      if (j >= p.r) continue;
+#pragma unroll
+      for (int rr = 0; rr < kGvRowsPerWave; ++rr)
+        bv[rr][h] = __builtin_amdgcn_raw_buffer_load_b16(rbb, (row[rr] * p.r + j) * 2, 0, 0);
+#pragma unroll
+      for (int m = 0; m < M; ++m) hv[m][h] = ld_tagged(&p.Hpart[(size_t)m * r16 + j]);
+    }
+  }
+  const int rt = lane >> 4;   // this lane's row in the wave's group, if lane % 16 == 0
+  if (half == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v[kGvRowsPerWave];
+#pragma unroll
+      for (int rr = 0; rr < kGvRowsPerWave; ++rr) v[rr] = acc[rr][m];
+      const float t = wave_sum4(v);
+      if ((lane & 15) == 0) red[(grp * kGvRowsPerWave + rt) * M + m] = t;
+    }
+    if (threadIdx.x == 0) {
+      // (the empty asm keeps the use of the reply here, at the end)
+      asm volatile("" : "+v"(ticket));
+      *tag_lds = (uint32_t)(ticket >> 20) + 1u;
+    }
+  }
+  __syncthreads();
+  if (half == 0) return;
+
+  if (lora) {
+    const uint32_t tag = *tag_lds;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = lane + 64 * h;
+      if (j >= p.r) continue;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float hval = poll_tagged(&p.Hpart[(size_t)m * r16 + j], hv[m][h], tag, p.ws);
+        if (tile == 0 && grp == 0 && p.H) p.H[m * p.r + j] = hval;
+        const float sh = p.scale * hval;
+#pragma unroll
+        for (int rr = 0; rr < kGvRowsPerWave; ++rr)
+          acc[rr][m] = __builtin_fmaf(sh, __uint_as_float(bv[rr][h] << 16), acc[rr][m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float v[kGvRowsPerWave];
+#pragma unroll
+    for (int rr = 0; rr < kGvRowsPerWave; ++rr) v[rr] = acc[rr][m];
+    const float t = wave_sum4(v);
+    if ((lane & 15) == 0 && row[0] + rt < (uint32_t)p.N) {
+      const float y = t + red[(grp * kGvRowsPerWave + rt) * M + m];
+      p.Y[(size_t)m * p.N + row[0] + rt] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
+    }
+  }
+}
+
+template <int M>
+__global__ void __launch_bounds__(kThreads, 2) qlora_gemv_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];   // 64 KiB
+  __shared__ float red[kRows * M];
+  __shared__ uint32_t tag;
+  const int tile = (int)blockIdx.x;
+  QLORA_FETCH_ARGS(p);
+  if (tile < p.n_htiles) {
+    uint64_t hticket = 0;
+    if (threadIdx.x == 0) hticket = take_down_ticket(p, tile);
+    gemv_down_tile<M>(p, tile, red, &tag, hticket);
+    return;
+  }
+  gemv_tile<M>(p, tile - p.n_htiles, lut, red, &tag);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_fwd(const DecodeParams& p0, hipStream_t s) {
+  DecodeParams p = p0;
+  p.n_htiles = p.r;   // one LoRA-down workgroup per row of A
+  const dim3 grid(p.n_htiles + p.n_wtiles);
+  if (p.M == 1)
+    hipLaunchKernelGGL(qlora_gemv_kernel<1>, grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(qlora_gemv_kernel<2>, grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace dec
+}  // namespace qlora
