@@ -44,8 +44,7 @@ __device__ __forceinline__ float* spare(char* lut, int f) {
 }
 constexpr int kRedOff = 0;              // [kWaves][256] wave partials
 constexpr int kHsOff = kWaves * 256;    // [16][128] H rows
-constexpr int kBsOff = kHsOff + 2048;   // [16][r + 1] B rows of the tile
-static_assert(kBsOff + 16 * 129 <= 256 * 32, "scratch floats exceed the spare table halves");
+static_assert(kHsOff + 16 * 128 <= 256 * 32, "scratch floats exceed the spare table halves");
 
 // ---------------------------------------------------------------- LoRA-down tile
 // Rows j0..j0+15 of A over a quarter of K; each wave takes a contiguous run of
@@ -258,50 +257,41 @@ __device__ void weight_tile(const DecodeParams& p, int tile, char* lut, uint32_t
       }
     }
   }
-  // rows n0..n0+15 of B (16 x r bf16, contiguous) and this thread's first
-  // LoRA-down partials: read together after the stream (one round trip)
-  const int bs_ld = p.r + 1;
-  const int rdiv = p.r > 0 ? p.r : 1;   // r = 0 (no adapter): every B/H loop is empty
-  const int b_chunks = p.b_vec ? (16 * p.r) / 8 : 0;
-  const rsrc_t rb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
-  u32x4 bchunk = {0u, 0u, 0u, 0u};
-  if (threadIdx.x < b_chunks)
-    bchunk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ((uint32_t)n0 * p.r + 8 * threadIdx.x) * 2, 0, 0));
-  constexpr int kBPer = 16 * 128 / kThreads;   // element loads when B is not 16-byte friendly
-  uint16_t bv[kBPer];
-  if (!p.b_vec) {
+  // Epilogue.  The LoRA term s H B^T goes through the matrix cores too: wave
+  // w < ceil(r / 32) takes j = 32 w .. 32 w + 31, with B[n0 + nl][j ..] read
+  // straight as the B operand and s H[m][j ..] as the A operand, split into
+  // bf16 high and low parts (two products: fp32 accuracy).  Its product
+  // joins the wave's partial sums, and the 8 waves' sums meet in LDS.
+  // B and this thread's LoRA-down partials are read right after the stream,
+  // so their replies come back during the barrier.
+  const int r16 = (p.r + 15) & ~15;
+  const bool lwave = wave * 32 < p.r;
+  const int jb = wave * 32 + 8 * g;                  // this lane's first j
+  u32x4 bop = {0u, 0u, 0u, 0u};
+  if (lwave && jb < p.r) {
+    const rsrc_t rb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
+    const uint32_t off = ((uint32_t)(n0 + nl) * p.r + jb) * 2;
+    if (p.b_vec) {   // r % 8 == 0: all 8 entries exist
+      bop = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    } else {
+      uint16_t e[8];
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int br = e / rdiv, bc = e - br * p.r;
-      bv[i] = (e < 16 * p.r && n0 + br < p.N) ? p.B[(size_t)(n0 + br) * p.r + bc] : (uint16_t)0;
+      for (int q = 0; q < 8; ++q)
+        e[q] = jb + q < p.r ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, off + 2 * q, 0, 0) : (uint16_t)0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bop[q] = (uint32_t)e[2 * q] | ((uint32_t)e[2 * q + 1] << 16);
     }
   }
   constexpr int kHPer = 16 * 128 / kThreads;   // up to M*r = 2048 sums per tile
-  const int r16 = (p.r + 15) & ~15;
-  uint64_t hp[kHSplit];
-  if ((int)threadIdx.x < p.M * p.r) {
-    const int m = threadIdx.x / p.r, j = threadIdx.x - m * p.r;
+  const int mr = p.M * p.r;
+  uint64_t hp[kHPer][kHSplit];
 #pragma unroll
-    for (int ks = 0; ks < kHSplit; ++ks) hp[ks] = ld_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j]);
-  }
-  // acc[v] = partial Y0[m = 4g + v][n0 + nl]
+  for (int u = 0; u < kHPer; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i < mr) {
+      const int m = i / p.r, j = i - m * p.r;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) *spare(lut, kRedOff + wave * 256 + (4 * g + v) * 16 + nl) = acc[v];
-  if (threadIdx.x < b_chunks) {
-    const int e0 = 8 * threadIdx.x, br = e0 / p.r, bc = e0 - br * p.r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *spare(lut, kBsOff + br * bs_ld + bc + 2 * q) = bf16_lo(bchunk[q]);
-      *spare(lut, kBsOff + br * bs_ld + bc + 2 * q + 1) = bf16_hi(bchunk[q]);
-    }
-  }
-  if (!p.b_vec) {
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int br = e / rdiv, bc = e - br * p.r;
-      if (e < 16 * p.r) *spare(lut, kBsOff + br * bs_ld + bc) = __uint_as_float((uint32_t)bv[i] << 16);
+      for (int ks = 0; ks < kHSplit; ++ks) hp[u][ks] = ld_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j]);
     }
   }
   if (threadIdx.x == 0) {
@@ -316,41 +306,48 @@ __device__ void weight_tile(const DecodeParams& p, int tile, char* lut, uint32_t
 #pragma unroll
   for (int u = 0; u < kHPer; ++u) {
     const int i = threadIdx.x + u * kThreads;
-    if (i < p.M * p.r) {
+    if (i < mr) {
       const int m = i / p.r, j = i - m * p.r;
       float h = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < kHSplit; ++ks) {
-        const uint64_t* src = &p.Hpart[((size_t)ks * p.M + m) * r16 + j];
-        h += poll_tagged(src, u == 0 ? hp[ks] : ld_tagged(src), tag, p.ws);
-      }
-      *spare(lut, kHsOff + i) = h;
+      for (int ks = 0; ks < kHSplit; ++ks)
+        h += poll_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j], hp[u][ks], tag, p.ws);
+      *spare(lut, kHsOff + m * 128 + j) = h;
       if (tile == 0 && p.H) p.H[i] = h;
     }
   }
   __syncthreads();
 
-  // epilogue: output o = m*16 + nn gets G threads (G = 512 / (16 M), capped at
-  // 32); each sums a share of the wave partials and of the r-long LoRA dot
-  // product, then the G lanes combine
-  {
-    const int G = p.epi_group;
-    const int o = threadIdx.x / G, sub = threadIdx.x - o * G;
-    const bool valid = o < 16 * p.M;
-    float part = 0.f;
-    if (valid) {
-      const int m = o >> 4, nn = o & 15;
-      for (int w = sub; w < kWaves; w += G) part += *spare(lut, kRedOff + w * 256 + o);
-      float lora = 0.f;
-      for (int j = sub; j < p.r; j += G)
-        lora = __builtin_fmaf(*spare(lut, kHsOff + m * p.r + j), *spare(lut, kBsOff + nn * bs_ld + j), lora);
-      part = __builtin_fmaf(p.scale, lora, part);
+  if (lwave) {
+    // A operand: s H[m = nl][jb .. jb + 7] as bf16 hi + lo (zeros past M or r)
+    u32x4 ahi = {0u, 0u, 0u, 0u}, alo = {0u, 0u, 0u, 0u};
+    if (nl < p.M) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = jb + 2 * q + e;
+          v[e] = j < p.r ? p.scale * *spare(lut, kHsOff + nl * 128 + j) : 0.f;
+        }
+        const uint32_t hi = pack_bf16x2(v[0], v[1]);
+        ahi[q] = hi;
+        alo[q] = pack_bf16x2(v[0] - bf16_lo(hi), v[1] - bf16_hi(hi));
+      }
     }
-    part = group_sum(part, G);
-    if (valid && sub == 0) {
-      const int m = o >> 4, n = n0 + (o & 15);
-      if (n < p.N) p.Y[(size_t)m * p.N + n] = (uint16_t)(pack_bf16x2(part, 0.f) & 0xFFFFu);
-    }
+    acc = mfma16(as_bf16x8(ahi), as_bf16x8(bop), acc);
+    acc = mfma16(as_bf16x8(alo), as_bf16x8(bop), acc);
+  }
+  // acc[v] = partial Y[m = 4g + v][n0 + nl]: the 8 waves' sums meet
+#pragma unroll
+  for (int v = 0; v < 4; ++v) *spare(lut, kRedOff + wave * 256 + (4 * g + v) * 16 + nl) = acc[v];
+  __syncthreads();
+  if ((int)threadIdx.x < 16 * p.M) {
+    const int o = threadIdx.x, m = o >> 4, n = n0 + (o & 15);
+    float y = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) y += *spare(lut, kRedOff + w * 256 + o);
+    if (n < p.N) p.Y[(size_t)m * p.N + n] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
   }
 }
 
@@ -398,9 +395,6 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   if (a.M <= 2) return launch_gemv_fwd(p, s);
   const int64_t r16 = (a.r + 15) & ~15;
   p.n_htiles = (int)(r16 / kRows) * kHSplit;
-  int G = kThreads / (16 * (int)a.M);
-  G = G >= 32 ? 32 : (G >= 16 ? 16 : (G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1))));
-  p.epi_group = G;
   // batches of kBatch blocks per wave (the weight tile's split of K)
   const int nblk = (int)(a.K / 64);
   const int per = ((nblk + kWaves - 1) / kWaves + kBatch - 1) / kBatch * kBatch;

@@ -64,7 +64,6 @@ struct DecodeParams {
   char* ws;
   int n_htiles;
   int n_wtiles;
-  int epi_group;   // threads per output in the epilogue (power of two, <= 32)
   int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
   int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
   uint32_t hi[16]; // bf16(level) per code
@@ -222,17 +221,6 @@ __device__ __forceinline__ float wave_sum(float v) {   // every lane: the wave's
   return swap32_add(v, v);
 }
 
-// Sum over aligned groups of G lanes (G a power of two, 1..32): every lane
-// of a group ends with its group's sum.
-__device__ __forceinline__ float group_sum(float v, int G) {
-  if (G >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  if (G >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  if (G >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-  if (G >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-  if (G >= 32) v = swap16_add(v, v);
-  return v;
-}
-
 // The launch arguments both paths of a kernel use, fetched in one round trip
 // ahead of the first branch (left alone, each branch waits for its own).
 #define QLORA_FETCH_ARGS(p)                                                                              \
@@ -246,8 +234,8 @@ __device__ __forceinline__ float group_sum(float v, int G) {
                  "s"((p).hi[15]));                                                                       \
   } while (0)
 
-// Host side: the parameters every decode path shares (tile counts and the
-// epilogue group are set by the path).
+// Host side: the parameters every decode path shares (the LoRA-down tile
+// count is set by the path).
 inline DecodeParams decode_params(const FwdArgs& a) {
   DecodeParams p;
   p.X = a.X;
@@ -268,7 +256,6 @@ inline DecodeParams decode_params(const FwdArgs& a) {
   p.H = a.H;
   p.n_htiles = 0;
   p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
-  p.epi_group = 1;
   p.c2_vec = (a.K % 256 == 0) && (reinterpret_cast<uintptr_t>(a.w.c2) % 4 == 0);
   p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
   const Nf4HiLo& hl = nf4_hilo();
