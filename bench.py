@@ -237,12 +237,16 @@ def bench_decoder(torch, qa, reps, seed=5):
 
 # ----------------------------------------------------------------------------- traffic from counters
 
-def kernel_source_hash(name):
-    with open(os.path.join(ROOT, "bit_nf4_quantized_quant_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(names):
+    """sha256[:16] over the kernel's source files, concatenated in order."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "bit_nf4_quantized_quant_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def recorded_traffic(summary_name, source_name):
+def recorded_traffic(summary_name, source_names):
     """HBM bytes per launch recorded in a profiles/ summary, or None when the
     kernel source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", summary_name)
@@ -251,7 +255,7 @@ def recorded_traffic(summary_name, source_name):
     text = open(path).read()
     m_hash = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]+)", text)
     m_traf = re.search(r"HBM traffic per launch \(bytes\):\s*([0-9.e+]+)", text)
-    if not m_hash or not m_traf or m_hash.group(1) != kernel_source_hash(source_name):
+    if not m_hash or not m_traf or m_hash.group(1) != kernel_source_hash(source_names):
         return None
     return float(m_traf.group(1))
 
@@ -371,7 +375,7 @@ def main():
             f"M=512 {res['m512']['ms']:.3f} ms ({res['m512']['TFLOPs']:.0f} TFLOP/s)")
         torch.cuda.empty_cache()
 
-    traffic = recorded_traffic("qlora_decode_kernel_decode_4096x4096_m1.md", "decode.hip")
+    traffic = recorded_traffic("qlora_gemv_kernel_decode_4096x4096_m1.md", ["gemv.hip", "decode_common.h"])
     line = {
         "metric": METRIC,
         "value": round(head["GBps"], 2),
