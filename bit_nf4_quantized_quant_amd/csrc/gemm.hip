@@ -9,13 +9,14 @@
 // y = W x + (alpha/r) B A x; backward updates A and B only.
 //
 // The engine computes C[i][j] = sum_k Aop[i][k] * Bop[j][k] for a BM x BN
-// output tile: both operands are staged in LDS as [rows][64 + 8] bf16 tiles
-// (reduction contiguous, 16-byte pad so that 16-byte fragment reads of eight
-// consecutive rows hit distinct banks), double-buffered with one barrier per
-// 64-wide reduction step.  2 x WN waves each own (BM/2) x (BN/WN) of the
-// tile as 32x32x16 MFMA accumulators: 4 waves for 128 x 128 tiles, 8 waves
-// (two per SIMD, so one wave's dequantization overlaps the other's MFMAs)
-// for 256 x 256 tiles.
+// output tile, double-buffered in LDS with one barrier per 64-wide reduction
+// step.  2 x WN waves each own (BM/2) x (BN/WN) of the tile as 32x32x16 MFMA
+// accumulators: 4 waves for 128 x 128 tiles, 8 waves (two per SIMD, so one
+// wave's dequantization overlaps the other's MFMAs) for 256 x 256 tiles.
+// The forward product keeps its operands in fragment-major tiles (below)
+// with loads two steps ahead; the backward's products stage [rows][64 + 8]
+// bf16 tiles (reduction contiguous, 16-byte pad so that 16-byte fragment
+// reads of eight consecutive rows hit distinct banks).
 //
 // Loaders turn every source layout into that LDS form:
 //   RowsBf16  bf16 [rows][red] (X, dY, A, B)
