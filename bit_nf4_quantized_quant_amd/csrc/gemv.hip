@@ -34,16 +34,18 @@ namespace {
 // H[m][j] as one tagged word.
 constexpr int kGvRowsPerWave = 4;
 
+// kDw: the rows of c2 are dword aligned (K % 256 == 0, 4-byte aligned base):
+// c2 comes as the dword holding the block's byte.
 template <int M>
 struct GvPiece {
   u32x4 x[M][4];               // the piece's 32 X values per batch row
   u32x4 w[kGvRowsPerWave];     // 16 bytes of codes per row
-  uint8_t c2[kGvRowsPerWave];  // (bytes: widened where used, not ahead of a loop)
+  uint32_t c2[kGvRowsPerWave];   // the c2 byte, or (kDw) the dword holding it
   float c1[kGvRowsPerWave];
 };
 
 // piece c of each of the wave's rows (c < K / 32), X first: it is used first
-template <int M>
+template <int M, bool kDw>
 __device__ __forceinline__ void gv_load(const DecodeParams& p, const rsrc_t& rc, const rsrc_t& r2, const rsrc_t& r1,
                                         const rsrc_t& rx, const uint32_t (&row)[kGvRowsPerWave], uint32_t c,
                                         GvPiece<M>& L) {
@@ -54,23 +56,31 @@ __device__ __forceinline__ void gv_load(const DecodeParams& p, const rsrc_t& rc,
     for (int q = 0; q < 4; ++q)
       L.x[m][q] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ((uint32_t)m * p.K + 32 * c) * 2 + 16 * q, 0, 0));
-  // (constants through plain byte loads, which widen for free, on a row
-  // clamped to N - 1; the buffer form's byte result costs a separate
-  // widening instruction, which the compiler places early)
+  // (a byte load's result needs a widening instruction, which the compiler
+  // moves next to the load, where it waits for the reply: so c2 comes as a
+  // dword when the rows allow, else through plain byte loads on a row
+  // clamped to N - 1)
   const uint32_t last = (uint32_t)p.N - 1u, n_c2 = (uint32_t)p.N * nblk;
 #pragma unroll
   for (int rr = 0; rr < kGvRowsPerWave; ++rr) {
-    const uint32_t rowc = row[rr] < last ? row[rr] : last;
-    const uint32_t blk = rowc * nblk + (c >> 1);
+    const uint32_t blk = row[rr] * nblk + (c >> 1);
     L.w[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, row[rr] * rb + 16 * c, 0, 0));
-    L.c2[rr] = p.c2[blk < n_c2 ? blk : n_c2 - 1u];
+    if constexpr (kDw) {
+      L.c2[rr] = __builtin_amdgcn_raw_buffer_load_b32(r2, blk & ~3u, 0, 0);   // rows >= N read as 0
+    } else {
+      const uint32_t rowc = row[rr] < last ? row[rr] : last;
+      const uint32_t bc = rowc * nblk + (c >> 1);
+      L.c2[rr] = p.c2[bc < n_c2 ? bc : n_c2 - 1u];
+    }
     L.c1[rr] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (blk >> 8) * 4, 0, 0));
   }
 }
 
-template <int M>
+// c2sh: with kDw, 8 x the byte's place in its dword (the same for the four
+// rows: rows of c2 are dword aligned)
+template <int M, bool kDw>
 __device__ __forceinline__ void gv_mul(const GvPiece<M>& L, float mu, const char* lut, uint32_t lane4,
-                                       float (&acc)[kGvRowsPerWave][M]) {
+                                       uint32_t c2sh, float (&acc)[kGvRowsPerWave][M]) {
 #pragma unroll
   for (int rr = 0; rr < kGvRowsPerWave; ++rr) {
     float part[M];
@@ -96,7 +106,12 @@ __device__ __forceinline__ void gv_mul(const GvPiece<M>& L, float mu, const char
         }
       }
     }
-    const float chat = dequant_constant(L.c2[rr], L.c1[rr], mu);
+    // (the empty asm keeps the work on the loaded byte here, where it is
+    // used; otherwise the compiler moves it next to the load, into a wait)
+    uint32_t c2 = L.c2[rr];
+    asm volatile("" : "+v"(c2));
+    if constexpr (kDw) c2 >>= c2sh;
+    const float chat = dequant_constant(c2, L.c1[rr], mu);
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[rr][m] = __builtin_fmaf(chat, part[m], acc[rr][m]);
   }
@@ -150,8 +165,12 @@ __device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_
   }
 }
 
-template <int M>
+// kNPL: 16-byte pieces per lane and row (the launcher's exact count), or 0
+// for any count (the launcher takes 0 whenever the rows of c2 are not dword
+// aligned).
+template <int M, int kNPL>
 __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red, uint32_t* tag_lds) {
+  constexpr bool kDw = kNPL > 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = wave & 3, half = wave >> 2;
   const float mu = load_mean(p);
@@ -173,59 +192,85 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   const int hp = p.K / 64;                 // pieces per row in each half of K
   const int npl = (hp + 63) / 64;          // pieces per lane
   const uint32_t c0 = (uint32_t)(half * hp + lane);
-  // two pieces in flight at M = 1; at M = 2 one (registers)
-  constexpr bool kTwo = M == 1;
-  GvPiece<M> La, Lb;
-  gv_load<M>(p, rc, r2, r1, rx, row, c0, La);
-  if (kTwo && 1 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64, Lb);
-
-  // the pair table, while the loads are in flight
-  build_pair_table<kThreads>(p, lut);
-  __syncthreads();
-
   const uint32_t lane4 = (uint32_t)(lane & 31) * 4u;
   float acc[kGvRowsPerWave][M];
 #pragma unroll
   for (int rr = 0; rr < kGvRowsPerWave; ++rr)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[rr][m] = 0.f;
-  if constexpr (kTwo) {
-    for (int i = 0; i < npl; i += 2) {
-      if (i != 0 && i + 1 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 1), Lb);
-      if (lane + 64 * i < hp) gv_mul<M>(La, mu, lut, lane4, acc);
-      if (i + 2 < npl) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 2), La);
-      if (i + 1 < npl && lane + 64 * (i + 1) < hp) gv_mul<M>(Lb, mu, lut, lane4, acc);
+
+  // LoRA operands of the second half's waves (see the epilogue): B[row][j]
+  // for j = lane, lane + 64 and the first read of this launch's H partials
+  const bool lora = p.r > 0;
+  const int r16 = (p.r + 15) & ~15;
+  uint32_t bv[kGvRowsPerWave][2];
+  uint64_t hv[M][2];
+  auto read_lora = [&]() {
+    if (half == 1 && lora) {
+      const uint32_t last = (uint32_t)p.N - 1u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = lane + 64 * h;
+        if (j >= p.r) continue;
+        // plain 16-bit loads (they widen for free) on rows clamped to N - 1
+#pragma unroll
+        for (int rr = 0; rr < kGvRowsPerWave; ++rr)
+          bv[rr][h] = p.B[(size_t)(row[rr] < last ? row[rr] : last) * p.r + j];
+#pragma unroll
+        for (int m = 0; m < M; ++m) hv[m][h] = ld_tagged(&p.Hpart[(size_t)m * r16 + j]);
+      }
     }
+  };
+
+  if constexpr (kNPL > 0) {
+    // A known piece count: every load is issued whatever the lane's share
+    // (offsets of pieces past the row end stay in bounds or read zero; their
+    // products are skipped), so each wait counts exactly the loads issued
+    // after the one it waits for.  Two pieces in flight at M = 1, one at
+    // M = 2 (registers).
+    constexpr int kDepth = M == 1 ? 2 : 1;
+    GvPiece<M> L[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth && i < kNPL; ++i) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64 * i, L[i]);
+    build_pair_table<kThreads>(p, lut);   // while the loads are in flight
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kNPL; ++i) {
+      GvPiece<M>& cur = L[i % kDepth];
+      if (lane + 64 * i < hp) gv_mul<M, kDw>(cur, mu, lut, lane4, 8u * (((c0 + 64 * i) >> 1) & 3u), acc);
+      if (i + kDepth < kNPL) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64 * (i + kDepth), cur);
+    }
+    // (read here, H has been published by now: read any earlier, the first
+    // read comes back stale and the poll adds a round trip)
+    read_lora();
   } else {
-    for (int i = 0; i < npl; ++i) {
-      if (i != 0) gv_load<M>(p, rc, r2, r1, rx, row, c0 + 64 * i, La);
-      if (lane + 64 * i < hp) gv_mul<M>(La, mu, lut, lane4, acc);
+    // two pieces in flight at M = 1; at M = 2 one (registers)
+    constexpr bool kTwo = M == 1;
+    GvPiece<M> La, Lb;
+    gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0, La);
+    if (kTwo && 1 < npl) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64, Lb);
+    build_pair_table<kThreads>(p, lut);   // while the loads are in flight
+    __syncthreads();
+    if constexpr (kTwo) {
+      for (int i = 0; i < npl; i += 2) {
+        if (i != 0 && i + 1 < npl) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 1), Lb);
+        if (lane + 64 * i < hp) gv_mul<M, kDw>(La, mu, lut, lane4, 0u, acc);
+        if (i + 2 < npl) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64 * (i + 2), La);
+        if (i + 1 < npl && lane + 64 * (i + 1) < hp) gv_mul<M, kDw>(Lb, mu, lut, lane4, 0u, acc);
+      }
+    } else {
+      for (int i = 0; i < npl; ++i) {
+        if (i != 0) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64 * i, La);
+        if (lane + 64 * i < hp) gv_mul<M, kDw>(La, mu, lut, lane4, 0u, acc);
+      }
     }
+    read_lora();
   }
 
   // Epilogue.  Waves of the first half of K reduce their sums and leave them
   // in LDS, and thread 0 publishes the launch tag there; waves of the second
   // half add s H B^T (H from this launch's tagged partials, tag = epoch + 1,
   // polled until present), their own sums and the first half's, and store.
-  // The second half reads B and H before the barrier: the replies come back
-  // while it waits.
-  const bool lora = p.r > 0;
-  uint32_t bv[kGvRowsPerWave][2];
-  uint64_t hv[M][2];
-  const int r16 = (p.r + 15) & ~15;
-  if (half == 1 && lora) {
-    const rsrc_t rbb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = lane + 64 * h;
-      if (j >= p.r) continue;
-#pragma unroll
-      for (int rr = 0; rr < kGvRowsPerWave; ++rr)
-        bv[rr][h] = __builtin_amdgcn_raw_buffer_load_b16(rbb, (row[rr] * p.r + j) * 2, 0, 0);
-#pragma unroll
-      for (int m = 0; m < M; ++m) hv[m][h] = ld_tagged(&p.Hpart[(size_t)m * r16 + j]);
-    }
-  }
   const int rt = lane >> 4;   // this lane's row in the wave's group, if lane % 16 == 0
   if (half == 0) {
 #pragma unroll
@@ -257,8 +302,11 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
         if (tile == 0 && grp == 0 && p.H) p.H[m * p.r + j] = hval;
         const float sh = p.scale * hval;
 #pragma unroll
-        for (int rr = 0; rr < kGvRowsPerWave; ++rr)
-          acc[rr][m] = __builtin_fmaf(sh, __uint_as_float(bv[rr][h] << 16), acc[rr][m]);
+        for (int rr = 0; rr < kGvRowsPerWave; ++rr) {
+          uint32_t b = bv[rr][h];
+          asm volatile("" : "+v"(b));   // (as for c2: the widening stays here)
+          acc[rr][m] = __builtin_fmaf(sh, __uint_as_float(b << 16), acc[rr][m]);
+        }
       }
     }
   }
@@ -275,7 +323,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   }
 }
 
-template <int M>
+template <int M, int kNPL>
 __global__ void __launch_bounds__(kThreads, 2) qlora_gemv_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];   // 64 KiB
   __shared__ float red[kRows * M];
@@ -288,7 +336,19 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_gemv_kernel(DecodeParams p)
     gemv_down_tile<M>(p, tile, red, &tag, hticket);
     return;
   }
-  gemv_tile<M>(p, tile - p.n_htiles, lut, red, &tag);
+  gemv_tile<M, kNPL>(p, tile - p.n_htiles, lut, red, &tag);
+}
+
+typedef void (*GemvKernel)(DecodeParams);
+template <int M>
+GemvKernel gemv_kernel(int npl) {
+  switch (npl) {
+    case 1: return qlora_gemv_kernel<M, 1>;
+    case 2: return qlora_gemv_kernel<M, 2>;
+    case 3: return qlora_gemv_kernel<M, 3>;
+    case 4: return qlora_gemv_kernel<M, 4>;
+    default: return qlora_gemv_kernel<M, 0>;
+  }
 }
 
 }  // namespace
@@ -296,11 +356,10 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_gemv_kernel(DecodeParams p)
 hipError_t launch_gemv_fwd(const DecodeParams& p0, hipStream_t s) {
   DecodeParams p = p0;
   p.n_htiles = p.r;   // one LoRA-down workgroup per row of A
+  const int hp = p.K / 64, npl = p.c2_vec ? (hp + 63) / 64 : 0;
+  const GemvKernel k = p.M == 1 ? gemv_kernel<1>(npl) : gemv_kernel<2>(npl);
   const dim3 grid(p.n_htiles + p.n_wtiles);
-  if (p.M == 1)
-    hipLaunchKernelGGL(qlora_gemv_kernel<1>, grid, dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(qlora_gemv_kernel<2>, grid, dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
