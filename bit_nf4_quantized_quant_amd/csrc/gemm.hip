@@ -954,6 +954,125 @@ __global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
   }
 }
 
+// ---------------------------------------------------------------- dX at large M
+// At large M the backward's dX = dY W_deq is a dense, compute-bound product
+// whose reduction runs over the weight's rows n.  The weight is then expanded
+// once per call into a scratch W_deq^T, bf16 [K][ldt] (ldt = N rounded up to
+// 64, zero past N), and the product runs on the pipelined bf16 engine with
+// both operands stored along the reduction.  The expansion moves 2.5 bytes
+// per weight (codes in, bf16 out), a few percent of the product's time at
+// M >= 512; below that the fused dx_gemm_kernel reads the codes directly.
+constexpr int64_t kDxtMinM = 512;
+constexpr int kDtN = 64, kDtK = 128;   // tile of the transposing expansion (n x k)
+
+// W_deq^T tile: thread t takes rows n0 + 2 (t % 32) + {0, 1} and the 16
+// columns k0 + 16 (t / 32) .. +15 (one block of each row, so one constant
+// per row), expands them to bf16 (fp32 level * c_hat, bit-exact with W_deq),
+// and stores (n, n+1) pairs per column into an LDS tile [k][n]; the tile then
+// leaves as 128-byte rows of the output.
+__global__ void __launch_bounds__(256) nf4_dequant_t_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ c2,
+                                                            const float* __restrict__ c1,
+                                                            const float* __restrict__ mean, int64_t N, int64_t K,
+                                                            int64_t ldt, uint16_t* __restrict__ out, Nf4Table tab) {
+  __shared__ float lut[16];
+  __shared__ __attribute__((aligned(16))) uint32_t t[kDtK * kDtN / 2];   // [k][n pair], 16 KiB
+  load_lut(lut, tab);
+  const int64_t ntiles = ldt / kDtN;
+  const int64_t n0 = (int64_t)(blockIdx.x % ntiles) * kDtN, k0 = (int64_t)(blockIdx.x / ntiles) * kDtK;
+  const int np = threadIdx.x & 31, kg = threadIdx.x >> 5;
+  const int64_t kc = k0 + 16 * kg;
+  const float mu = *mean;
+  uint32_t w[2][2];
+  float chat[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t n = n0 + 2 * np + h;
+    if (n < N && kc < K) {
+      const uint8_t* src = codes + n * (K / 2) + kc / 2;
+      w[h][0] = *reinterpret_cast<const uint32_t*>(src);
+      w[h][1] = *reinterpret_cast<const uint32_t*>(src + 4);
+      const int64_t bi = n * (K / 64) + kc / 64;
+      chat[h] = dequant_constant(c2[bi], c1[bi >> 8], mu);
+    } else {   // rows past N (and columns past K) expand to zero
+      w[h][0] = w[h][1] = 0u;
+      chat[h] = 0.f;
+    }
+  }
+  __syncthreads();   // the level table
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float lo = __fmul_rn(lut[(w[0][e >> 3] >> (4 * (e & 7))) & 15u], chat[0]);
+    const float hi = __fmul_rn(lut[(w[1][e >> 3] >> (4 * (e & 7))) & 15u], chat[1]);
+    t[(16 * kg + e) * (kDtN / 2) + np] = pack_bf16x2(lo, hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kDtK * kDtN / 8 / 256; ++i) {
+    const int c = threadIdx.x + i * 256, kr = c >> 3, j = c & 7;
+    const int64_t k = k0 + kr;
+    if (k < K) *reinterpret_cast<u32x4*>(out + k * ldt + n0 + 8 * j) = *reinterpret_cast<const u32x4*>(&t[kr * 32 + 4 * j]);
+  }
+}
+
+struct DxtParams {
+  const uint16_t* dY;
+  const uint16_t* wt;   // W_deq^T [K][ldt]
+  int64_t M, N, K, ldt;
+  int r;
+  const float* dH;
+  const uint16_t* A;
+  uint16_t* dX;
+  float* part;          // split-K partials [splits][M][K] (splits > 1)
+  int splits, steps_per_split;
+  int mtiles, ntiles, gm;
+};
+
+// dX = dY W_deq + dH A on the pipelined engine: rows of dY (reduction n
+// contiguous; past N they meet W_deq^T's zero columns) against rows of
+// W_deq^T.  kVecY: N % 8 == 0 (16-byte rows of dY).
+template <int BM, int BN, int WN, bool kVecY>
+__global__ void __launch_bounds__(128 * WN) dxt_gemm_kernel(DxtParams p) {
+  constexpr int T = 128 * WN;
+  extern __shared__ __attribute__((aligned(16))) lds_t smem[];
+  lds_t* sa = smem;
+  lds_t* sb = smem + 2 * BM * BK;   // fragment-major tiles, double-buffered
+  const int tiles = p.mtiles * p.ntiles;
+  const int split = (int)blockIdx.x / tiles;
+  int mi, ki;
+  tile_of((int)blockIdx.x - split * tiles, p.mtiles, p.ntiles, p.gm, mi, ki);
+  const int64_t m0 = (int64_t)mi * BM, k0 = (int64_t)ki * BN;
+  const int nsteps = (int)(p.ldt / BK);
+  const int nt0 = split * p.steps_per_split, nt1 = min(nsteps, nt0 + p.steps_per_split);
+  Acc<BM, BN, WN> acc;
+  zero(acc);
+  __syncthreads();
+  {
+    XRows<BM, T, kVecY, (WN == 4 && kVecY ? 2 : 1)> la;
+    la.init(p.dY, p.N, p.M, m0);
+    XRows<BN, T, true, (WN == 4 ? 2 : 1)> lb;
+    lb.init(p.wt, p.ldt, p.K, k0);
+    run_pipelined<BM, BN, WN>(la, lb, nt0, nt1, sa, sb, acc);
+  }
+  if (split == 0)
+    lora_tail<BM, BN, WN>(
+        acc, p.r,
+        [&](int i, int kk) { return frag_f32_row(p.dH, p.r, m0 + i, p.M, kk, p.r, 1.0f); },
+        [&](int j, int kk) { return frag_bf16_col(p.A, p.K, k0 + j, p.K, kk, p.r); });
+  if (p.splits == 1) {
+    for_each_out(acc, [&](int i, int j, float v) {
+      const int64_t m = m0 + i, k = k0 + j;
+      if (m < p.M && k < p.K) p.dX[m * p.K + k] = to_bf16(v);
+    });
+  } else {
+    float* out = p.part + (int64_t)split * p.M * p.K;
+    for_each_out(acc, [&](int i, int j, float v) {
+      const int64_t m = m0 + i, k = k0 + j;
+      if (m < p.M && k < p.K) out[m * p.K + k] = v;
+    });
+  }
+}
+
 // Skinny-product loaders with a per-tile origin, built on the loaders above.
 template <int R>
 struct SRowsBf16 : RowsBf16<R, NT> {
@@ -1028,12 +1147,20 @@ size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r) {
 template <class Kern, class P>
 hipError_t launch_tiled(Kern kern, int threads, size_t lds, int mtiles, int ntiles, int splits, P& p,
                         hipStream_t s) {
-  static bool attr_set = false;  // per instantiation; setting it twice is harmless
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // the LDS limit is raised once per kernel (several kernels can share this
+  // instantiation: remember which ones; setting it twice is harmless)
+  static const void* done[8] = {};
+  const void* kp = reinterpret_cast<const void*>(kern);
+  bool seen = false;
+  for (const void* d : done) seen = seen || d == kp;
+  if (!seen) {
+    hipError_t e = hipFuncSetAttribute(kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    for (const void*& d : done)
+      if (!d) {
+        d = kp;
+        break;
+      }
   }
   p.mtiles = mtiles;
   p.ntiles = ntiles;
@@ -1105,10 +1232,13 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Backward workspace: H (if recomputed), dH, and split-K partials.
+// Backward workspace: H (if recomputed), dH, split-K partials and, at large
+// M, the expanded W_deq^T.
 struct BwdPlan {
   int s_dh, s_db, s_da;
-  size_t off_H, off_dH, off_part, bytes;
+  bool dxt;        // dX through the expanded W_deq^T
+  int64_t ldt;     // its row length (N rounded up to 64)
+  size_t off_H, off_dH, off_part, off_wt, bytes;
 };
 
 static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -1122,9 +1252,12 @@ static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   b.off_part = b.off_dH + al((size_t)M * r * 4);
   size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * r, (size_t)b.s_da * r * K}) * 4;
   part = std::max(part, lora_down_scratch_bytes(M, K, r));
-  const GemmPlan g = gemm_plan(M, K, (N + BK - 1) / BK);
+  b.dxt = M >= kDxtMinM && N > 0;
+  b.ldt = (N + 63) / 64 * 64;
+  const GemmPlan g = gemm_plan(M, K, b.dxt ? b.ldt / BK : (N + BK - 1) / BK);
   if (g.splits > 1) part = std::max(part, (size_t)g.splits * M * K * sizeof(float));
-  b.bytes = b.off_part + al(part);
+  b.off_wt = b.off_part + al(part);
+  b.bytes = b.off_wt + (b.dxt ? al((size_t)b.ldt * K * 2) : 0);
   return b;
 }
 
@@ -1178,7 +1311,37 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     }
   }
   // dX = dY W_deq + dH A
-  if (a.dX && a.M > 0) {
+  if (a.dX && a.M > 0 && plan.dxt) {
+    uint16_t* wt = reinterpret_cast<uint16_t*>(ws + plan.off_wt);
+    hipLaunchKernelGGL(nf4_dequant_t_kernel, dim3((unsigned)((plan.ldt / kDtN) * cdiv(a.K, kDtK))), dim3(256), 0, s,
+                       a.w.codes, a.w.c2, a.w.c1, a.w.mean, a.N, a.K, plan.ldt, wt, nf4_table());
+    DxtParams p;
+    p.dY = a.dY;
+    p.wt = wt;
+    p.M = a.M;
+    p.N = a.N;
+    p.K = a.K;
+    p.ldt = plan.ldt;
+    p.r = (int)a.r;
+    p.dH = dH;
+    p.A = a.A;
+    p.dX = a.dX;
+    const GemmPlan g = gemm_plan(a.M, a.K, plan.ldt / BK);
+    p.part = part;
+    p.splits = g.splits;
+    p.steps_per_split = g.steps_per_split;
+    const bool vy = (a.N % 8) == 0;
+    if (g.tile == 256)
+      e = launch_tiled(vy ? dxt_gemm_kernel<256, 256, 4, true> : dxt_gemm_kernel<256, 256, 4, false>, 512,
+                       frag_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits, p, s);
+    else
+      e = launch_tiled(vy ? dxt_gemm_kernel<128, 128, 2, true> : dxt_gemm_kernel<128, 128, 2, false>, 256,
+                       frag_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits, p, s);
+    if (e != hipSuccess) return e;
+    if (g.splits > 1)
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.K, 256), 4096)),
+                         dim3(256), 0, s, part, g.splits, (int64_t)(a.M * a.K), 1.0f, a.dX, (float*)nullptr);
+  } else if (a.dX && a.M > 0) {
     DxParams p;
     p.dY = a.dY;
     p.M = a.M;
