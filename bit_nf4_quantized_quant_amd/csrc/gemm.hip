@@ -19,11 +19,10 @@
 // reads of eight consecutive rows hit distinct banks).
 //
 // Loaders turn every source layout into that LDS form:
-//   RowsBf16  bf16 [rows][red] (X, dY, A, B)
+//   RowsBf16  bf16 [rows][red] (X, dY, A, B, and the bf16 H^T, dH^T)
 //   Nf4Rows   NF4 codes [rows][K/2] -> bf16 W_deq, bit-exact with the spec
 //   Nf4Cols   NF4 codes read as [red = n][rows = k]: the transposed weight for dX
 //   ColsBf16  bf16 [red][rows] (transposed operands of the LoRA gradients)
-//   RowsF32 / ColsF32  fp32 sources (H, dH) rounded to bf16, optionally scaled
 // A transposed source is read as 4 x 8 patches (4 rows of 8 contiguous
 // elements) and written to LDS as 8 rows of 4 reduction elements.
 #include <algorithm>
@@ -100,46 +99,6 @@ struct RowsBf16 {
   }
 };
 
-// fp32 source with rows contiguous in the reduction index, scaled and rounded to bf16.
-template <int R, int T = NT>
-struct RowsF32 {
-  static constexpr int kChunks = R * BK / 8 / T;
-  const float* src;
-  int64_t ld;
-  int rows;
-  int red;
-  int64_t row0;
-  float scale;
-  u32x4 reg[kChunks];
-
-  __device__ __forceinline__ void load(int kt) {
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int idx = threadIdx.x + c * T;
-      const int rr = idx >> 3, ch = idx & 7;
-      const int k = kt * BK + ch * 8;
-      float f[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) f[q] = 0.f;
-      if (rr < rows) {
-        const float* p = src + (row0 + rr) * ld + k;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (k + q < red) f[q] = p[q] * scale;
-      }
-      reg[c] = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                     pack_bf16x2(f[6], f[7])};
-    }
-  }
-  __device__ __forceinline__ void store(lds_t* t) const {
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int idx = threadIdx.x + c * T;
-      st_lds16(t + (idx >> 3) * PITCH + (idx & 7) * 8, reg[c]);
-    }
-  }
-};
-
 // bf16 source stored [red][rows]: tile row i is source column col0 + i.
 template <int R, int T = NT>
 struct ColsBf16 {
@@ -194,48 +153,6 @@ struct ColsBf16 {
         st_lds8(t + (pc * 8 + 2 * w + 1) * PITCH + pr * 4, b);
       }
     }
-  }
-};
-
-// fp32 source stored [red][rows], rounded to bf16 (optionally scaled).
-template <int R, int T = NT>
-struct ColsF32 {
-  static constexpr int kPatches = 2 * R;
-  const float* src;
-  int64_t ld;
-  int cols;
-  int red;
-  int64_t col0;
-  float scale;
-  uint32_t reg[8][2];
-  bool active;
-
-  __device__ __forceinline__ void load(int kt) {
-    const int pid = threadIdx.x;
-    active = pid < kPatches;
-    if (!active) return;
-    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
-    const int c = pc * 8;
-    float f[4][8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = kt * BK + pr * 4 + q;
-      const float* p = src + (int64_t)k * ld + col0 + c;
-#pragma unroll
-      for (int z = 0; z < 8; ++z) f[q][z] = (k < red && c + z < cols) ? p[z] * scale : 0.f;
-    }
-#pragma unroll
-    for (int z = 0; z < 8; ++z) {
-      reg[z][0] = pack_bf16x2(f[0][z], f[1][z]);
-      reg[z][1] = pack_bf16x2(f[2][z], f[3][z]);
-    }
-  }
-  __device__ __forceinline__ void store(lds_t* t) const {
-    if (!active) return;
-    const int pid = threadIdx.x;
-    const int pr = pid % (BK / 4), pc = pid / (BK / 4);
-#pragma unroll
-    for (int z = 0; z < 8; ++z) st_lds8(t + (pc * 8 + z) * PITCH + pr * 4, u32x2{reg[z][0], reg[z][1]});
   }
 };
 
@@ -893,6 +810,38 @@ __global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restr
   }
 }
 
+// out[c][r] = bf16(src[r][c]) for an fp32 src [rows][cols] (out row length
+// rows): the LoRA factors' gradients take H and dH with the reduction index m
+// contiguous, as 16-byte vector loads.  16 x 64 tiles through LDS (one
+// workgroup per 16 rows, so a 4096-row source fills the chip); each thread
+// stores pairs of consecutive rows (4 bytes).
+__global__ void __launch_bounds__(256) f32_to_bf16_t_kernel(const float* __restrict__ src, int64_t rows,
+                                                            int64_t cols, uint16_t* __restrict__ out) {
+  __shared__ float t[16][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 16, c0 = (int64_t)blockIdx.y * 64;
+  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + tr + 4 * i, c = c0 + tc;
+    t[tr + 4 * i][tc] = (r < rows && c < cols) ? src[r * cols + c] : 0.f;
+  }
+  __syncthreads();
+  const int pr = threadIdx.x & 7, pc = threadIdx.x >> 3;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cc = pc + 32 * i;
+    const int64_t c = c0 + cc, r = r0 + 2 * pr;
+    if (c >= cols || r >= rows) continue;
+    const uint32_t v = pack_bf16x2(t[2 * pr][cc], t[2 * pr + 1][cc]);
+    if (r + 1 < rows && (rows & 1) == 0)
+      *reinterpret_cast<uint32_t*>(out + c * rows + r) = v;
+    else {
+      out[c * rows + r] = (uint16_t)(v & 0xFFFFu);
+      if (r + 1 < rows) out[c * rows + r + 1] = (uint16_t)(v >> 16);
+    }
+  }
+}
+
 // dX = dY W_deq + dH A (bf16 output).  Phase 1 contracts over n with the
 // transposed NF4 weight; phase 2 appends r steps of dH against A^T.
 struct DxParams {
@@ -1088,14 +1037,6 @@ struct SColsBf16 : ColsBf16<R, NT> {
     this->cols = (int)lmin(R, total - o);
   }
 };
-template <int R>
-struct SColsF32 : ColsF32<R, NT> {
-  __device__ __forceinline__ void row_origin(int64_t o, int64_t total) {
-    this->col0 = o;
-    this->cols = (int)lmin(R, total - o);
-  }
-};
-
 unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 template <int BM, int BN, class LA, class LB>
@@ -1232,13 +1173,13 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Backward workspace: H (if recomputed), dH, split-K partials and, at large
-// M, the expanded W_deq^T.
+// Backward workspace: H (if recomputed), dH, their bf16 transposes, split-K
+// partials and, at large M, the expanded W_deq^T.
 struct BwdPlan {
   int s_dh, s_db, s_da;
   bool dxt;        // dX through the expanded W_deq^T
   int64_t ldt;     // its row length (N rounded up to 64)
-  size_t off_H, off_dH, off_part, off_wt, bytes;
+  size_t off_H, off_dH, off_Ht, off_dHt, off_part, off_wt, bytes;
 };
 
 static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -1249,7 +1190,9 @@ static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   b.off_H = 0;
   b.off_dH = al((size_t)M * r * 4);
-  b.off_part = b.off_dH + al((size_t)M * r * 4);
+  b.off_Ht = b.off_dH + al((size_t)M * r * 4);     // bf16 H^T and dH^T [r][M]
+  b.off_dHt = b.off_Ht + al((size_t)M * r * 2);
+  b.off_part = b.off_dHt + al((size_t)M * r * 2);
   size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * r, (size_t)b.s_da * r * K}) * 4;
   part = std::max(part, lora_down_scratch_bytes(M, K, r));
   b.dxt = M >= kDxtMinM && N > 0;
@@ -1279,6 +1222,11 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     }
     const bool n_vec = (a.N % 8) == 0;
     const bool r_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
+    const bool m_vec = (a.M % 8) == 0;
+    uint16_t* Ht = reinterpret_cast<uint16_t*>(ws + plan.off_Ht);
+    uint16_t* dHt = reinterpret_cast<uint16_t*>(ws + plan.off_dHt);
+    const dim3 tgrid(cdiv(a.M, 16), cdiv(a.r, 64));
+    if (a.M > 0) hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, H, a.M, a.r, Ht);
     // dH = s dY B : rows m, cols j, reduction n
     if (a.M > 0) {
       SRowsBf16<128> la;
@@ -1288,21 +1236,22 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
       if ((e = launch_skinny<128, 64>(la, lb, a.M, a.r, a.N, plan.s_dh, part, s)) != hipSuccess) return e;
       hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.M * a.r, 256)), dim3(256), 0, s, part, plan.s_dh,
                          (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
+      hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, dH, a.M, a.r, dHt);
     }
     // dB = s dY^T H : rows n, cols j, reduction m
     if (a.N > 0) {
       SColsBf16<128> la;
       la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
-      SColsF32<64> lb;
-      lb.src = H; lb.ld = a.r; lb.red = (int)a.M; lb.scale = 1.0f;
+      SRowsBf16<64> lb;
+      lb.src = Ht; lb.ld = a.M; lb.red = (int)a.M; lb.vec = m_vec;
       if ((e = launch_skinny<128, 64>(la, lb, a.N, a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
       hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, part, plan.s_db,
                          (int64_t)(a.N * a.r), a.scale, a.dB, (float*)nullptr);
     }
     // dA = dH^T X : rows j, cols k, reduction m
     {
-      SColsF32<64> la;
-      la.src = dH; la.ld = a.r; la.red = (int)a.M; la.scale = 1.0f;
+      SRowsBf16<64> la;
+      la.src = dHt; la.ld = a.M; la.red = (int)a.M; la.vec = m_vec;
       SColsBf16<128> lb;
       lb.src = a.X; lb.ld = a.K; lb.red = (int)a.M; lb.vec = true;
       if ((e = launch_skinny<64, 128>(la, lb, a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
