@@ -668,6 +668,18 @@ __device__ __forceinline__ u32x4 frag_bf16_col(const uint16_t* src, int64_t ld, 
 
 // ---------------------------------------------------------------- kernels
 
+// A workgroup-uniform value computed with vector instructions (integer
+// division has no scalar form) moved back to a scalar register, so that the
+// step counters derived from it stay scalar: a buffer load's scalar offset
+// that lives in a vector register costs a loop around every load.
+// (Through an asm operand: the readfirstlane builtin is folded away when the
+// compiler knows the value is uniform, leaving it in the vector register.)
+__device__ __forceinline__ int uniform(int v) {
+  int r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+  return r;
+}
+
 // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each
 // with its own L2.  Workgroup L runs on XCD L % 8; give XCD x a contiguous
 // range of logical tiles (a bijection of [0, T)), and walk logical tiles in
@@ -683,8 +695,8 @@ __device__ __forceinline__ void tile_of(int L, int mtiles, int ntiles, int gm, i
   const int first_m = group * gm;
   const int gm_eff = min(gm, mtiles - first_m);
   const int in_group = logical - group * per_group;
-  mi = first_m + in_group % gm_eff;
-  ni = in_group / gm_eff;
+  mi = uniform(first_m + in_group % gm_eff);
+  ni = uniform(in_group / gm_eff);
 }
 
 // dynamic LDS of the pipelined products (fragment-major tiles, two buffers)
@@ -727,7 +739,7 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
   lds_t* sb = smem + 2 * BM * BK;   // fragment-major tiles, double-buffered
   load_lut(lut, p.tab);
   const int tiles = p.mtiles * p.ntiles;
-  const int split = (int)blockIdx.x / tiles;
+  const int split = uniform((int)blockIdx.x / tiles);
   int mi, ni;
   tile_of((int)blockIdx.x - split * tiles, p.mtiles, p.ntiles, p.gm, mi, ni);
   const int64_t m0 = (int64_t)mi * BM, n0 = (int64_t)ni * BN;
@@ -870,7 +882,7 @@ __global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
   float* lut = reinterpret_cast<float*>(sb + 2 * BN * PITCH);
   load_lut(lut, p.tab);
   const int tiles = p.mtiles * p.ntiles;
-  const int split = (int)blockIdx.x / tiles;
+  const int split = uniform((int)blockIdx.x / tiles);
   int mi, ki;
   tile_of((int)blockIdx.x - split * tiles, p.mtiles, p.ntiles, p.gm, mi, ki);
   const int64_t m0 = (int64_t)mi * BM, k0 = (int64_t)ki * BN;
@@ -987,7 +999,7 @@ __global__ void __launch_bounds__(128 * WN) dxt_gemm_kernel(DxtParams p) {
   lds_t* sa = smem;
   lds_t* sb = smem + 2 * BM * BK;   // fragment-major tiles, double-buffered
   const int tiles = p.mtiles * p.ntiles;
-  const int split = (int)blockIdx.x / tiles;
+  const int split = uniform((int)blockIdx.x / tiles);
   int mi, ki;
   tile_of((int)blockIdx.x - split * tiles, p.mtiles, p.ntiles, p.gm, mi, ki);
   const int64_t m0 = (int64_t)mi * BM, k0 = (int64_t)ki * BN;
