@@ -1,5 +1,5 @@
-// Fused QLoRA forward for 3 <= M <= 16 (decode), gfx950: the matrix-core
-// path.  (M <= 2 takes the GEMV path; the launcher dispatches.)
+// Fused QLoRA forward for 5 <= M <= 16 (decode), gfx950: the matrix-core
+// path.  (M <= 4 takes the GEMV path; the launcher dispatches.)
 //
 // Y = bf16( X W_deq^T + s (X A^T) B^T )   (itwiki "QLoRA", section on the
 // computation; minnong511 "quantization", y = W x + (alpha/r) B A x).
@@ -392,7 +392,7 @@ size_t decode_workspace_bytes(int64_t M, int64_t r) {
 
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   DecodeParams p = decode_params(a);
-  if (a.M <= 2) return launch_gemv_fwd(p, s);
+  if (a.M <= 4) return launch_gemv_fwd(p, s);
   const int64_t r16 = (a.r + 15) & ~15;
   p.n_htiles = (int)(r16 / kRows) * kHSplit;
   // batches of kBatch blocks per wave (the weight tile's split of K)

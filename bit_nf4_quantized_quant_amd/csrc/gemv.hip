@@ -1,9 +1,9 @@
-// Fused QLoRA forward for M <= 2 (decode), gfx950: the GEMV path.
+// Fused QLoRA forward for M <= 4 (decode), gfx950: the GEMV path.
 //
 // Y = bf16( X W_deq^T + s (X A^T) B^T )   (itwiki "QLoRA", section on the
 // computation; minnong511 "quantization", y = W x + (alpha/r) B A x).
 //
-// At M <= 2 the layer is bound by HBM bandwidth on the 4-bit weight.  The
+// At M <= 4 the layer is bound by HBM bandwidth on the 4-bit weight.  The
 // pages describe the slow path as a separate dequantization kernel whose bf16
 // output makes a round trip through memory before the matrix product
 // (irregular6612 "QLoRA - Efficient Finetuning of Quantized LLMs", the
@@ -227,7 +227,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
     // (offsets of pieces past the row end stay in bounds or read zero; their
     // products are skipped), so each wait counts exactly the loads issued
     // after the one it waits for.  Two pieces in flight at M = 1, one at
-    // M = 2 (registers).
+    // M >= 2 (registers).
     constexpr int kDepth = M == 1 ? 2 : 1;
     GvPiece<M> L[kDepth];
 #pragma unroll
@@ -244,7 +244,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
     // read comes back stale and the poll adds a round trip)
     read_lora();
   } else {
-    // two pieces in flight at M = 1; at M = 2 one (registers)
+    // two pieces in flight at M = 1; at M >= 2 one (registers)
     constexpr bool kTwo = M == 1;
     GvPiece<M> La, Lb;
     gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0, La);
@@ -323,8 +323,10 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   }
 }
 
+// Two workgroups per CU (4 waves per SIMD) up to M = 3; at M = 4 the X
+// registers need more, and one workgroup per CU runs faster than spilling.
 template <int M, int kNPL>
-__global__ void __launch_bounds__(kThreads, 2) qlora_gemv_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kThreads, M <= 3 ? 4 : 2) qlora_gemv_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];   // 64 KiB
   __shared__ float red[kRows * M];
   __shared__ uint32_t tag;
@@ -357,7 +359,10 @@ hipError_t launch_gemv_fwd(const DecodeParams& p0, hipStream_t s) {
   DecodeParams p = p0;
   p.n_htiles = p.r;   // one LoRA-down workgroup per row of A
   const int hp = p.K / 64, npl = p.c2_vec ? (hp + 63) / 64 : 0;
-  const GemvKernel k = p.M == 1 ? gemv_kernel<1>(npl) : gemv_kernel<2>(npl);
+  const GemvKernel k = p.M == 1 ? gemv_kernel<1>(npl)
+                      : p.M == 2 ? gemv_kernel<2>(npl)
+                      : p.M == 3 ? gemv_kernel<3>(npl)
+                                 : gemv_kernel<4>(npl);
   const dim3 grid(p.n_htiles + p.n_wtiles);
   hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
