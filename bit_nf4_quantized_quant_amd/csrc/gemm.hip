@@ -724,7 +724,8 @@ struct FwdGemmParams {
   bool b_vec;
   float scale;
   uint16_t* Y;
-  float* part;          // split-K partials [splits][M][N] (splits > 1)
+  int64_t ldy;          // elements between rows of Y (N, or more for a column range)
+  float* part;          // split-K partials [splits][M][N] (splits > 1, ldy = N)
   int splits, steps_per_split;
   int mtiles, ntiles, gm;
   Nf4Table tab;
@@ -763,7 +764,7 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
   if (p.splits == 1) {
     for_each_out(acc, [&](int i, int j, float v) {
       const int64_t m = m0 + i, n = n0 + j;
-      if (m < p.M && n < p.N) p.Y[m * p.N + n] = to_bf16(v);
+      if (m < p.M && n < p.N) p.Y[m * p.ldy + n] = to_bf16(v);
     });
   } else {
     float* out = p.part + (int64_t)split * p.M * p.N;
@@ -1151,35 +1152,71 @@ size_t gemm_fwd_scratch_bytes(int64_t M, int64_t N, int64_t K) {
   return g.splits > 1 ? (size_t)g.splits * M * N * sizeof(float) : 0;
 }
 
-hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
-  const GemmPlan g = gemm_plan(a.M, a.N, a.K / BK);
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// The forward product over output columns [n0, n0 + nn) of the layer (rows n0..
+// of the weight), with the given tile size and split.
+hipError_t launch_fwd_cols(const FwdArgs& a, int64_t n0, int64_t nn, int tile, int splits, int steps_per_split,
+                           float* scratch, hipStream_t s) {
+  const int64_t nblk = a.K / BK;
   FwdGemmParams p;
   p.X = a.X;
   p.M = a.M;
-  p.N = a.N;
+  p.N = nn;
   p.K = a.K;
   p.r = (int)a.r;
-  p.codes = a.w.codes;
-  p.c2 = a.w.c2;
-  p.c1 = a.w.c1;
+  p.codes = a.w.codes + n0 * (a.K / 2);
+  p.c2 = a.w.c2 + n0 * nblk;
+  p.c1 = a.w.c1 + n0 * nblk / 256;   // (n0 * nblk is a multiple of 256)
   p.mean = a.w.mean;
   p.H = a.H;
-  p.B = a.B;
-  p.b_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
+  p.B = a.B + n0 * a.r;
+  p.b_vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(p.B) % 16) == 0;
   p.scale = a.scale;
-  p.Y = a.Y;
+  p.Y = a.Y + n0;
+  p.ldy = a.N;
   p.part = scratch;
-  p.splits = g.splits;
-  p.steps_per_split = g.steps_per_split;
+  p.splits = splits;
+  p.steps_per_split = steps_per_split;
   p.tab = nf4_table();
+  const int mtiles = (int)cdiv(a.M, tile), ntiles = (int)cdiv(nn, tile);
+  if (tile == 256)
+    return launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, frag_lds_bytes(256, 256), mtiles, ntiles, splits, p, s);
+  return launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, frag_lds_bytes(128, 128), mtiles, ntiles, splits, p, s);
+}
+
+// Large layers run on 256 x 256 tiles, one workgroup per CU.  When their
+// count leaves the last round of workgroups partly empty, the columns of
+// whole rounds stay on 256 x 256 tiles and the remaining columns (at least
+// a whole 256 block of them) run as a second launch on 128 x 128 tiles, two
+// per CU, whose single round takes a fraction of a 256 round.
+hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
+  const GemmPlan g = gemm_plan(a.M, a.N, a.K / BK);
   hipError_t e;
-  if (g.tile == 256)
-    e = launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, frag_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits,
-                     p, s);
-  else
-    e = launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, frag_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits,
-                     p, s);
-  if (e != hipSuccess || g.splits == 1) return e;
+  if (g.tile == 256 && g.splits == 1) {
+    const int64_t cus = cu_count();
+    const int64_t tiles = (int64_t)g.mtiles * g.ntiles, rounds = tiles / cus;
+    const int64_t nt_main = rounds * cus / g.mtiles;         // 256-wide column tiles of whole rounds
+    const int64_t n_main = nt_main * 256;
+    const int64_t tail_tiles = cdiv(a.M, 128) * cdiv(a.N - n_main, 128);
+    if (tiles % cus != 0 && rounds >= 1 && n_main > 0 && n_main < a.N && tail_tiles <= 2 * cus) {
+      if ((e = launch_fwd_cols(a, 0, n_main, 256, 1, g.steps_per_split, scratch, s)) != hipSuccess) return e;
+      return launch_fwd_cols(a, n_main, a.N - n_main, 128, 1, (int)(a.K / BK), scratch, s);
+    }
+  }
+  if ((e = launch_fwd_cols(a, 0, a.N, g.tile, g.splits, g.steps_per_split, scratch, s)) != hipSuccess) return e;
+  if (g.splits == 1) return e;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.N, 256), 4096)),
                      dim3(256), 0, s, scratch, g.splits, (int64_t)(a.M * a.N), 1.0f, a.Y, (float*)nullptr);
   return hipGetLastError();
