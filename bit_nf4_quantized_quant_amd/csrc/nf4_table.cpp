@@ -90,6 +90,32 @@ const Nf4HiLo& nf4_hilo() {
   return hl;
 }
 
+const Nf4Buckets& nf4_buckets() {
+  static Nf4Buckets b;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const Nf4Table& t = nf4_table();
+    b.ok = 1;
+    for (int q = 0; q <= 32; ++q) {
+      const double lo = q / 16.0 - 1.0, hi = (q + 1) / 16.0 - 1.0;
+      b.thr[q] = INFINITY;
+      b.base[q] = 0;
+      int inside = 0;
+      for (int j = 0; j < 15; ++j) {
+        const double v = t.thr[j];
+        if (v < lo) ++b.base[q];
+        if (v >= lo && v < hi) {
+          b.thr[q] = t.thr[j];
+          ++inside;
+        }
+        if (std::fabs(v - lo) <= std::ldexp(1.0, -20)) b.ok = 0;
+      }
+      if (inside > 1) b.ok = 0;
+    }
+  });
+  return b;
+}
+
 const Nf4Table& nf4_table() {
   static Nf4Table table;
   static std::once_flag once;

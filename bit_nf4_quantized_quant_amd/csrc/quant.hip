@@ -21,14 +21,29 @@ namespace {
 //
 // One thread per float4: 16 consecutive lanes hold one 64-element block.  The
 // block absmax is a 4-step xor-shuffle reduction inside the 16-lane group; the
-// quotient uses IEEE fp32 division and the level index is the count of
-// thresholds at or below it.  Codes leave as one 16-bit store per thread
-// (4 nibbles), i.e. 128 contiguous bytes per wave.
-__global__ void __launch_bounds__(256) nf4_quantize_kernel(const float4* __restrict__ W,
-                                                           uint64_t n_vec4,
+// quotient uses IEEE fp32 division.  Its level index is the count of
+// thresholds at or below it: with kBuckets, one comparison against the single
+// threshold of the quotient's 1/16-wide bucket (a 33-entry table in LDS; the
+// count of the 15 thresholds is what limits the pass otherwise), else all 15
+// comparisons.  Codes leave as one 16-bit store per thread (4 nibbles), i.e.
+// 128 contiguous bytes per wave.
+__device__ __forceinline__ uint32_t nf4_code_bucket(float x, const float2* lut) {
+  int q = (int)__builtin_fmaf(x, 16.0f, 16.0f);   // |x| <= 1: 16 (x + 1), rounded, truncated
+  q = min(max(q, 0), 32);
+  const float2 e = lut[q];
+  return __float_as_uint(e.y) + (x >= e.x ? 1u : 0u);
+}
+
+template <bool kBuckets>
+__global__ void __launch_bounds__(256) nf4_quantize_kernel(const float4* __restrict__ W, uint64_t n_vec4,
                                                            uint16_t* __restrict__ codes,
-                                                           float* __restrict__ absmax,
-                                                           Nf4Table tab) {
+                                                           float* __restrict__ absmax, Nf4Table tab,
+                                                           Nf4Buckets bk) {
+  __shared__ float2 lut[33];
+  if (kBuckets) {
+    if (threadIdx.x < 33) lut[threadIdx.x] = make_float2(bk.thr[threadIdx.x], __uint_as_float(bk.base[threadIdx.x]));
+    __syncthreads();
+  }
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec4; i += stride) {
     const float4 w = W[i];
@@ -39,11 +54,11 @@ __global__ void __launch_bounds__(256) nf4_quantize_kernel(const float4* __restr
     a = fmaxf(a, __shfl_xor(a, 8));
     uint32_t packed;
     if (a > 0.0f) {
-      const uint32_t c0 = nf4_code(w.x / a, tab);
-      const uint32_t c1 = nf4_code(w.y / a, tab);
-      const uint32_t c2 = nf4_code(w.z / a, tab);
-      const uint32_t c3 = nf4_code(w.w / a, tab);
-      packed = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
+      uint32_t c[4];
+      const float x[4] = {w.x / a, w.y / a, w.z / a, w.w / a};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = kBuckets ? nf4_code_bucket(x[e], lut) : nf4_code(x[e], tab);
+      packed = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12);
     } else {
       packed = 0x7777u;  // the zero level
     }
@@ -177,9 +192,10 @@ unsigned grid_for(uint64_t work_items, unsigned per_block, unsigned cap) {
 hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                                hipStream_t s) {
   const uint64_t n_vec4 = (uint64_t)N * (uint64_t)K / 4;
-  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s,
-                     reinterpret_cast<const float4*>(W), n_vec4, reinterpret_cast<uint16_t*>(codes),
-                     absmax, nf4_table());
+  const Nf4Buckets& bk = nf4_buckets();
+  hipLaunchKernelGGL(bk.ok ? nf4_quantize_kernel<true> : nf4_quantize_kernel<false>,
+                     dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s, reinterpret_cast<const float4*>(W),
+                     n_vec4, reinterpret_cast<uint16_t*>(codes), absmax, nf4_table(), bk);
   return hipGetLastError();
 }
 

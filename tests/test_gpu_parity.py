@@ -96,6 +96,34 @@ def test_quantize_constant_constants_and_zero_weight():
     check_quantized(gpu_quantize(Z), oracle.quantize_layer(Z))
 
 
+def test_quantize_quotients_at_midpoints_and_bucket_edges():
+    """Quotients exactly at, and up to 3 fp32 ulps around, every midpoint of
+    adjacent levels and every multiple of 1/16 in [-1, 1] (the edges of the
+    kernel's threshold buckets): blocks whose absmax is exactly 1, so each
+    quotient is the weight itself; codes bit-exact with the oracle."""
+    say("[quantize] quotients at midpoints and bucket edges")
+    L = oracle.nf4_levels_f32().astype(np.float64)
+    centres = list((L[:-1] + L[1:]) / 2) + [q / 16 - 1 for q in range(33)]
+    probes = []
+    for c in centres:
+        up = dn = np.float32(c)
+        probes.append(up)
+        for _ in range(3):
+            up = np.nextafter(up, np.float32(2))
+            dn = np.nextafter(dn, np.float32(-2))
+            probes += [up, dn]
+    probes = np.array([v for v in probes if -1 <= v <= 1], np.float32)
+    nblk = -(-len(probes) // 63)
+    nblk += (-nblk) % 4                       # 4 blocks per row
+    flat = np.zeros(nblk * 63, np.float32)
+    flat[:len(probes)] = probes
+    W = np.zeros((nblk, 64), np.float32)
+    W[:, 0] = np.where(np.arange(nblk) % 2 == 0, 1.0, -1.0)   # absmax exactly 1
+    W[:, 1:] = flat.reshape(nblk, 63)
+    W = W.reshape(nblk // 4, 256)
+    check_quantized(gpu_quantize(W), oracle.quantize_layer(W))
+
+
 @pytest.mark.parametrize("N,K", [(256, 256), (5, 192), (33, 1088)])
 def test_dequant_bitexact(N, K):
     W = special_weight(N, K, seed=3 * N + K)
