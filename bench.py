@@ -178,10 +178,15 @@ def bench_quantize(torch, qa, N, K, steps, warmup):
     mean = torch.empty(1, dtype=torch.float32, device="cuda")
     ws = torch.empty(qa.qlora_double_quant_workspace(n_c2), dtype=torch.uint8, device="cuda")
     ms_q = timed_eager(torch, lambda i: qa.qlora_nf4_quantize(W, codes, absmax), steps, warmup)
+    Wb = W.to(torch.bfloat16)
+    ms_qb = timed_eager(torch, lambda i: qa.qlora_nf4_quantize_bf16(Wb, codes, absmax), steps, warmup)
     ms_dq = timed_eager(torch, lambda i: qa.qlora_double_quant(absmax, c2, c1, mean, ws), steps, warmup)
     qbytes = N * K * 4 + N * K // 2 + 4 * n_c2
+    qbytes_b = N * K * 2 + N * K // 2 + 4 * n_c2
     return {"N": N, "K": K, "quantize_ms": ms_q, "quantize_GBps": qbytes / ms_q / 1e6,
-            "quantize_hbm_frac": qbytes / ms_q / 1e6 / HBM_PEAK_GBS, "double_quant_ms": ms_dq,
+            "quantize_hbm_frac": qbytes / ms_q / 1e6 / HBM_PEAK_GBS,
+            "quantize_bf16_ms": ms_qb, "quantize_bf16_GBps": qbytes_b / ms_qb / 1e6,
+            "quantize_bf16_hbm_frac": qbytes_b / ms_qb / 1e6 / HBM_PEAK_GBS, "double_quant_ms": ms_dq,
             "double_quant_GBps": (5 * n_c2 + 4 * n_c1) / ms_dq / 1e6}
 
 
@@ -366,7 +371,8 @@ def main():
         log(f"[bench] 65B layer bwd M=4096: {res['ms']:.3f} ms, {res['TFLOPs']:.0f} TFLOP/s")
         res = bench_quantize(torch, qa, Nl, Kl, 5, 1)
         extra["quantize_22016x8192"] = res
-        log(f"[bench] quantize: {res['quantize_GBps']:.0f} GB/s, double quant {res['double_quant_ms'] * 1e3:.1f} us")
+        log(f"[bench] quantize: {res['quantize_GBps']:.0f} GB/s (bf16 input {res['quantize_bf16_GBps']:.0f} GB/s), "
+            f"double quant {res['double_quant_ms'] * 1e3:.1f} us")
         torch.cuda.empty_cache()
         res = bench_decoder(torch, qa, 20)
         extra["decoder_7b_224_linears"] = res

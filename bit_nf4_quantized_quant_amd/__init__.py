@@ -14,7 +14,7 @@ from . import _lib
 from ._lib import (QLoraError, lib, qlora_double_quant, qlora_double_quant_workspace,  # noqa: F401
                    qlora_linear_bwd, qlora_linear_bwd_workspace, qlora_linear_fwd,
                    qlora_linear_fwd_workspace, qlora_nf4_dequant, qlora_nf4_levels,
-                   qlora_nf4_quantize, qlora_nf4_sizes)
+                   qlora_nf4_quantize, qlora_nf4_quantize_bf16, qlora_nf4_sizes)
 
 
 @dataclasses.dataclass
@@ -30,7 +30,7 @@ class QuantizedWeight:
 
 
 def quantize(W, stream=None) -> QuantizedWeight:
-    """NF4-quantize an fp32 [N, K] device tensor and double-quantize its constants."""
+    """NF4-quantize an fp32 or bf16 [N, K] device tensor and double-quantize its constants."""
     import torch
     N, K = W.shape
     code_bytes, n_c2, n_c1 = qlora_nf4_sizes(N, K)
@@ -40,7 +40,10 @@ def quantize(W, stream=None) -> QuantizedWeight:
     c2 = torch.empty(n_c2, dtype=torch.uint8, device=dev)
     c1 = torch.empty(max(n_c1, 1), dtype=torch.float32, device=dev)
     mean = torch.zeros(1, dtype=torch.float32, device=dev)
-    qlora_nf4_quantize(W, codes, absmax, stream)
+    if W.dtype == torch.bfloat16:
+        qlora_nf4_quantize_bf16(W, codes, absmax, stream)
+    else:
+        qlora_nf4_quantize(W, codes, absmax, stream)
     ws = torch.empty(max(qlora_double_quant_workspace(n_c2), 8), dtype=torch.uint8, device=dev)
     qlora_double_quant(absmax, c2, c1, mean, ws, stream)
     return QuantizedWeight(N, K, codes, absmax, c2, c1, mean)

@@ -27,6 +27,7 @@ SIGNATURES = {
     "qlora_nf4_sizes": (ctypes.c_int, [_i64, _i64, _p, _p, _p]),
     "qlora_nf4_levels": (ctypes.c_int, [_p]),
     "qlora_nf4_quantize": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "qlora_nf4_quantize_bf16": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
     "qlora_double_quant_workspace": (_sz, [_i64]),
     "qlora_double_quant": (ctypes.c_int, [_p, _i64, _p, _p, _p, _p, _sz, _p]),
     "qlora_nf4_dequant": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _p]),
@@ -109,6 +110,14 @@ def qlora_nf4_quantize(W, codes, absmax, stream=None):
     N, K = W.shape
     _check(lib().qlora_nf4_quantize(_ptr(W), N, K, _ptr(codes), _ptr(absmax), _stream(stream)),
            "qlora_nf4_quantize")
+
+
+def qlora_nf4_quantize_bf16(W, codes, absmax, stream=None):
+    """W: a bf16 (or int16 bit-pattern) [N, K] device tensor."""
+    _need_cuda(W, codes, absmax)
+    N, K = W.shape
+    _check(lib().qlora_nf4_quantize_bf16(_ptr(W), N, K, _ptr(codes), _ptr(absmax), _stream(stream)),
+           "qlora_nf4_quantize_bf16")
 
 
 def qlora_double_quant_workspace(n_c2: int) -> int:

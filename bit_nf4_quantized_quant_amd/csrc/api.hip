@@ -110,6 +110,15 @@ int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, flo
   return status_of(launch_nf4_quantize(W, N, K, codes, absmax, (hipStream_t)stream));
 }
 
+int qlora_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax, void* stream) {
+  int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
+  if (st) return st;
+  if (N * K == 0) return QLORA_OK;
+  if (!W || !codes || !absmax) return QLORA_EINVAL;
+  if (!aligned(W, 8) || !aligned(codes, 16) || !aligned(absmax, 4)) return QLORA_EINVAL;
+  return status_of(launch_nf4_quantize_bf16(W, N, K, codes, absmax, (hipStream_t)stream));
+}
+
 size_t qlora_double_quant_workspace(int64_t n_c2) {
   (void)n_c2;
   return double_quant_workspace_bytes();

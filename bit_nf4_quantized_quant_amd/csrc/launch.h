@@ -10,6 +10,8 @@ namespace qlora {
 
 hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                                hipStream_t s);
+hipError_t launch_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                                    hipStream_t s);
 size_t double_quant_workspace_bytes();
 hipError_t launch_double_quant(const float* absmax, int64_t n, uint8_t* c2, float* c1, float* mean,
                                void* workspace, hipStream_t s);

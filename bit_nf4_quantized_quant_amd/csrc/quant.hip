@@ -19,7 +19,10 @@ namespace {
 
 // ------------------------------------------------------------------ quantize
 //
-// One thread per float4: 16 consecutive lanes hold one 64-element block.  The
+// One thread per 4 weights: 16 consecutive lanes hold one 64-element block.
+// The weights are fp32, or bf16 (minnong511 "quantization", the QLoRA
+// pipeline: a base model in FP16/BF16 is quantized to 4 bits), widened
+// exactly to fp32 first, so bf16 input gives the codes of its fp32 values.  The
 // block absmax is a 4-step xor-shuffle reduction inside the 16-lane group; the
 // quotient uses IEEE fp32 division.  Its level index is the count of
 // thresholds at or below it: with kBuckets, one comparison against the single
@@ -34,8 +37,9 @@ __device__ __forceinline__ uint32_t nf4_code_bucket(float x, const float2* lut) 
   return __float_as_uint(e.y) + (x >= e.x ? 1u : 0u);
 }
 
-template <bool kBuckets>
-__global__ void __launch_bounds__(256) nf4_quantize_kernel(const float4* __restrict__ W, uint64_t n_vec4,
+// kBf16: the weights come as bf16 (4 per 8-byte load), widened exactly to fp32.
+template <bool kBuckets, bool kBf16>
+__global__ void __launch_bounds__(256) nf4_quantize_kernel(const void* __restrict__ Wv, uint64_t n_vec4,
                                                            uint16_t* __restrict__ codes,
                                                            float* __restrict__ absmax, Nf4Table tab,
                                                            Nf4Buckets bk) {
@@ -46,7 +50,14 @@ __global__ void __launch_bounds__(256) nf4_quantize_kernel(const float4* __restr
   }
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec4; i += stride) {
-    const float4 w = W[i];
+    float4 w;
+    if constexpr (kBf16) {
+      const uint2 b = reinterpret_cast<const uint2*>(Wv)[i];
+      w = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u), __uint_as_float(b.y << 16),
+                      __uint_as_float(b.y & 0xFFFF0000u));
+    } else {
+      w = reinterpret_cast<const float4*>(Wv)[i];
+    }
     float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
     a = fmaxf(a, __shfl_xor(a, 1));
     a = fmaxf(a, __shfl_xor(a, 2));
@@ -193,9 +204,19 @@ hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* co
                                hipStream_t s) {
   const uint64_t n_vec4 = (uint64_t)N * (uint64_t)K / 4;
   const Nf4Buckets& bk = nf4_buckets();
-  hipLaunchKernelGGL(bk.ok ? nf4_quantize_kernel<true> : nf4_quantize_kernel<false>,
-                     dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s, reinterpret_cast<const float4*>(W),
-                     n_vec4, reinterpret_cast<uint16_t*>(codes), absmax, nf4_table(), bk);
+  hipLaunchKernelGGL((bk.ok ? nf4_quantize_kernel<true, false> : nf4_quantize_kernel<false, false>),
+                     dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s, static_cast<const void*>(W), n_vec4,
+                     reinterpret_cast<uint16_t*>(codes), absmax, nf4_table(), bk);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                                    hipStream_t s) {
+  const uint64_t n_vec4 = (uint64_t)N * (uint64_t)K / 4;
+  const Nf4Buckets& bk = nf4_buckets();
+  hipLaunchKernelGGL((bk.ok ? nf4_quantize_kernel<true, true> : nf4_quantize_kernel<false, true>),
+                     dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s, static_cast<const void*>(W), n_vec4,
+                     reinterpret_cast<uint16_t*>(codes), absmax, nf4_table(), bk);
   return hipGetLastError();
 }
 

@@ -95,6 +95,20 @@ int qlora_nf4_levels(float* levels16);
 int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                        void* stream);
 
+/*
+ * The same quantization of bf16 weights (minnong511 "quantization", the QLoRA
+ * pipeline: the base model's FP16/BF16 weights are what gets quantized to 4
+ * bits).  Each bf16 value is widened exactly to fp32 and quantized as in
+ * qlora_nf4_quantize, so the codes and absmax equal those of the widened
+ * fp32 weights bit for bit.
+ *   W      in   bf16 [N,K]      weights as uint16 bit patterns (8-B aligned)
+ *   codes  out  uint8 [N,K/2]   packed codes (16-B aligned)
+ *   absmax out  fp32 [N*K/64]   max |w| of each 64-element block
+ * Same shapes, status codes and stream behaviour as qlora_nf4_quantize.
+ */
+int qlora_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                            void* stream);
+
 /* Workspace bytes needed by qlora_double_quant for n_c2 constants. */
 size_t qlora_double_quant_workspace(int64_t n_c2);
 

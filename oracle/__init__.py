@@ -9,4 +9,5 @@ from .qlora_oracle import (nf4_levels_f64, nf4_levels_f32, uniform4_levels_f32, 
                            blockwise_absmax, e4m3_value, e4m3_encode, round_rational_to_f32,
                            exact_sum_f32, mean_f32, double_quant, dequant_constants,
                            bf16_round, bf16_to_f64, dequant_weight, lora_scale, linear_fwd, linear_fwd_f64, linear_bwd_f64,
-                           linear_bwd, storage_bits_per_param, quantize_layer)
+                           linear_bwd, storage_bits_per_param, quantize_layer,
+                           quantize_layer_bf16)

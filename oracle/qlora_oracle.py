@@ -380,3 +380,13 @@ def quantize_layer(W: np.ndarray):
     codes, absmax = nf4_quantize(W)
     c2, c1, mu = double_quant(absmax)
     return {"codes": codes, "absmax": absmax, "c2": c2, "c1": c1, "mu": mu}
+
+
+def quantize_layer_bf16(W_bits: np.ndarray):
+    """Quantization of a bf16 weight (uint16 bit patterns): minnong511
+    "quantization", the QLoRA pipeline, quantizes the base model's FP16/BF16
+    weights to 4 bits.  A bf16 number is an fp32 number with the low 16 bits
+    zero, so it widens exactly and is then quantized as an fp32 weight."""
+    bits = np.asarray(W_bits, dtype=np.uint16)
+    W = (bits.astype(np.uint32) << 16).view(F32)
+    return quantize_layer(W)

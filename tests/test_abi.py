@@ -31,7 +31,7 @@ def _declared():
 
 def test_header_declarations_are_exported():
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 12
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -71,6 +71,17 @@ def test_quantize_validation():
     # empty problems are accepted and queue nothing
     assert L.qlora_nf4_quantize(None, 0, 64, None, None, None) == _lib.QLORA_OK
     assert L.qlora_nf4_quantize(None, 8, 0, None, None, None) == _lib.QLORA_OK
+
+
+def test_quantize_bf16_validation():
+    L = _lib.lib()
+    assert L.qlora_nf4_quantize_bf16(None, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(A16, 4, 64, None, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(A16 + 4, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL   # W: 8-B aligned
+    assert L.qlora_nf4_quantize_bf16(A16, 4, 64, MIS, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(A16, 4, 96, A16, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_nf4_quantize_bf16(A16, -4, 64, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(None, 0, 64, None, None, None) == _lib.QLORA_OK
 
 
 def test_double_quant_validation():

@@ -96,6 +96,21 @@ def test_quantize_constant_constants_and_zero_weight():
     check_quantized(gpu_quantize(Z), oracle.quantize_layer(Z))
 
 
+@pytest.mark.parametrize("N,K", [(256, 256), (5, 192), (300, 832)])
+def test_quantize_bf16_weights_bitexact(N, K):
+    """bf16 base weights (normal ~0.02 rounded to bf16, an all-zero block and
+    a block of subnormals): codes and every constant bit-exact with the
+    oracle's quantization of the widened values."""
+    say(f"[quantize bf16] N={N} K={K}")
+    bits = oracle.bf16_round(special_weight(N, K, seed=3 * N + K))
+    bits[0, :64] = 0
+    if N > 1:
+        bits[1, :64] = np.arange(1, 65, dtype=np.uint16)     # subnormal bf16 values
+    ref = oracle.quantize_layer_bf16(bits)
+    Wd = torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    check_quantized(qa.quantize(Wd), ref)
+
+
 def test_quantize_quotients_at_midpoints_and_bucket_edges():
     """Quotients exactly at, and up to 3 fp32 ulps around, every midpoint of
     adjacent levels and every multiple of 1/16 in [-1, 1] (the edges of the

@@ -520,3 +520,24 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with pytest.raises(AssertionError):
         test_quantize_decision_boundaries()
     monkeypatch.setattr(qo, "_nearest_level", real_near)
+
+
+def test_bf16_weight_quantization_is_the_widened_fp32_quantization():
+    """A bf16 weight quantizes as the fp32 number it widens to: known bit
+    patterns decode to their values (1, -1, 0.5, the smallest subnormal, -0),
+    and on random weights the result equals quantize_layer of the widened
+    values computed through fp64."""
+    import oracle
+    probe = np.array([0x3F80, 0xBF80, 0x3F00, 0x0001, 0x8000] + [0] * 59, np.uint16).reshape(1, 64)
+    q = oracle.quantize_layer_bf16(probe)
+    assert q["absmax"][0] == np.float32(1.0)
+    codes = oracle.unpack_nibbles(q["codes"]).reshape(-1)
+    assert list(codes[:5]) == [15, 0, int(np.argmin(np.abs(oracle.nf4_levels_f32() - 0.5))), 7, 7]
+    rng = np.random.default_rng(11)
+    W = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    bits = oracle.bf16_round(W)
+    widened = oracle.bf16_to_f64(bits).astype(np.float32)
+    a, b = oracle.quantize_layer_bf16(bits), oracle.quantize_layer(widened)
+    for k in ("codes", "absmax", "c2", "c1"):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+    assert np.float32(a["mu"]).tobytes() == np.float32(b["mu"]).tobytes()
