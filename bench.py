@@ -35,6 +35,7 @@ METRIC = "QLoRA linear fwd: HBM GB/s at M=1, TFLOP/s at M=4096 (% of peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, public spec
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, public spec
 MALL_BYTES = 256 << 20
+FP64_PEAK_TFLOPS = 78.6   # MI355X fp64 vector peak
 
 
 def log(*a):
@@ -188,6 +189,18 @@ def bench_quantize(torch, qa, N, K, steps, warmup):
             "quantize_bf16_ms": ms_qb, "quantize_bf16_GBps": qbytes_b / ms_qb / 1e6,
             "quantize_bf16_hbm_frac": qbytes_b / ms_qb / 1e6 / HBM_PEAK_GBS, "double_quant_ms": ms_dq,
             "double_quant_GBps": (5 * n_c2 + 4 * n_c1) / ms_dq / 1e6}
+
+
+def bench_merge(torch, qa, N, K, r, steps, warmup):
+    """Merge W_deq + s B A into a bf16 weight: fp64 multiply-adds, r per weight."""
+    sets = make_layer_gpu(torch, qa, N, K, r, 1, 7)
+    q, A, B = sets[0]
+    out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    ms = timed_eager(torch, lambda i: qa.qlora_merge(q.codes, q.c2, q.c1, q.mean, N, K, A, B, 16.0, out),
+                     steps, warmup)
+    fl = 2 * N * K * r
+    return {"N": N, "K": K, "r": r, "ms": ms, "fp64_TFLOPs": fl / ms / 1e9,
+            "fp64_frac": fl / ms / 1e9 / FP64_PEAK_TFLOPS, "GBps": (N * K * 2.5 + N * K / 64) / ms / 1e6}
 
 
 def bench_decoder(torch, qa, reps, seed=5):
@@ -373,6 +386,9 @@ def main():
         extra["quantize_22016x8192"] = res
         log(f"[bench] quantize: {res['quantize_GBps']:.0f} GB/s (bf16 input {res['quantize_bf16_GBps']:.0f} GB/s), "
             f"double quant {res['double_quant_ms'] * 1e3:.1f} us")
+        res = bench_merge(torch, qa, 4096, 4096, 64, 20, 3)
+        extra["merge_4096x4096_r64"] = res
+        log(f"[bench] merge 4096x4096 r=64: {res['ms'] * 1e3:.1f} us, {res['fp64_TFLOPs']:.1f} fp64 TFLOP/s")
         torch.cuda.empty_cache()
         res = bench_decoder(torch, qa, 20)
         extra["decoder_7b_224_linears"] = res

@@ -13,7 +13,7 @@ import dataclasses
 from . import _lib
 from ._lib import (QLoraError, lib, qlora_double_quant, qlora_double_quant_workspace,  # noqa: F401
                    qlora_linear_bwd, qlora_linear_bwd_workspace, qlora_linear_fwd,
-                   qlora_linear_fwd_workspace, qlora_nf4_dequant, qlora_nf4_levels,
+                   qlora_linear_fwd_workspace, qlora_merge, qlora_nf4_dequant, qlora_nf4_levels,
                    qlora_nf4_quantize, qlora_nf4_quantize_bf16, qlora_nf4_sizes)
 
 
@@ -54,6 +54,14 @@ def dequantize(q: QuantizedWeight, stream=None):
     import torch
     out = torch.empty((q.N, q.K), dtype=torch.bfloat16, device=q.codes.device)
     qlora_nf4_dequant(q.codes, q.c2, q.c1, q.mean, q.N, q.K, out, stream)
+    return out
+
+
+def merge(q: QuantizedWeight, A, B, alpha: float, stream=None):
+    """The merged bf16 weight W_deq + (alpha / r) B A, [N, K]."""
+    import torch
+    out = torch.empty((q.N, q.K), dtype=torch.bfloat16, device=q.codes.device)
+    qlora_merge(q.codes, q.c2, q.c1, q.mean, q.N, q.K, A, B, alpha, out, stream)
     return out
 
 

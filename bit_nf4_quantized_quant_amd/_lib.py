@@ -31,6 +31,7 @@ SIGNATURES = {
     "qlora_double_quant_workspace": (_sz, [_i64]),
     "qlora_double_quant": (ctypes.c_int, [_p, _i64, _p, _p, _p, _p, _sz, _p]),
     "qlora_nf4_dequant": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _p]),
+    "qlora_merge": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _p, _i64, _f, _p, _p]),
     "qlora_linear_fwd_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "qlora_linear_fwd": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _f, _p, _p,
                                         _p, _sz, _p]),
@@ -135,6 +136,14 @@ def qlora_nf4_dequant(codes, c2, c1, mean, N: int, K: int, W_bf16, stream=None):
     _need_cuda(codes, c2, c1, mean, W_bf16)
     _check(lib().qlora_nf4_dequant(_ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), N, K, _ptr(W_bf16),
                                    _stream(stream)), "qlora_nf4_dequant")
+
+
+def qlora_merge(codes, c2, c1, mean, N: int, K: int, A, B, alpha: float, W_out, stream=None):
+    """A [r, K], B [N, r] bf16 device tensors (None for r = 0); W_out bf16 [N, K]."""
+    r = 0 if A is None else A.shape[0]
+    _need_cuda(codes, c2, c1, mean, A, B, W_out)
+    _check(lib().qlora_merge(_ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), N, K, _ptr(A), _ptr(B), r,
+                             float(alpha), _ptr(W_out), _stream(stream)), "qlora_merge")
 
 
 def qlora_linear_fwd_workspace(M: int, N: int, K: int, r: int) -> int:

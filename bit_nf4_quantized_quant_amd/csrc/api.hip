@@ -145,6 +145,20 @@ int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, 
   return status_of(launch_nf4_dequant(codes, c2, c1, mean, N, K, W_bf16, (hipStream_t)stream));
 }
 
+int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N, int64_t K,
+                const uint16_t* A, const uint16_t* B, int64_t r, float alpha, uint16_t* W_out, void* stream) {
+  int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
+  if (st) return st;
+  if (r < 0) return QLORA_EINVAL;
+  if (r > 128) return QLORA_ESHAPE;
+  if (N * K == 0) return QLORA_OK;
+  if ((st = check_weight(codes, c2, c1, mean))) return st;
+  if (!W_out || !aligned(W_out, 16)) return QLORA_EINVAL;
+  if (r > 0 && (!A || !B || !aligned(A, 2) || !aligned(B, 2))) return QLORA_EINVAL;
+  const float s = r > 0 ? alpha / (float)r : 0.f;
+  return status_of(launch_nf4_merge(codes, c2, c1, mean, N, K, A, B, r, s, W_out, (hipStream_t)stream));
+}
+
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (check_layer(M, N, K, r)) return 0;
   return fwd_ws(M, N, K, r);

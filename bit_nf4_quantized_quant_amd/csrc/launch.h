@@ -17,6 +17,9 @@ hipError_t launch_double_quant(const float* absmax, int64_t n, uint8_t* c2, floa
                                void* workspace, hipStream_t s);
 hipError_t launch_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
                               int64_t N, int64_t K, uint16_t* out, hipStream_t s);
+hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
+                            int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* out,
+                            hipStream_t st);
 
 // The quantized weight as the matrix kernels see it.
 struct Nf4Weight {

@@ -192,6 +192,103 @@ __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint4* __restric
   }
 }
 
+// ------------------------------------------------------------------ merge
+//
+// W' = bf16( W_deq + s B A ) for the whole weight, in fp64: per output, the
+// products B[n][j] A[j][k] (exact: two bf16 numbers) summed over j in
+// ascending order by fused multiply-adds (one rounding per addition), times
+// s (one rounding), plus W_deq (one rounding), then rounded to bf16 once.
+// Bound by the fp64 multiply-adds (r per weight).  A workgroup takes 64
+// columns and 256 rows (two chunks of 128); thread (row group, column group)
+// holds 4 rows x 8 columns of sums.  A's 64 columns and the chunk's B rows sit
+// in LDS as fp32 (exact for bf16); B rows are padded to 129 so that the 32
+// row groups of one j fall on distinct banks.
+constexpr int kMgCols = 64, kMgRows = 128, kMgChunks = 2, kMgMaxR = 128, kMgPitch = kMgMaxR + 1;
+
+// fp64 -> bf16, rounded to nearest even in effect: the fp64 value is first
+// rounded to fp32 by round-to-odd (truncate, then set the last bit if
+// anything was dropped), which keeps enough information for the second
+// rounding (24 >= 8 + 2 bits) to give the same result as one rounding.
+__device__ __forceinline__ uint32_t f64_to_bf16(double u) {
+  const float f = __double2float_rn(u);
+  uint32_t b = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != u) {
+    if (fabs(back) > fabs(u)) b -= 1u;   // one fp32 step toward zero (|f| > 0 here)
+    b |= 1u;
+  }
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__global__ void __launch_bounds__(256) nf4_merge_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ c2,
+                                                        const float* __restrict__ c1,
+                                                        const float* __restrict__ mean, int64_t N, int64_t K,
+                                                        const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B, int r, float s,
+                                                        uint16_t* __restrict__ out, Nf4Table tab) {
+  __shared__ float lut[16];
+  __shared__ __attribute__((aligned(16))) float at[kMgMaxR * kMgCols];     // A[j][k0 ..]
+  __shared__ float bt[kMgRows * kMgPitch];                                  // B[n][j] of the chunk
+  const int64_t k0 = (int64_t)blockIdx.x * kMgCols;
+  const int64_t nbase = (int64_t)blockIdx.y * (kMgRows * kMgChunks);
+  if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
+  for (int i = threadIdx.x; i < r * kMgCols; i += 256)
+    at[i] = __uint_as_float((uint32_t)A[(int64_t)(i / kMgCols) * K + k0 + (i % kMgCols)] << 16);
+  const float mu = mean[0];
+  const double s64 = (double)s;
+  const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  const int64_t k = k0 + 8 * cg;
+  for (int chunk = 0; chunk < kMgChunks; ++chunk) {
+    const int64_t n0 = nbase + (int64_t)chunk * kMgRows;
+    if (n0 >= N) break;
+    __syncthreads();   // (A and the level table; the previous chunk's B rows are no longer read)
+    for (int i = threadIdx.x; i < kMgRows * r; i += 256) {
+      const int row = i / r, j = i - row * r;
+      bt[row * kMgPitch + j] = n0 + row < N ? __uint_as_float((uint32_t)B[(n0 + row) * r + j] << 16) : 0.f;
+    }
+    __syncthreads();
+    double acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i][e] = 0.0;
+    for (int j = 0; j < r; ++j) {
+      const float4 a0 = *reinterpret_cast<const float4*>(&at[j * kMgCols + 8 * cg]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&at[j * kMgCols + 8 * cg + 4]);
+      const double a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double b = (double)bt[(4 * rg + i) * kMgPitch + j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = __fma_rn(b, a[e], acc[i][e]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n = n0 + 4 * rg + i;
+      if (n >= N) continue;
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + k / 2);
+      const int64_t bi = n * (K / 64) + k / 64;
+      const float chat = dequant_constant(c2[bi], c1[bi >> 8], mu);
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t h[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t code = (word >> (4 * (e + q))) & 15u;
+          const uint32_t wb = pack_bf16x2(__fmul_rn(lut[code], chat), 0.f) & 0xFFFFu;   // W_deq
+          const double w = (double)__uint_as_float(wb << 16);
+          h[q] = f64_to_bf16(__dadd_rn(w, __dmul_rn(s64, acc[i][e + q])));
+        }
+        o[e / 2] = h[0] | (h[1] << 16);
+      }
+      *reinterpret_cast<uint4*>(out + n * K + k) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 unsigned grid_for(uint64_t work_items, unsigned per_block, unsigned cap) {
   uint64_t g = (work_items + per_block - 1) / per_block;
   if (g > cap) g = cap;
@@ -241,6 +338,15 @@ hipError_t launch_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const flo
   hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(n_units, 256, 65536)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(codes), n_units, c2, c1, mean,
                      reinterpret_cast<uint4*>(out), nf4_table());
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
+                            int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* out,
+                            hipStream_t st) {
+  const dim3 grid((unsigned)(K / kMgCols), (unsigned)((N + kMgRows * kMgChunks - 1) / (kMgRows * kMgChunks)));
+  hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), 0, st, codes, c2, c1, mean, N, K, A, B, (int)r, s, out,
+                     nf4_table());
   return hipGetLastError();
 }
 

@@ -137,6 +137,26 @@ int qlora_double_quant(const float* absmax, int64_t n_c2, uint8_t* c2, float* c1
 int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
                       int64_t N, int64_t K, uint16_t* W_bf16, void* stream);
 
+/*
+ * Merge of the adapter into the dequantized base weight (irregular6612
+ * "QLoRA - Efficient Finetuning of Quantized LLMs": after training the
+ * adapter is folded into the bf16 base weight; minnong511 "quantization":
+ * W' = W + (alpha/r) B A).
+ *   codes, c2, c1, mean   the quantized weight [N,K], as for qlora_nf4_dequant
+ *   A      in   bf16 [r,K]
+ *   B      in   bf16 [N,r]
+ *   W_out  out  bf16 [N,K] (16-B aligned):
+ *          W' = bf16( W_deq + s * sum_j B[n][j] A[j][k] ),  s = fp32(alpha / r),
+ *          computed in fp64: the sum over j in ascending order (each product
+ *          exact, one rounding per addition), times s (one rounding), plus
+ *          W_deq (one rounding), one rounding to bf16 (nearest, ties to even).
+ * 0 <= r <= 128 (r = 0 gives W_deq); A and B may be NULL when r = 0.
+ * Same shape rules, status codes and stream behaviour as qlora_nf4_dequant.
+ */
+int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
+                int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float alpha, uint16_t* W_out,
+                void* stream);
+
 /* Workspace bytes needed by qlora_linear_fwd. */
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
 

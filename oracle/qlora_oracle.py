@@ -382,6 +382,38 @@ def quantize_layer(W: np.ndarray):
     return {"codes": codes, "absmax": absmax, "c2": c2, "c1": c1, "mu": mu}
 
 
+def bf16_round_f64(v64: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 in one step (8 significant bits, ties to even,
+    bf16 subnormals below 2^-126); returns the bf16 bits.  Finite inputs below
+    2^128 in magnitude."""
+    v = np.asarray(v64, dtype=F64)
+    _, e = np.frexp(v)
+    ulp_exp = np.maximum(e, -125) - 8
+    q = np.rint(np.ldexp(v, -ulp_exp))          # exact scaling; rint rounds half to even
+    r = np.ldexp(q, ulp_exp)                    # 8 significant bits: exact in fp32
+    return (f32(r).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def merge_weight(Wdeq_bits, A_bits, B_bits, alpha: float, r: int) -> np.ndarray:
+    """The merged weight W_deq + s B A as bf16 bits [N, K] (irregular6612 "QLoRA -
+    Efficient Finetuning of Quantized LLMs": after training the adapter is
+    folded into the dequantized bf16 base weight; minnong511 "quantization":
+    W' = W + (alpha / r) B A).
+
+    Arithmetic, in fp64: the product B A summed over j in ascending order (each
+    product of two bf16 numbers is exact; one rounding per addition), that sum
+    times s (one rounding), plus W_deq (one rounding), then one rounding to
+    bf16."""
+    s = F64(lora_scale(alpha, r))
+    A = bf16_to_f64(A_bits).reshape(r, -1)
+    B = bf16_to_f64(B_bits).reshape(-1, r)
+    W = bf16_to_f64(Wdeq_bits).reshape(B.shape[0], A.shape[1])
+    acc = np.zeros_like(W)
+    for j in range(r):
+        acc = acc + B[:, j:j + 1] * A[j:j + 1, :]
+    return bf16_round_f64(W + s * acc)
+
+
 def quantize_layer_bf16(W_bits: np.ndarray):
     """Quantization of a bf16 weight (uint16 bit patterns): minnong511
     "quantization", the QLoRA pipeline, quantizes the base model's FP16/BF16

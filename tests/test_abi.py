@@ -31,7 +31,7 @@ def _declared():
 
 def test_header_declarations_are_exported():
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -82,6 +82,18 @@ def test_quantize_bf16_validation():
     assert L.qlora_nf4_quantize_bf16(A16, 4, 96, A16, A16, None) == _lib.QLORA_ESHAPE
     assert L.qlora_nf4_quantize_bf16(A16, -4, 64, A16, A16, None) == _lib.QLORA_EINVAL
     assert L.qlora_nf4_quantize_bf16(None, 0, 64, None, None, None) == _lib.QLORA_OK
+
+
+def test_merge_validation():
+    L = _lib.lib()
+    f = ctypes.c_float(16.0)
+    assert L.qlora_merge(None, A16, A16, A16, 4, 64, A16, A16, 8, f, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, None, A16, 8, f, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, A16, A16, 8, f, MIS, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(A16, A16, A16, A16, 4, 100, A16, A16, 8, f, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, A16, A16, 129, f, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, A16, A16, -1, f, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(None, None, None, None, 0, 64, None, None, 8, f, None, None) == _lib.QLORA_OK
 
 
 def test_double_quant_validation():

@@ -139,6 +139,25 @@ def test_quantize_quotients_at_midpoints_and_bucket_edges():
     check_quantized(gpu_quantize(W), oracle.quantize_layer(W))
 
 
+@pytest.mark.parametrize("N,K,r", [(256, 256, 8), (5, 192, 16), (300, 832, 72), (33, 1088, 128), (70, 64, 1),
+                                   (9, 128, 0)])
+def test_merge_bitexact(N, K, r):
+    """Merged weight W_deq + s B A (bf16) bit-exact with the oracle's fp64
+    definition; ragged row counts, r from 0 to 128."""
+    say(f"[merge] N={N} K={K} r={r}")
+    d = synth.make_layer(synth.LayerShape("t", M=1, N=N, K=K, r=max(r, 1), seed_offset=17 * N + K + r))
+    ref = oracle.quantize_layer(d["W"])
+    wd = oracle.dequant_weight(ref["codes"], ref["c2"], ref["c1"], ref["mu"], N, K)
+    alpha = 16.0
+    if r > 0:
+        exp = oracle.merge_weight(wd, d["A"][:r], d["B"][:, :r], alpha, r)
+        A, B = dev_bf16(np.ascontiguousarray(d["A"][:r])), dev_bf16(np.ascontiguousarray(d["B"][:, :r]))
+    else:
+        exp, A, B = wd, None, None
+    got = host_bf16_bits(qa.merge(gpu_quantize(d["W"]), A, B, alpha))
+    assert np.array_equal(got, exp)
+
+
 @pytest.mark.parametrize("N,K", [(256, 256), (5, 192), (33, 1088)])
 def test_dequant_bitexact(N, K):
     W = special_weight(N, K, seed=3 * N + K)

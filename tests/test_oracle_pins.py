@@ -541,3 +541,68 @@ def test_bf16_weight_quantization_is_the_widened_fp32_quantization():
     for k in ("codes", "absmax", "c2", "c1"):
         assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
     assert np.float32(a["mu"]).tobytes() == np.float32(b["mu"]).tobytes()
+
+
+def _bf16_rne_exact(v):
+    """bf16 bits of the rational v rounded to nearest, ties to even (reference
+    by rational arithmetic)."""
+    from fractions import Fraction
+    import math
+    v = Fraction(v)
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # 2^e <= a < 2^(e+1)
+    ulp = Fraction(2) ** (max(e, -126) - 7)
+    q = a / ulp
+    n = math.floor(q)
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = float(n * ulp)
+    return sign | (int(np.float32(val).view(np.uint32)) >> 16)
+
+
+def test_bf16_round_f64_matches_rational_rounding():
+    """One-step fp64 -> bf16 rounding against rational round-to-nearest-even on
+    random values, exact halfway points (both parities), bf16 subnormals and
+    values one fp64 ulp either side of a halfway point."""
+    import oracle
+    rng = np.random.default_rng(5)
+    vals = list(rng.standard_normal(400) * np.exp2(rng.integers(-140, 20, 400)))
+    for bits in (0x3F80, 0x3F81, 0x4049, 0x0003, 0x0080, 0xBF83):
+        lo = float(np.uint32(bits << 16).view(np.float32))
+        hi = float(np.uint32((bits + 1) << 16).view(np.float32))
+        mid = (lo + hi) / 2                       # exact in fp64
+        vals += [mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf), -mid]
+    vals = np.array(vals, dtype=np.float64)
+    got = oracle.bf16_round_f64(vals)
+    exp = np.array([_bf16_rne_exact(v) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, exp)
+
+
+def test_merge_weight_special_cases_and_exact_sums():
+    """Merged weight: B = 0 gives W_deq itself; with s a power of two and
+    operands whose fp64 sums are exact, the result is the rational W + s B A
+    rounded once to bf16."""
+    import oracle
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    N, K, r, alpha = 6, 16, 8, 16.0                # s = 2
+    def bf(x):
+        return oracle.bf16_round(np.asarray(x, np.float32))
+    Wb = bf(rng.uniform(-1, 1, (N, K)) * 0.05)
+    Ab = bf(rng.uniform(0.25, 1, (r, K)) * rng.choice([-1, 1], (r, K)))
+    Bb = bf(rng.uniform(0.25, 1, (N, r)) * rng.choice([-1, 1], (N, r)) * 2.0 ** -6)
+    assert np.array_equal(oracle.merge_weight(Wb, Ab, np.zeros_like(Bb), alpha, r), Wb)
+    got = oracle.merge_weight(Wb, Ab, Bb, alpha, r)
+    W, A, B = (oracle.bf16_to_f64(x) for x in (Wb, Ab, Bb))
+    s = Fraction(oracle.lora_scale(alpha, r))
+    assert s == 2
+    for n in range(N):
+        for k in range(K):
+            v = Fraction(W[n, k]) + s * sum(Fraction(B[n, j]) * Fraction(A[j, k]) for j in range(r))
+            assert got[n, k] == _bf16_rne_exact(v), (n, k)
