@@ -82,6 +82,16 @@ def uniform4_levels_f32() -> np.ndarray:
     return f32(np.linspace(-1.0, 1.0, 16))
 
 
+def fp4_levels_f32() -> np.ndarray:
+    """FP4 as a 16-entry table (a reading: the pages name FP4 -- irregular6612
+    "QLoRA - Efficient Finetuning of Quantized LLMs" and itwiki "QLoRA" compare
+    NF4 with it -- but give no grid): the 4-bit float with 2 exponent and 1
+    mantissa bits, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, divided by 6 so that
+    it spans [-1, 1]; ascending, with its two zeros at codes 7 and 8 (both +0)."""
+    mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]) / 6.0
+    return f32(np.concatenate([-mag[:0:-1], [0.0, 0.0], mag[1:]]))
+
+
 # ---------------------------------------------------------------------------
 # Blockwise quantization (itwiki "QLoRA", NF4 section; minnong511
 # "quantization", block-wise quantization)
@@ -94,14 +104,29 @@ def blockwise_absmax(W: np.ndarray, block: int = BLOCK) -> np.ndarray:
 
 
 def _nearest_level(x32: np.ndarray, levels32: np.ndarray) -> np.ndarray:
-    """argmin_i |x - L_i|, lowest index on an exact tie.
+    """argmin_i |x - L_i| for an ascending level table, lowest index on an exact tie.
 
-    x and L are fp32 values held in fp64.  Near a decision boundary both are of
-    similar magnitude, so the two distances are exact in fp64 and the argmin is
-    the exact one; away from a boundary rounding cannot reorder them.
+    x and L are fp32 values; each distance |x - L| is taken in fp64, rounded
+    once, so it is within 2^-53 (relative) of the exact one.  Where the two
+    nearest distinct levels are that close to equidistant -- an exact midpoint,
+    or a tiny x between two levels of opposite sign -- the choice is made again
+    in exact rational arithmetic.  Equal levels (FP4's two zeros) count once,
+    under their lowest index.
     """
-    d = np.abs(x32.astype(F64)[..., None] - levels32.astype(F64)[None, :])
-    return np.argmin(d, axis=-1).astype(np.uint8)   # numpy returns the first minimum
+    L = np.asarray(levels32, dtype=F32).astype(F64)
+    assert np.all(np.diff(L) >= 0), "levels must be ascending"
+    uniq, first = np.unique(L, return_index=True)
+    x = np.asarray(x32, dtype=F32)
+    d = np.abs(x.astype(F64)[..., None] - uniq)
+    k = np.argmin(d, axis=-1)
+    two = np.partition(d, 1, axis=-1)
+    unsure = two[..., 1] - two[..., 0] <= 2.0 ** -50 * two[..., 1]
+    if np.any(unsure):
+        Lq = [Fraction(float(v)) for v in uniq]
+        for pos in zip(*np.nonzero(unsure)):
+            xv = Fraction(float(x[pos]))
+            k[pos] = min(range(len(Lq)), key=lambda i: (abs(xv - Lq[i]), i))
+    return first[k].astype(np.uint8)
 
 
 def quantize_codes(W: np.ndarray, levels32: np.ndarray | None = None,
@@ -143,11 +168,12 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def nf4_quantize(W: np.ndarray):
-    """W fp32 [N, K] (K % 64 == 0) -> packed codes u8 [N, K/2], absmax fp32 [N*K/64]."""
+def nf4_quantize(W: np.ndarray, levels32: np.ndarray | None = None):
+    """W fp32 [N, K] (K % 64 == 0) -> packed codes u8 [N, K/2], absmax fp32 [N*K/64]
+    (NF4 levels unless another 16-level table is given)."""
     N, K = W.shape
     assert K % BLOCK == 0
-    codes, absmax = quantize_codes(W)
+    codes, absmax = quantize_codes(W, levels32)
     return pack_nibbles(codes).reshape(N, K // 2), absmax
 
 
@@ -375,9 +401,10 @@ def storage_bits_per_param(N: int, K: int) -> float:
     return (8 * n_c2 + 32 * n_c1 + 32) / (N * K)
 
 
-def quantize_layer(W: np.ndarray):
-    """Full quantization of one fp32 weight: packed codes, absmax, c2, c1, mu."""
-    codes, absmax = nf4_quantize(W)
+def quantize_layer(W: np.ndarray, levels32: np.ndarray | None = None):
+    """Full quantization of one fp32 weight: packed codes, absmax, c2, c1, mu
+    (NF4 levels unless another 16-level table is given)."""
+    codes, absmax = nf4_quantize(W, levels32)
     c2, c1, mu = double_quant(absmax)
     return {"codes": codes, "absmax": absmax, "c2": c2, "c1": c1, "mu": mu}
 

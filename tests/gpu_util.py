@@ -5,6 +5,13 @@ Tolerance (written here, used by every floating-point parity check): relative
 Frobenius error <= 5e-3 and max |err| <= 2e-2 * RMS(reference), each output
 checked against its own reference (fp32 accumulation of bf16 operands, bf16
 outputs).
+
+A rank-one output (the LoRA factors' gradients at M = 1 are outer products)
+has a max/RMS ratio of about the product of its two vectors' ratios, often
+above 10, so rounding even the exact result to bf16 (up to half an ulp, 2^-8
+relative) can exceed 2e-2 * RMS by itself.  For those outputs
+(``bf16_floor=True``) the max criterion is taken on the error beyond half a
+bf16 ulp of each reference value; the Frobenius criterion is unchanged.
 """
 
 import numpy as np
@@ -41,7 +48,14 @@ def bf16_f64(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def check_close(got, ref, name):
+def half_ulp_bf16(v):
+    """Half a bf16 ulp at each value: 2^(floor(log2|v|) - 8); 0 at 0."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(v)                       # v = m 2^e, m in [0.5, 1)
+    return np.where(v > 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def check_close(got, ref, name, bf16_floor=False):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -49,7 +63,10 @@ def check_close(got, ref, name):
     ref_norm = np.linalg.norm(ref)
     rms = ref_norm / np.sqrt(ref.size)
     fro = np.linalg.norm(err) / max(ref_norm, 1e-300)
-    mx = np.max(np.abs(err)) / max(rms, 1e-300)
+    aerr = np.abs(err)
+    if bf16_floor:
+        aerr = np.maximum(aerr - half_ulp_bf16(ref), 0.0)
+    mx = (np.max(aerr) if aerr.size else 0.0) / max(rms, 1e-300)
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     assert fro <= FRO_TOL, f"{name}: relative Frobenius error {fro:.3e} > {FRO_TOL}"
     assert mx <= MAX_TOL, f"{name}: max error {mx:.3e} x RMS > {MAX_TOL}"

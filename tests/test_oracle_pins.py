@@ -118,6 +118,28 @@ def test_quantize_matches_exact_bruteforce_random():
     assert np.array_equal(absmax, np.abs(W.reshape(-1, 64)).max(1))
 
 
+@pytest.mark.parametrize("table", ["nf4", "uniform4", "fp4"])
+def test_quantize_other_tables_match_exact_bruteforce(table):
+    """Every table against exact-rational nearest level, with the quotients
+    where fp64 distances alone cannot decide: tiny numbers between two levels of
+    opposite sign (uniform 4-bit has no zero level, so +-1e-40 lie within one
+    fp64 rounding of equidistant from +-1/15), signed zeros, exact midpoints,
+    and FP4's duplicated zero."""
+    L = {"nf4": o.nf4_levels_f32, "uniform4": o.uniform4_levels_f32, "fp4": o.fp4_levels_f32}[table]()
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((4, 128)) * 0.02).astype(np.float32)
+    W[0, 0] = 1.0                                     # block max 1: quotients equal the weights
+    special = [1e-40, -1e-40, 1e-45, -1e-45, 0.0, -0.0, 1e-30, -1e-30]
+    special += [(float(L[j]) + float(L[j + 1])) / 2 for j in range(15) if L[j] != L[j + 1]]
+    special = [np.float32(v) for v in special]
+    W[0, 1:1 + len(special)] = special
+    W[2, :64] = 0.0
+    codes, _ = o.quantize_codes(W, L)
+    assert np.array_equal(codes, _brute_codes(W, L))
+    if table == "uniform4":
+        assert codes[1] == 8 and codes[2] == 7        # +1e-40 -> +1/15, -1e-40 -> -1/15
+
+
 def test_quantize_decision_boundaries():
     """Quotients exactly at, and one or two fp32 ulps around, every midpoint."""
     L = o.nf4_levels_f32()
@@ -606,3 +628,28 @@ def test_merge_weight_special_cases_and_exact_sums():
         for k in range(K):
             v = Fraction(W[n, k]) + s * sum(Fraction(B[n, j]) * Fraction(A[j, k]) for j in range(r))
             assert got[n, k] == _bf16_rne_exact(v), (n, k)
+
+
+# ---------------------------------------------------------------- the parity tolerance itself
+
+def test_check_close_bf16_floor():
+    """Half a bf16 ulp at powers of two and between them; and a rank-one
+    output rounded exactly to bf16 passes only with the floor (its own rounding
+    exceeds 2e-2 * RMS), while a real error of 3e-2 * RMS still fails."""
+    from gpu_util import bf16_f64, check_close, half_ulp_bf16
+    v = np.array([1.0, 1.5, 0.75, -2.0, 0.0, 2.0 ** -130])
+    assert np.array_equal(half_ulp_bf16(v), [2.0 ** -8, 2.0 ** -8, 2.0 ** -9, 2.0 ** -7, 0.0, 2.0 ** -138])
+    rng = np.random.default_rng(5)
+    u, w = rng.standard_normal(300), rng.standard_normal(1024)
+    u[0], w[0] = 4.5, 4.4                       # a large corner element: max/RMS ~ 20
+    ref = np.outer(u, w)
+    got = bf16_f64(o.bf16_round_f64(ref))
+    rms = np.linalg.norm(ref) / np.sqrt(ref.size)
+    assert np.max(np.abs(got - ref)) / rms > 2e-2       # the output's own rounding misses the bar
+    with pytest.raises(AssertionError):
+        check_close(got, ref, "rank one")
+    check_close(got, ref, "rank one", bf16_floor=True)
+    bad = got.copy()
+    bad[1, 1] += 3e-2 * rms + half_ulp_bf16(ref[1, 1])
+    with pytest.raises(AssertionError):
+        check_close(bad, ref, "rank one", bf16_floor=True)
