@@ -27,9 +27,10 @@ class QuantizedWeight:
     c2: "object"      # uint8 [N*K/64]
     c1: "object"      # fp32 [ceil(N*K/16384)]
     mean: "object"    # fp32 [1]
+    table: int = 0    # code table: 0 NF4, 1 uniform 4-bit, 2 FP4
 
 
-def quantize(W, stream=None) -> QuantizedWeight:
+def quantize(W, stream=None, table: int = 0) -> QuantizedWeight:
     """NF4-quantize an fp32 or bf16 [N, K] device tensor and double-quantize its constants."""
     import torch
     N, K = W.shape
@@ -41,19 +42,19 @@ def quantize(W, stream=None) -> QuantizedWeight:
     c1 = torch.empty(max(n_c1, 1), dtype=torch.float32, device=dev)
     mean = torch.zeros(1, dtype=torch.float32, device=dev)
     if W.dtype == torch.bfloat16:
-        qlora_nf4_quantize_bf16(W, codes, absmax, stream)
+        qlora_nf4_quantize_bf16(W, codes, absmax, stream, table)
     else:
-        qlora_nf4_quantize(W, codes, absmax, stream)
+        qlora_nf4_quantize(W, codes, absmax, stream, table)
     ws = torch.empty(max(qlora_double_quant_workspace(n_c2), 8), dtype=torch.uint8, device=dev)
     qlora_double_quant(absmax, c2, c1, mean, ws, stream)
-    return QuantizedWeight(N, K, codes, absmax, c2, c1, mean)
+    return QuantizedWeight(N, K, codes, absmax, c2, c1, mean, table)
 
 
 def dequantize(q: QuantizedWeight, stream=None):
     """bf16 [N, K] weight (returned as int16 bit patterns viewed as bfloat16)."""
     import torch
     out = torch.empty((q.N, q.K), dtype=torch.bfloat16, device=q.codes.device)
-    qlora_nf4_dequant(q.codes, q.c2, q.c1, q.mean, q.N, q.K, out, stream)
+    qlora_nf4_dequant(q.codes, q.c2, q.c1, q.mean, q.N, q.K, out, stream, q.table)
     return out
 
 
@@ -61,7 +62,7 @@ def merge(q: QuantizedWeight, A, B, alpha: float, stream=None):
     """The merged bf16 weight W_deq + (alpha / r) B A, [N, K]."""
     import torch
     out = torch.empty((q.N, q.K), dtype=torch.bfloat16, device=q.codes.device)
-    qlora_merge(q.codes, q.c2, q.c1, q.mean, q.N, q.K, A, B, alpha, out, stream)
+    qlora_merge(q.codes, q.c2, q.c1, q.mean, q.N, q.K, A, B, alpha, out, stream, q.table)
     return out
 
 
@@ -83,7 +84,7 @@ def linear_fwd(X, q: QuantizedWeight, A, B, alpha: float, workspace=None, want_h
     H = torch.empty((M, r), dtype=torch.float32, device=X.device) if want_h and r > 0 else None
     if workspace is None:
         workspace = fwd_workspace(M, q.N, q.K, r, X.device)
-    qlora_linear_fwd(X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, Y, H, workspace, q.N, stream)
+    qlora_linear_fwd(X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, Y, H, workspace, q.N, stream, q.table)
     return Y, H
 
 
@@ -98,5 +99,5 @@ def linear_bwd(dY, X, q: QuantizedWeight, A, B, alpha: float, H=None, want_dx: b
     dA = torch.empty((r, K), dtype=torch.bfloat16, device=X.device) if r > 0 else None
     dB = torch.empty((q.N, r), dtype=torch.bfloat16, device=X.device) if r > 0 else None
     ws = torch.empty(max(qlora_linear_bwd_workspace(M, q.N, K, r), 256), dtype=torch.uint8, device=X.device)
-    qlora_linear_bwd(dY, X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, H, dX, dA, dB, ws, stream)
+    qlora_linear_bwd(dY, X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, H, dX, dA, dB, ws, stream, q.table)
     return dX, dA, dB

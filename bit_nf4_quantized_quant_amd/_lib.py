@@ -18,6 +18,7 @@ QLORA_OK, QLORA_EINVAL, QLORA_ESHAPE, QLORA_EHIP = 0, 1, 2, 3
 
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
+_int = ctypes.c_int
 _p = ctypes.c_void_p
 _f = ctypes.c_float
 
@@ -25,19 +26,19 @@ _f = ctypes.c_float
 SIGNATURES = {
     "qlora_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_nf4_sizes": (ctypes.c_int, [_i64, _i64, _p, _p, _p]),
-    "qlora_nf4_levels": (ctypes.c_int, [_p]),
-    "qlora_nf4_quantize": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
-    "qlora_nf4_quantize_bf16": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "qlora_nf4_levels": (ctypes.c_int, [_int, _p]),
+    "qlora_nf4_quantize": (ctypes.c_int, [_p, _i64, _i64, _int, _p, _p, _p]),
+    "qlora_nf4_quantize_bf16": (ctypes.c_int, [_p, _i64, _i64, _int, _p, _p, _p]),
     "qlora_double_quant_workspace": (_sz, [_i64]),
     "qlora_double_quant": (ctypes.c_int, [_p, _i64, _p, _p, _p, _p, _sz, _p]),
-    "qlora_nf4_dequant": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _p]),
-    "qlora_merge": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _p, _i64, _f, _p, _p]),
+    "qlora_nf4_dequant": (ctypes.c_int, [_p, _p, _p, _p, _int, _i64, _i64, _p, _p]),
+    "qlora_merge": (ctypes.c_int, [_p, _p, _p, _p, _int, _i64, _i64, _p, _p, _i64, _f, _p, _p]),
     "qlora_linear_fwd_workspace": (_sz, [_i64, _i64, _i64, _i64]),
-    "qlora_linear_fwd": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _f, _p, _p,
-                                        _p, _sz, _p]),
+    "qlora_linear_fwd": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _i64, _f, _p,
+                                        _p, _p, _sz, _p]),
     "qlora_linear_bwd_workspace": (_sz, [_i64, _i64, _i64, _i64]),
-    "qlora_linear_bwd": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _f, _p,
-                                        _p, _p, _p, _p, _sz, _p]),
+    "qlora_linear_bwd": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _i64, _f,
+                                        _p, _p, _p, _p, _p, _sz, _p]),
 }
 
 
@@ -100,24 +101,24 @@ def qlora_nf4_sizes(N: int, K: int):
     return cb.value, n2.value, n1.value
 
 
-def qlora_nf4_levels():
+def qlora_nf4_levels(table: int = 0):
     buf = (ctypes.c_float * 16)()
-    _check(lib().qlora_nf4_levels(buf), "qlora_nf4_levels")
+    _check(lib().qlora_nf4_levels(table, buf), "qlora_nf4_levels")
     return list(buf)
 
 
-def qlora_nf4_quantize(W, codes, absmax, stream=None):
+def qlora_nf4_quantize(W, codes, absmax, stream=None, table: int = 0):
     _need_cuda(W, codes, absmax)
     N, K = W.shape
-    _check(lib().qlora_nf4_quantize(_ptr(W), N, K, _ptr(codes), _ptr(absmax), _stream(stream)),
+    _check(lib().qlora_nf4_quantize(_ptr(W), N, K, table, _ptr(codes), _ptr(absmax), _stream(stream)),
            "qlora_nf4_quantize")
 
 
-def qlora_nf4_quantize_bf16(W, codes, absmax, stream=None):
+def qlora_nf4_quantize_bf16(W, codes, absmax, stream=None, table: int = 0):
     """W: a bf16 (or int16 bit-pattern) [N, K] device tensor."""
     _need_cuda(W, codes, absmax)
     N, K = W.shape
-    _check(lib().qlora_nf4_quantize_bf16(_ptr(W), N, K, _ptr(codes), _ptr(absmax), _stream(stream)),
+    _check(lib().qlora_nf4_quantize_bf16(_ptr(W), N, K, table, _ptr(codes), _ptr(absmax), _stream(stream)),
            "qlora_nf4_quantize_bf16")
 
 
@@ -132,17 +133,17 @@ def qlora_double_quant(absmax, c2, c1, mean, workspace, stream=None):
                                     _stream(stream)), "qlora_double_quant")
 
 
-def qlora_nf4_dequant(codes, c2, c1, mean, N: int, K: int, W_bf16, stream=None):
+def qlora_nf4_dequant(codes, c2, c1, mean, N: int, K: int, W_bf16, stream=None, table: int = 0):
     _need_cuda(codes, c2, c1, mean, W_bf16)
-    _check(lib().qlora_nf4_dequant(_ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), N, K, _ptr(W_bf16),
+    _check(lib().qlora_nf4_dequant(_ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), table, N, K, _ptr(W_bf16),
                                    _stream(stream)), "qlora_nf4_dequant")
 
 
-def qlora_merge(codes, c2, c1, mean, N: int, K: int, A, B, alpha: float, W_out, stream=None):
+def qlora_merge(codes, c2, c1, mean, N: int, K: int, A, B, alpha: float, W_out, stream=None, table: int = 0):
     """A [r, K], B [N, r] bf16 device tensors (None for r = 0); W_out bf16 [N, K]."""
     r = 0 if A is None else A.shape[0]
     _need_cuda(codes, c2, c1, mean, A, B, W_out)
-    _check(lib().qlora_merge(_ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), N, K, _ptr(A), _ptr(B), r,
+    _check(lib().qlora_merge(_ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), table, N, K, _ptr(A), _ptr(B), r,
                              float(alpha), _ptr(W_out), _stream(stream)), "qlora_merge")
 
 
@@ -151,11 +152,11 @@ def qlora_linear_fwd_workspace(M: int, N: int, K: int, r: int) -> int:
 
 
 def qlora_linear_fwd(X, codes, c2, c1, mean, A, B, alpha: float, Y, H_out, workspace, N: int,
-                     stream=None):
+                     stream=None, table: int = 0):
     _need_cuda(X, codes, c2, c1, mean, A, B, Y, H_out, workspace)
     M, K = X.shape
     r = 0 if A is None else A.shape[0]
-    _check(lib().qlora_linear_fwd(_ptr(X), M, N, K, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), _ptr(A),
+    _check(lib().qlora_linear_fwd(_ptr(X), M, N, K, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), table, _ptr(A),
                                   _ptr(B), r, float(alpha), _ptr(Y), _ptr(H_out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "qlora_linear_fwd")
@@ -166,12 +167,12 @@ def qlora_linear_bwd_workspace(M: int, N: int, K: int, r: int) -> int:
 
 
 def qlora_linear_bwd(dY, X, codes, c2, c1, mean, A, B, alpha: float, H, dX, dA, dB, workspace,
-                     stream=None):
+                     stream=None, table: int = 0):
     _need_cuda(dY, X, codes, c2, c1, mean, A, B, H, dX, dA, dB, workspace)
     M, K = X.shape
     N = dY.shape[1]
     r = 0 if A is None else A.shape[0]
     _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), M, N, K, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean),
-                                  _ptr(A), _ptr(B), r, float(alpha), _ptr(H), _ptr(dX), _ptr(dA), _ptr(dB),
+                                  table, _ptr(A), _ptr(B), r, float(alpha), _ptr(H), _ptr(dX), _ptr(dA), _ptr(dB),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "qlora_linear_bwd")

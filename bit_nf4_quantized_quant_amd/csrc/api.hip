@@ -47,6 +47,8 @@ int check_layer(int64_t M, int64_t N, int64_t K, int64_t r) {
   return QLORA_OK;
 }
 
+bool table_ok(int table) { return table >= 0 && table < kCodeTables; }
+
 int check_weight(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean) {
   if (!codes || !c2 || !c1 || !mean) return QLORA_EINVAL;
   if (!aligned(codes, 16) || !aligned(c1, 4) || !aligned(mean, 4)) return QLORA_EINVAL;
@@ -95,28 +97,32 @@ int qlora_nf4_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* n_c2, in
   return QLORA_OK;
 }
 
-int qlora_nf4_levels(float* levels16) {
-  if (!levels16) return QLORA_EINVAL;
-  std::memcpy(levels16, nf4_table().level, 16 * sizeof(float));
+int qlora_nf4_levels(int table, float* levels16) {
+  if (!levels16 || !table_ok(table)) return QLORA_EINVAL;
+  std::memcpy(levels16, code_table(table).level, 16 * sizeof(float));
   return QLORA_OK;
 }
 
-int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax, void* stream) {
+int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, int table, uint8_t* codes, float* absmax,
+                       void* stream) {
   int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
   if (st) return st;
+  if (!table_ok(table)) return QLORA_EINVAL;
   if (N * K == 0) return QLORA_OK;
   if (!W || !codes || !absmax) return QLORA_EINVAL;
   if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(absmax, 4)) return QLORA_EINVAL;
-  return status_of(launch_nf4_quantize(W, N, K, codes, absmax, (hipStream_t)stream));
+  return status_of(launch_nf4_quantize(W, N, K, table, codes, absmax, (hipStream_t)stream));
 }
 
-int qlora_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax, void* stream) {
+int qlora_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, int table, uint8_t* codes, float* absmax,
+                            void* stream) {
   int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
   if (st) return st;
+  if (!table_ok(table)) return QLORA_EINVAL;
   if (N * K == 0) return QLORA_OK;
   if (!W || !codes || !absmax) return QLORA_EINVAL;
   if (!aligned(W, 8) || !aligned(codes, 16) || !aligned(absmax, 4)) return QLORA_EINVAL;
-  return status_of(launch_nf4_quantize_bf16(W, N, K, codes, absmax, (hipStream_t)stream));
+  return status_of(launch_nf4_quantize_bf16(W, N, K, table, codes, absmax, (hipStream_t)stream));
 }
 
 size_t qlora_double_quant_workspace(int64_t n_c2) {
@@ -135,20 +141,23 @@ int qlora_double_quant(const float* absmax, int64_t n_c2, uint8_t* c2, float* c1
   return status_of(launch_double_quant(absmax, n_c2, c2, c1, mean, workspace, (hipStream_t)stream));
 }
 
-int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
-                      int64_t K, uint16_t* W_bf16, void* stream) {
+int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table,
+                      int64_t N, int64_t K, uint16_t* W_bf16, void* stream) {
   int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
   if (st) return st;
+  if (!table_ok(table)) return QLORA_EINVAL;
   if (N * K == 0) return QLORA_OK;
   if ((st = check_weight(codes, c2, c1, mean))) return st;
   if (!W_bf16 || !aligned(W_bf16, 16)) return QLORA_EINVAL;
-  return status_of(launch_nf4_dequant(codes, c2, c1, mean, N, K, W_bf16, (hipStream_t)stream));
+  return status_of(launch_nf4_dequant(codes, c2, c1, mean, table, N, K, W_bf16, (hipStream_t)stream));
 }
 
-int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N, int64_t K,
-                const uint16_t* A, const uint16_t* B, int64_t r, float alpha, uint16_t* W_out, void* stream) {
+int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table, int64_t N,
+                int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float alpha, uint16_t* W_out,
+                void* stream) {
   int st = qlora_nf4_sizes(N, K, nullptr, nullptr, nullptr);
   if (st) return st;
+  if (!table_ok(table)) return QLORA_EINVAL;
   if (r < 0) return QLORA_EINVAL;
   if (r > 128) return QLORA_ESHAPE;
   if (N * K == 0) return QLORA_OK;
@@ -156,7 +165,7 @@ int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const 
   if (!W_out || !aligned(W_out, 16)) return QLORA_EINVAL;
   if (r > 0 && (!A || !B || !aligned(A, 2) || !aligned(B, 2))) return QLORA_EINVAL;
   const float s = r > 0 ? alpha / (float)r : 0.f;
-  return status_of(launch_nf4_merge(codes, c2, c1, mean, N, K, A, B, r, s, W_out, (hipStream_t)stream));
+  return status_of(launch_nf4_merge(codes, c2, c1, mean, table, N, K, A, B, r, s, W_out, (hipStream_t)stream));
 }
 
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -165,10 +174,11 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
 }
 
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes, const uint8_t* c2,
-                     const float* c1, const float* mean, const uint16_t* A, const uint16_t* B, int64_t r,
-                     float alpha, uint16_t* Y, float* H_out, void* workspace, size_t workspace_bytes,
+                     const float* c1, const float* mean, int table, const uint16_t* A, const uint16_t* B,
+                     int64_t r, float alpha, uint16_t* Y, float* H_out, void* workspace, size_t workspace_bytes,
                      void* stream) {
   int st = check_layer(M, N, K, r);
+  if (!st && !table_ok(table)) st = QLORA_EINVAL;
   if (st) return st;
   if (K == 0) return QLORA_ESHAPE;
   if (M == 0 || N == 0) return QLORA_OK;
@@ -186,7 +196,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
   a.N = N;
   a.K = K;
   a.r = r;
-  a.w = Nf4Weight{codes, c2, c1, mean};
+  a.w = Nf4Weight{codes, c2, c1, mean, table};
   a.A = A;
   a.B = B;
   a.scale = r > 0 ? alpha / (float)r : 0.f;
@@ -211,10 +221,11 @@ size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
 }
 
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
-                     const uint8_t* c2, const float* c1, const float* mean, const uint16_t* A, const uint16_t* B,
-                     int64_t r, float alpha, const float* H, uint16_t* dX, uint16_t* dA, uint16_t* dB,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     const uint8_t* c2, const float* c1, const float* mean, int table, const uint16_t* A,
+                     const uint16_t* B, int64_t r, float alpha, const float* H, uint16_t* dX, uint16_t* dA,
+                     uint16_t* dB, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_layer(M, N, K, r);
+  if (!st && !table_ok(table)) st = QLORA_EINVAL;
   if (st) return st;
   if (K == 0) return QLORA_ESHAPE;
   if ((st = check_weight(codes, c2, c1, mean))) return st;
@@ -238,7 +249,7 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N
   a.N = N;
   a.K = K;
   a.r = r;
-  a.w = Nf4Weight{codes, c2, c1, mean};
+  a.w = Nf4Weight{codes, c2, c1, mean, table};
   a.A = A;
   a.B = B;
   a.scale = r > 0 ? alpha / (float)r : 0.f;

@@ -347,6 +347,7 @@ __device__ void weight_tile(const DecodeParams& p, int tile, char* lut, uint32_t
     float y = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) y += *spare(lut, kRedOff + w * 256 + o);
+    y *= p.inv_kappa;
     if (n < p.N) p.Y[(size_t)m * p.N + n] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
   }
 }

@@ -66,7 +66,8 @@ struct DecodeParams {
   int n_wtiles;
   int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
   int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
-  uint32_t hi[16]; // bf16(level) per code
+  uint32_t hi[16]; // bf16(kappa * level) per code
+  float inv_kappa; // 1 / kappa: scales the block sums back at the output
 };
 
 // Cross-workgroup data (H partials, counters) moves only through relaxed
@@ -249,7 +250,11 @@ inline DecodeParams decode_params(const FwdArgs& a) {
   p.mean = a.w.mean;
   p.A = a.A;
   p.B = a.B;
-  p.scale = a.scale;
+  // the main product comes out kappa times too large; so does the LoRA term
+  // with scale * kappa, and the sum is multiplied by 1 / kappa at the output
+  const DecodeLevels& dl = decode_levels(a.w.table);
+  p.scale = a.scale * dl.kappa;
+  p.inv_kappa = 1.0f / dl.kappa;
   p.Y = a.Y;
   p.ws = reinterpret_cast<char*>(a.workspace);
   p.Hpart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff);
@@ -258,8 +263,7 @@ inline DecodeParams decode_params(const FwdArgs& a) {
   p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
   p.c2_vec = (a.K % 256 == 0) && (reinterpret_cast<uintptr_t>(a.w.c2) % 4 == 0);
   p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);
-  const Nf4HiLo& hl = nf4_hilo();
-  for (int i = 0; i < 16; ++i) p.hi[i] = hl.word[i] & 0xFFFFu;
+  for (int i = 0; i < 16; ++i) p.hi[i] = dl.bf16[i];
   return p;
 }
 

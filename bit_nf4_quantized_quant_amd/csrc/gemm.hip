@@ -824,12 +824,25 @@ __global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restr
 }
 
 // out[c][r] = bf16(src[r][c]) for an fp32 src [rows][cols] (out row length
-// rows): the LoRA factors' gradients take H and dH with the reduction index m
-// contiguous, as 16-byte vector loads.  16 x 64 tiles through LDS (one
-// workgroup per 16 rows, so a 4096-row source fills the chip); each thread
-// stores pairs of consecutive rows (4 bytes).
+// rows), and, with lo_out, lo_out[c][r] = bf16(src[r][c] - out[c][r]): the
+// pair carries each value to about 2^-17 relative, so the LoRA factors'
+// gradients see H and dH at fp32-like precision through bf16 matrix cores.
+// The reduction index m ends up contiguous, for 16-byte vector loads.  16 x 64
+// tiles through LDS (one workgroup per 16 rows, so a 4096-row source fills
+// the chip); each thread stores pairs of consecutive rows (4 bytes).
+__device__ __forceinline__ void store_pair_t(uint16_t* __restrict__ out, int64_t rows, int64_t r, int64_t c,
+                                             uint32_t v) {
+  if (r + 1 < rows && (rows & 1) == 0)
+    *reinterpret_cast<uint32_t*>(out + c * rows + r) = v;
+  else {
+    out[c * rows + r] = (uint16_t)(v & 0xFFFFu);
+    if (r + 1 < rows) out[c * rows + r + 1] = (uint16_t)(v >> 16);
+  }
+}
+
 __global__ void __launch_bounds__(256) f32_to_bf16_t_kernel(const float* __restrict__ src, int64_t rows,
-                                                            int64_t cols, uint16_t* __restrict__ out) {
+                                                            int64_t cols, uint16_t* __restrict__ out,
+                                                            uint16_t* __restrict__ lo_out) {
   __shared__ float t[16][65];
   const int64_t r0 = (int64_t)blockIdx.x * 16, c0 = (int64_t)blockIdx.y * 64;
   const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
@@ -845,13 +858,32 @@ __global__ void __launch_bounds__(256) f32_to_bf16_t_kernel(const float* __restr
     const int cc = pc + 32 * i;
     const int64_t c = c0 + cc, r = r0 + 2 * pr;
     if (c >= cols || r >= rows) continue;
-    const uint32_t v = pack_bf16x2(t[2 * pr][cc], t[2 * pr + 1][cc]);
-    if (r + 1 < rows && (rows & 1) == 0)
-      *reinterpret_cast<uint32_t*>(out + c * rows + r) = v;
-    else {
-      out[c * rows + r] = (uint16_t)(v & 0xFFFFu);
-      if (r + 1 < rows) out[c * rows + r + 1] = (uint16_t)(v >> 16);
+    const float x0 = t[2 * pr][cc], x1 = t[2 * pr + 1][cc];
+    const uint32_t v = pack_bf16x2(x0, x1);
+    store_pair_t(out, rows, r, c, v);
+    // x - bf16(x) is exact in fp32 (the rounding error of a rounding to 8 bits)
+    if (lo_out) store_pair_t(lo_out, rows, r, c, pack_bf16x2(x0 - bf16_lo(v), x1 - bf16_hi(v)));
+  }
+}
+
+// Gradient of a LoRA factor from a product whose small operand came as hi
+// and lo bf16 halves: part[s] holds the product against [hi; lo], so
+// out[i][j] = bf16(scale * sum_s (part[s][i*pitch + j] + part[s][i*pitch + j + lo_off])).
+__global__ void __launch_bounds__(256) reduce_hilo_kernel(const float* __restrict__ part, int splits,
+                                                          int64_t split_stride, int64_t rows, int64_t cols,
+                                                          int64_t pitch, int64_t lo_off, float scale,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t count = rows * cols;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < count; o += stride) {
+    const int64_t i = o / cols, j = o - i * cols;
+    const float* p = part + i * pitch + j;
+    float hi = 0.f, lo = 0.f;
+    for (int k = 0; k < splits; ++k) {
+      hi += p[(int64_t)k * split_stride];
+      lo += p[(int64_t)k * split_stride + lo_off];
     }
+    out[o] = to_bf16(scale * (hi + lo));
   }
 }
 
@@ -1189,7 +1221,7 @@ hipError_t launch_fwd_cols(const FwdArgs& a, int64_t n0, int64_t nn, int tile, i
   p.part = scratch;
   p.splits = splits;
   p.steps_per_split = steps_per_split;
-  p.tab = nf4_table();
+  p.tab = code_table(a.w.table);
   const int mtiles = (int)cdiv(a.M, tile), ntiles = (int)cdiv(nn, tile);
   if (tile == 256)
     return launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, frag_lds_bytes(256, 256), mtiles, ntiles, splits, p, s);
@@ -1234,15 +1266,15 @@ struct BwdPlan {
 static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   BwdPlan b;
   b.s_dh = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), (N + BK - 1) / BK);
-  b.s_db = pick_splits((int64_t)cdiv(N, 128) * cdiv(r, 64), (M + BK - 1) / BK);
-  b.s_da = pick_splits((int64_t)cdiv(r, 64) * cdiv(K, 128), (M + BK - 1) / BK);
+  b.s_db = pick_splits((int64_t)cdiv(N, 64) * cdiv(2 * r, 128), (M + BK - 1) / BK);
+  b.s_da = pick_splits((int64_t)cdiv(2 * r, 128) * cdiv(K, 64), (M + BK - 1) / BK);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   b.off_H = 0;
   b.off_dH = al((size_t)M * r * 4);
-  b.off_Ht = b.off_dH + al((size_t)M * r * 4);     // bf16 H^T and dH^T [r][M]
-  b.off_dHt = b.off_Ht + al((size_t)M * r * 2);
-  b.off_part = b.off_dHt + al((size_t)M * r * 2);
-  size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * r, (size_t)b.s_da * r * K}) * 4;
+  b.off_Ht = b.off_dH + al((size_t)M * r * 4);     // bf16 hi/lo of H^T and dH^T [2r][M]
+  b.off_dHt = b.off_Ht + al((size_t)M * r * 4);
+  b.off_part = b.off_dHt + al((size_t)M * r * 4);
+  size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * 2 * r, (size_t)b.s_da * 2 * r * K}) * 4;
   part = std::max(part, lora_down_scratch_bytes(M, K, r));
   b.dxt = M >= kDxtMinM && N > 0;
   b.ldt = (N + 63) / 64 * 64;
@@ -1275,7 +1307,7 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     uint16_t* Ht = reinterpret_cast<uint16_t*>(ws + plan.off_Ht);
     uint16_t* dHt = reinterpret_cast<uint16_t*>(ws + plan.off_dHt);
     const dim3 tgrid(cdiv(a.M, 16), cdiv(a.r, 64));
-    if (a.M > 0) hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, H, a.M, a.r, Ht);
+    if (a.M > 0) hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, H, a.M, a.r, Ht, Ht + a.r * a.M);
     // dH = s dY B : rows m, cols j, reduction n
     if (a.M > 0) {
       SRowsBf16<128> la;
@@ -1285,34 +1317,34 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
       if ((e = launch_skinny<128, 64>(la, lb, a.M, a.r, a.N, plan.s_dh, part, s)) != hipSuccess) return e;
       hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.M * a.r, 256)), dim3(256), 0, s, part, plan.s_dh,
                          (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
-      hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, dH, a.M, a.r, dHt);
+      hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, dH, a.M, a.r, dHt, dHt + a.r * a.M);
     }
-    // dB = s dY^T H : rows n, cols j, reduction m
+    // dB = s dY^T H : rows n, cols j, reduction m; H as [hi; lo] (2r columns)
     if (a.N > 0) {
-      SColsBf16<128> la;
+      SColsBf16<64> la;
       la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
-      SRowsBf16<64> lb;
+      SRowsBf16<128> lb;
       lb.src = Ht; lb.ld = a.M; lb.red = (int)a.M; lb.vec = m_vec;
-      if ((e = launch_skinny<128, 64>(la, lb, a.N, a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
-      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, part, plan.s_db,
-                         (int64_t)(a.N * a.r), a.scale, a.dB, (float*)nullptr);
+      if ((e = launch_skinny<64, 128>(la, lb, a.N, 2 * a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(reduce_hilo_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, part, plan.s_db,
+                         (int64_t)(a.N * 2 * a.r), a.N, a.r, 2 * a.r, a.r, a.scale, a.dB);
     }
-    // dA = dH^T X : rows j, cols k, reduction m
+    // dA = dH^T X : rows j, cols k, reduction m; dH^T as [hi; lo] (2r rows)
     {
-      SRowsBf16<64> la;
+      SRowsBf16<128> la;
       la.src = dHt; la.ld = a.M; la.red = (int)a.M; la.vec = m_vec;
-      SColsBf16<128> lb;
+      SColsBf16<64> lb;
       lb.src = a.X; lb.ld = a.K; lb.red = (int)a.M; lb.vec = true;
-      if ((e = launch_skinny<64, 128>(la, lb, a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
-      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.r * a.K, 256)), dim3(256), 0, s, part, plan.s_da,
-                         (int64_t)(a.r * a.K), 1.0f, a.dA, (float*)nullptr);
+      if ((e = launch_skinny<128, 64>(la, lb, 2 * a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(reduce_hilo_kernel, dim3(cdiv(a.r * a.K, 256)), dim3(256), 0, s, part, plan.s_da,
+                         (int64_t)(2 * a.r * a.K), a.r, a.K, a.K, a.r * a.K, 1.0f, a.dA);
     }
   }
   // dX = dY W_deq + dH A
   if (a.dX && a.M > 0 && plan.dxt) {
     uint16_t* wt = reinterpret_cast<uint16_t*>(ws + plan.off_wt);
     hipLaunchKernelGGL(nf4_dequant_t_kernel, dim3((unsigned)((plan.ldt / kDtN) * cdiv(a.K, kDtK))), dim3(256), 0, s,
-                       a.w.codes, a.w.c2, a.w.c1, a.w.mean, a.N, a.K, plan.ldt, wt, nf4_table());
+                       a.w.codes, a.w.c2, a.w.c1, a.w.mean, a.N, a.K, plan.ldt, wt, code_table(a.w.table));
     DxtParams p;
     p.dY = a.dY;
     p.wt = wt;
@@ -1357,7 +1389,7 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     p.part = part;
     p.splits = g.splits;
     p.steps_per_split = g.steps_per_split;
-    p.tab = nf4_table();
+    p.tab = code_table(a.w.table);
     if (g.tile == 256)
       e = launch_tiled(dx_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits,
                        p, s);

@@ -317,7 +317,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
     for (int rr = 0; rr < kGvRowsPerWave; ++rr) v[rr] = acc[rr][m];
     const float t = wave_sum4(v);
     if ((lane & 15) == 0 && row[0] + rt < (uint32_t)p.N) {
-      const float y = t + red[(grp * kGvRowsPerWave + rt) * M + m];
+      const float y = (t + red[(grp * kGvRowsPerWave + rt) * M + m]) * p.inv_kappa;
       p.Y[(size_t)m * p.N + row[0] + rt] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
     }
   }

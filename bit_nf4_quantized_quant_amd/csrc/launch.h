@@ -8,16 +8,18 @@
 
 namespace qlora {
 
-hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+// table: the code table (0 NF4, 1 uniform 4-bit, 2 FP4; checked by the caller)
+hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, int table, uint8_t* codes, float* absmax,
                                hipStream_t s);
-hipError_t launch_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
-                                    hipStream_t s);
+hipError_t launch_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, int table, uint8_t* codes,
+                                    float* absmax, hipStream_t s);
 size_t double_quant_workspace_bytes();
 hipError_t launch_double_quant(const float* absmax, int64_t n, uint8_t* c2, float* c1, float* mean,
                                void* workspace, hipStream_t s);
 hipError_t launch_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
-                              int64_t N, int64_t K, uint16_t* out, hipStream_t s);
-hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
+                              int table, int64_t N, int64_t K, uint16_t* out, hipStream_t s);
+hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table,
+                            int64_t N,
                             int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* out,
                             hipStream_t st);
 
@@ -27,6 +29,7 @@ struct Nf4Weight {
   const uint8_t* c2;     // [N*K/64]
   const float* c1;       // [ceil(N*K/16384)]
   const float* mean;     // [1]
+  int table;             // code table (0 NF4, 1 uniform 4-bit, 2 FP4)
 };
 
 struct FwdArgs {

@@ -44,7 +44,22 @@ float next_f32_above(long double m) {
   return f;
 }
 
-Nf4Table build_table() {
+// Decision thresholds of an ascending level table: code(x) = #{j : x >= thr[j]}
+// picks the nearest level, the lowest code on a tie.  Where two codes share
+// a level (FP4's two zeros) the upper one is never the lowest nearest code, so
+// its boundary coincides with the next one and both are crossed together.
+void set_thresholds(Nf4Table& t) {
+  for (int j = 14; j >= 0; --j) {
+    if (t.level[j] == t.level[j + 1] && j < 14) {
+      t.thr[j] = t.thr[j + 1];
+      continue;
+    }
+    const long double mid = ((long double)t.level[j] + (long double)t.level[j + 1]) / 2.0L;
+    t.thr[j] = next_f32_above(mid);
+  }
+}
+
+Nf4Table build_nf4() {
   long double v[16];
   int k = 0;
   for (int i = 7; i >= 1; --i) v[k++] = -normal_quantile(0.5L + (kOffset - 0.5L) * i / 7.0L);
@@ -54,10 +69,35 @@ Nf4Table build_table() {
   for (int i = 0; i < 16; ++i) mx = std::fmax(mx, std::fabs(v[i]));
   Nf4Table t;
   for (int i = 0; i < 16; ++i) t.level[i] = (float)(v[i] / mx);
-  for (int j = 0; j < 15; ++j) {
-    const long double mid = ((long double)t.level[j] + (long double)t.level[j + 1]) / 2.0L;
-    t.thr[j] = next_f32_above(mid);
+  set_thresholds(t);
+  return t;
+}
+
+// Uniform 4-bit: 16 evenly spaced levels on [-1, 1] (itwiki "QLoRA", NF4
+// section: the comparison grid of the worked example), each the fp32 rounding
+// of -1 + 2 i / 15 as an fp64 number -1 + i * (2 / 15).
+Nf4Table build_uniform4() {
+  Nf4Table t;
+  const double step = 2.0 / 15.0;
+  for (int i = 0; i < 16; ++i) t.level[i] = i == 15 ? 1.0f : (float)(-1.0 + i * step);
+  set_thresholds(t);
+  return t;
+}
+
+// FP4: the 4-bit float with 2 exponent and 1 mantissa bits (magnitudes 0,
+// 0.5, 1, 1.5, 2, 3, 4, 6), scaled by 1/6 to span [-1, 1] like the other
+// tables; its two zeros are codes 7 and 8 (both +0), so code 7 stays the zero
+// level.  The pages name FP4 (irregular6612 "QLoRA - Efficient Finetuning of
+// Quantized LLMs"; itwiki "QLoRA": bitsandbytes' default 4-bit type) but give
+// no grid: this one is a reading.
+Nf4Table build_fp4() {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  Nf4Table t;
+  for (int i = 0; i < 8; ++i) {
+    t.level[7 - i] = i == 0 ? 0.0f : (float)(-mag[i] / 6.0);
+    t.level[8 + i] = (float)(mag[i] / 6.0);
   }
+  set_thresholds(t);
   return t;
 }
 
@@ -76,51 +116,70 @@ float bf16_value(uint16_t b) {
 
 }  // namespace
 
-const Nf4HiLo& nf4_hilo() {
-  static Nf4HiLo hl;
+const Nf4Table& code_table(int type) {
+  static Nf4Table tables[kCodeTables];
   static std::once_flag once;
   std::call_once(once, [] {
-    const Nf4Table& t = nf4_table();
-    for (int i = 0; i < 16; ++i) {
-      const uint16_t hi = bf16_rne(t.level[i]);
-      const uint16_t lo = bf16_rne(t.level[i] - bf16_value(hi));
-      hl.word[i] = (uint32_t)hi | ((uint32_t)lo << 16);
-    }
+    tables[kTableNf4] = build_nf4();
+    tables[kTableUniform4] = build_uniform4();
+    tables[kTableFp4] = build_fp4();
   });
-  return hl;
+  return tables[type];
 }
 
-const Nf4Buckets& nf4_buckets() {
-  static Nf4Buckets b;
+const DecodeLevels& decode_levels(int type) {
+  static DecodeLevels dl[kCodeTables];
   static std::once_flag once;
   std::call_once(once, [] {
-    const Nf4Table& t = nf4_table();
-    b.ok = 1;
-    for (int q = 0; q <= 32; ++q) {
-      const double lo = q / 16.0 - 1.0, hi = (q + 1) / 16.0 - 1.0;
-      b.thr[q] = INFINITY;
-      b.base[q] = 0;
-      int inside = 0;
-      for (int j = 0; j < 15; ++j) {
-        const double v = t.thr[j];
-        if (v < lo) ++b.base[q];
-        if (v >= lo && v < hi) {
-          b.thr[q] = t.thr[j];
-          ++inside;
+    for (int ty = 0; ty < kCodeTables; ++ty) {
+      const Nf4Table& t = code_table(ty);
+      int kappa = 1;
+      for (int k = 1; k <= 64; ++k) {
+        bool exact = true;
+        for (int i = 0; i < 16; ++i) {
+          const double v = (double)k * t.level[i];
+          const double b = bf16_value(bf16_rne((float)v));
+          exact = exact && std::fabs(b - v) <= std::ldexp(std::fabs(v), -20);
         }
-        if (std::fabs(v - lo) <= std::ldexp(1.0, -20)) b.ok = 0;
+        if (exact) {
+          kappa = k;
+          break;
+        }
       }
-      if (inside > 1) b.ok = 0;
+      dl[ty].kappa = (float)kappa;
+      for (int i = 0; i < 16; ++i) dl[ty].bf16[i] = bf16_rne((float)((double)kappa * t.level[i]));
     }
   });
-  return b;
+  return dl[type];
 }
 
-const Nf4Table& nf4_table() {
-  static Nf4Table table;
+const Nf4Buckets& code_buckets(int type) {
+  static Nf4Buckets bk[kCodeTables];
   static std::once_flag once;
-  std::call_once(once, [] { table = build_table(); });
-  return table;
+  std::call_once(once, [] {
+    for (int ty = 0; ty < kCodeTables; ++ty) {
+      const Nf4Table& t = code_table(ty);
+      Nf4Buckets& b = bk[ty];
+      b.ok = 1;
+      for (int q = 0; q <= 32; ++q) {
+        const double lo = q / 16.0 - 1.0, hi = (q + 1) / 16.0 - 1.0;
+        b.thr[q] = INFINITY;
+        b.base[q] = 0;
+        int inside = 0;
+        for (int j = 0; j < 15; ++j) {
+          const double v = t.thr[j];
+          if (v < lo) ++b.base[q];
+          if (v >= lo && v < hi) {
+            b.thr[q] = t.thr[j];
+            ++inside;
+          }
+          if (std::fabs(v - lo) <= std::ldexp(1.0, -20)) b.ok = 0;
+        }
+        if (inside > 1) b.ok = 0;
+      }
+    }
+  });
+  return bk[type];
 }
 
 }  // namespace qlora

@@ -1,6 +1,8 @@
 // The NF4 code table as passed to the kernels (plain data, host and device).
 #pragma once
 
+#include <cstdint>
+
 namespace qlora {
 
 // The 16 NF4 levels (fp32, ascending) and the 15 decision thresholds passed by
@@ -12,8 +14,12 @@ struct Nf4Table {
   float thr[15];
 };
 
-// Host: the library's table, built once from the quantile construction.
-const Nf4Table& nf4_table();
+// The code tables the library knows (the C ABI's QLORA_TABLE_* values).
+constexpr int kTableNf4 = 0, kTableUniform4 = 1, kTableFp4 = 2, kCodeTables = 3;
+
+// Host: table `type` (0 <= type < kCodeTables), built once.  NF4 comes from
+// the quantile construction.
+const Nf4Table& code_table(int type);
 
 // The thresholds by bucket, for a code search with one comparison: bucket q
 // (0..32) is [q/16 - 1, (q+1)/16 - 1); it holds at most one threshold, thr[q]
@@ -29,16 +35,20 @@ struct Nf4Buckets {
   int ok;
 };
 
-const Nf4Buckets& nf4_buckets();
+const Nf4Buckets& code_buckets(int type);
 
-// Each level split into two bf16 numbers, hi = bf16(L) and lo = bf16(L - hi),
-// packed as hi | lo << 16.  hi + lo carries L to about 2^-17 relative, which
-// lets the fused matrix kernels feed bf16 matrix cores with the levels and
-// apply the per-block fp32 scale after the product.
-struct Nf4HiLo {
-  unsigned int word[16];
+// The levels as the decode kernels feed them to bf16 dot products and matrix
+// cores: bf16(kappa * L[i]), with the block sums scaled by 1/kappa at the end.
+// kappa is the smallest integer in 1..64 for which every kappa * L[i] is a
+// bf16 number (to 2^-20 relative) -- 15 for the uniform table, whose levels
+// are odd multiples of 1/15, and 3 for FP4, whose levels are E2M1 values over
+// 6 -- so those tables enter exactly; NF4's quantiles have no such multiple,
+// kappa = 1, and the kernels take bf16(L).
+struct DecodeLevels {
+  uint16_t bf16[16];
+  float kappa;
 };
 
-const Nf4HiLo& nf4_hilo();
+const DecodeLevels& decode_levels(int type);
 
 }  // namespace qlora

@@ -297,23 +297,23 @@ unsigned grid_for(uint64_t work_items, unsigned per_block, unsigned cap) {
 
 }  // namespace
 
-hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, int table, uint8_t* codes, float* absmax,
                                hipStream_t s) {
   const uint64_t n_vec4 = (uint64_t)N * (uint64_t)K / 4;
-  const Nf4Buckets& bk = nf4_buckets();
+  const Nf4Buckets& bk = code_buckets(table);
   hipLaunchKernelGGL((bk.ok ? nf4_quantize_kernel<true, false> : nf4_quantize_kernel<false, false>),
                      dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s, static_cast<const void*>(W), n_vec4,
-                     reinterpret_cast<uint16_t*>(codes), absmax, nf4_table(), bk);
+                     reinterpret_cast<uint16_t*>(codes), absmax, code_table(table), bk);
   return hipGetLastError();
 }
 
-hipError_t launch_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
-                                    hipStream_t s) {
+hipError_t launch_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, int table, uint8_t* codes,
+                                    float* absmax, hipStream_t s) {
   const uint64_t n_vec4 = (uint64_t)N * (uint64_t)K / 4;
-  const Nf4Buckets& bk = nf4_buckets();
+  const Nf4Buckets& bk = code_buckets(table);
   hipLaunchKernelGGL((bk.ok ? nf4_quantize_kernel<true, true> : nf4_quantize_kernel<false, true>),
                      dim3(grid_for(n_vec4, 256, 65536)), dim3(256), 0, s, static_cast<const void*>(W), n_vec4,
-                     reinterpret_cast<uint16_t*>(codes), absmax, nf4_table(), bk);
+                     reinterpret_cast<uint16_t*>(codes), absmax, code_table(table), bk);
   return hipGetLastError();
 }
 
@@ -333,20 +333,20 @@ hipError_t launch_double_quant(const float* absmax, int64_t n, uint8_t* c2, floa
 }
 
 hipError_t launch_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
-                              int64_t N, int64_t K, uint16_t* out, hipStream_t s) {
+                              int table, int64_t N, int64_t K, uint16_t* out, hipStream_t s) {
   const uint64_t n_units = (uint64_t)N * (uint64_t)K / 32;
   hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(n_units, 256, 65536)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(codes), n_units, c2, c1, mean,
-                     reinterpret_cast<uint4*>(out), nf4_table());
+                     reinterpret_cast<uint4*>(out), code_table(table));
   return hipGetLastError();
 }
 
-hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
-                            int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* out,
+hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table,
+                            int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* out,
                             hipStream_t st) {
   const dim3 grid((unsigned)(K / kMgCols), (unsigned)((N + kMgRows * kMgChunks - 1) / (kMgRows * kMgChunks)));
   hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), 0, st, codes, c2, c1, mean, N, K, A, B, (int)r, s, out,
-                     nf4_table());
+                     code_table(table));
   return hipGetLastError();
 }
 

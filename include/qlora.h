@@ -62,6 +62,25 @@ extern "C" {
 #define QLORA_ESHAPE 2  /* K % 64 != 0, r above 128, sizes past the supported range */
 #define QLORA_EHIP 3    /* the HIP runtime rejected a launch (hipGetLastError) */
 
+/*
+ * Code tables (the `table` argument): the 16 levels a 4-bit code stands for,
+ * ascending.  The quantizer picks the nearest level, the lowest code on a
+ * tie; an all-zero block stores code 7 (the zero level of NF4 and FP4; the
+ * uniform grid has no zero).  The weight's codes, the quantizer and every
+ * consumer must use the same table.
+ *   QLORA_TABLE_NF4       4-bit NormalFloat (itwiki "QLoRA", NF4 section)
+ *   QLORA_TABLE_UNIFORM4  16 evenly spaced levels on [-1, 1], fp32(-1 + i*(2/15))
+ *                         (the comparison grid of the same section's example)
+ *   QLORA_TABLE_FP4       4-bit float, 2 exponent and 1 mantissa bits (0, 0.5,
+ *                         1, 1.5, 2, 3, 4, 6 and negatives) divided by 6; codes
+ *                         7 and 8 are both zero.  The pages name FP4 without
+ *                         giving its grid; this grid is the library's reading.
+ * Any other value is rejected with QLORA_EINVAL.
+ */
+#define QLORA_TABLE_NF4 0
+#define QLORA_TABLE_UNIFORM4 1
+#define QLORA_TABLE_FP4 2
+
 /* Human-readable name of a status code (static string). */
 const char* qlora_status_str(int status);
 
@@ -73,26 +92,27 @@ const char* qlora_status_str(int status);
 int qlora_nf4_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* n_c2, int64_t* n_c1);
 
 /*
- * Host-only.  Copies the library's 16 NF4 levels (fp32, ascending, code i ->
- * levels[i]) into host memory `levels16`.  The table is built from the
+ * Host-only.  Copies the 16 levels of code table `table` (fp32, ascending,
+ * code i -> levels[i]) into host memory `levels16`.  For QLORA_TABLE_NF4:  The table is built from the
  * quantile construction on the itwiki "QLoRA" page (NF4 section): standard
  * normal quantiles at 8 probabilities spaced evenly from 0.5 (excluded) to the
  * offset 0.9677083 for the positive half, 7 for the negative half, an exact 0,
  * normalized by the largest magnitude.
  */
-int qlora_nf4_levels(float* levels16);
+int qlora_nf4_levels(int table, float* levels16);
 
 /*
  * Blockwise NF4 quantization (itwiki "QLoRA", NF4 section; minnong511
  * "quantization", block-wise quantization).
  *   W      in   fp32 [N,K]      weights (16-B aligned)
+ *   table  in   code table (QLORA_TABLE_*; NF4 is the method's)
  *   codes  out  uint8 [N,K/2]   packed codes (16-B aligned)
  *   absmax out  fp32 [N*K/64]   max |w| of each 64-element block
  * Each element becomes the index of the level nearest to fp32(w / absmax)
  * (IEEE division; an exact tie goes to the lower level); a block with absmax
  * 0 stores code 7 (the zero level).  N >= 0; K >= 0 with K % 64 == 0.
  */
-int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, int table, uint8_t* codes, float* absmax,
                        void* stream);
 
 /*
@@ -102,11 +122,12 @@ int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, flo
  * qlora_nf4_quantize, so the codes and absmax equal those of the widened
  * fp32 weights bit for bit.
  *   W      in   bf16 [N,K]      weights as uint16 bit patterns (8-B aligned)
+ *   table  in   code table (QLORA_TABLE_*)
  *   codes  out  uint8 [N,K/2]   packed codes (16-B aligned)
  *   absmax out  fp32 [N*K/64]   max |w| of each 64-element block
  * Same shapes, status codes and stream behaviour as qlora_nf4_quantize.
  */
-int qlora_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+int qlora_nf4_quantize_bf16(const uint16_t* W, int64_t N, int64_t K, int table, uint8_t* codes, float* absmax,
                             void* stream);
 
 /* Workspace bytes needed by qlora_double_quant for n_c2 constants. */
@@ -131,10 +152,11 @@ int qlora_double_quant(const float* absmax, int64_t n_c2, uint8_t* c2, float* c1
  * Standalone dequantization to bf16 (itwiki "QLoRA", section on the
  * computation: doubleDequant; irregular6612 "QLoRA - Efficient Finetuning of
  * Quantized LLMs": the base weight is dequantized to bf16 before merging).
+ *   table  in   the code table the codes were made with (QLORA_TABLE_*)
  *   W_bf16 out  bf16 [N,K]:  W_deq = bf16( fp32( L[code] * c_hat ) ),
  *   c_hat = fp32( fp32( e4m3(c2) * c1 ) + mean )   (no fused multiply-add).
  */
-int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
+int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table,
                       int64_t N, int64_t K, uint16_t* W_bf16, void* stream);
 
 /*
@@ -142,7 +164,7 @@ int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, 
  * "QLoRA - Efficient Finetuning of Quantized LLMs": after training the
  * adapter is folded into the bf16 base weight; minnong511 "quantization":
  * W' = W + (alpha/r) B A).
- *   codes, c2, c1, mean   the quantized weight [N,K], as for qlora_nf4_dequant
+ *   codes, c2, c1, mean, table   the quantized weight [N,K], as for qlora_nf4_dequant
  *   A      in   bf16 [r,K]
  *   B      in   bf16 [N,r]
  *   W_out  out  bf16 [N,K] (16-B aligned):
@@ -153,8 +175,8 @@ int qlora_nf4_dequant(const uint8_t* codes, const uint8_t* c2, const float* c1, 
  * 0 <= r <= 128 (r = 0 gives W_deq); A and B may be NULL when r = 0.
  * Same shape rules, status codes and stream behaviour as qlora_nf4_dequant.
  */
-int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int64_t N,
-                int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float alpha, uint16_t* W_out,
+int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table,
+                int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float alpha, uint16_t* W_out,
                 void* stream);
 
 /* Workspace bytes needed by qlora_linear_fwd. */
@@ -165,6 +187,7 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  * minnong511 "quantization", y = W x + (alpha/r) B A x).
  *   X      in   bf16 [M,K]       activations (16-B aligned)
  *   codes, c2, c1, mean          the quantized weight W [N,K] (see above)
+ *   table                        its code table (QLORA_TABLE_*)
  *   A      in   bf16 [r,K]       LoRA down factor (16-B aligned)
  *   B      in   bf16 [N,r]       LoRA up factor
  *   r, alpha                     rank (0..128) and LoRA alpha; s = alpha / r in fp32.
@@ -181,7 +204,7 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  * Requires K % 64 == 0.
  */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
-                     const uint8_t* c2, const float* c1, const float* mean, const uint16_t* A,
+                     const uint8_t* c2, const float* c1, const float* mean, int table, const uint16_t* A,
                      const uint16_t* B, int64_t r, float alpha, uint16_t* Y, float* H_out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
@@ -195,6 +218,7 @@ size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  * get gradients).  With H = X A^T and s = alpha / r:
  *   dH = s dY B      dB = s dY^T H      dA = dH^T X      dX = dY W_deq + dH A
  *   dY  in   bf16 [M,N];  X in bf16 [M,K]
+ *   codes, c2, c1, mean, table   the quantized weight, as for the forward
  *   H   in   fp32 [M,r] from the forward, or NULL to recompute it
  *   dX  out  bf16 [M,K] (may be NULL to skip the input gradient)
  *   dA  out  bf16 [r,K];  dB out bf16 [N,r]
@@ -204,7 +228,7 @@ size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  *              (contents on entry do not matter)
  */
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N, int64_t K,
-                     const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean,
+                     const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table,
                      const uint16_t* A, const uint16_t* B, int64_t r, float alpha, const float* H,
                      uint16_t* dX, uint16_t* dA, uint16_t* dB, void* workspace,
                      size_t workspace_bytes, void* stream);

@@ -54,46 +54,49 @@ def test_sizes():
     assert L.qlora_nf4_sizes(0, 0, None, None, None) == _lib.QLORA_OK
 
 
-def test_library_levels_match_oracle_table():
+def test_library_levels_match_oracle_tables():
     import oracle
-    lv = np.array(_lib.qlora_nf4_levels(), dtype=np.float32)
-    assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels_f32().view(np.uint32))
+    for table, ref in ((0, oracle.nf4_levels_f32()), (1, oracle.uniform4_levels_f32()), (2, oracle.fp4_levels_f32())):
+        lv = np.array(_lib.qlora_nf4_levels(table), dtype=np.float32)
+        assert np.array_equal(lv.view(np.uint32), np.asarray(ref, np.float32).view(np.uint32)), table
+    assert _lib.lib().qlora_nf4_levels(3, None) == _lib.QLORA_EINVAL
 
 
 def test_quantize_validation():
     L = _lib.lib()
-    assert L.qlora_nf4_quantize(None, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize(A16, 4, 64, None, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize(MIS, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize(A16, 4, 64, MIS, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize(A16, 4, 96, A16, A16, None) == _lib.QLORA_ESHAPE
-    assert L.qlora_nf4_quantize(A16, -4, 64, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(None, 4, 64, 0, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(A16, 4, 64, 0, None, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(MIS, 4, 64, 0, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(A16, 4, 64, 0, MIS, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize(A16, 4, 96, 0, A16, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_nf4_quantize(A16, -4, 64, 0, A16, A16, None) == _lib.QLORA_EINVAL
     # empty problems are accepted and queue nothing
-    assert L.qlora_nf4_quantize(None, 0, 64, None, None, None) == _lib.QLORA_OK
-    assert L.qlora_nf4_quantize(None, 8, 0, None, None, None) == _lib.QLORA_OK
+    assert L.qlora_nf4_quantize(None, 0, 64, 0, None, None, None) == _lib.QLORA_OK
+    assert L.qlora_nf4_quantize(None, 8, 0, 0, None, None, None) == _lib.QLORA_OK
+    assert L.qlora_nf4_quantize(A16, 4, 64, 3, A16, A16, None) == _lib.QLORA_EINVAL      # unknown table
 
 
 def test_quantize_bf16_validation():
     L = _lib.lib()
-    assert L.qlora_nf4_quantize_bf16(None, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize_bf16(A16, 4, 64, None, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize_bf16(A16 + 4, 4, 64, A16, A16, None) == _lib.QLORA_EINVAL   # W: 8-B aligned
-    assert L.qlora_nf4_quantize_bf16(A16, 4, 64, MIS, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize_bf16(A16, 4, 96, A16, A16, None) == _lib.QLORA_ESHAPE
-    assert L.qlora_nf4_quantize_bf16(A16, -4, 64, A16, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_quantize_bf16(None, 0, 64, None, None, None) == _lib.QLORA_OK
+    assert L.qlora_nf4_quantize_bf16(None, 4, 64, 0, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(A16, 4, 64, 0, None, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(A16 + 4, 4, 64, 0, A16, A16, None) == _lib.QLORA_EINVAL   # W: 8-B aligned
+    assert L.qlora_nf4_quantize_bf16(A16, 4, 64, 0, MIS, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(A16, 4, 96, 0, A16, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_nf4_quantize_bf16(A16, -4, 64, 0, A16, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_quantize_bf16(None, 0, 64, 0, None, None, None) == _lib.QLORA_OK
 
 
 def test_merge_validation():
     L = _lib.lib()
     f = ctypes.c_float(16.0)
-    assert L.qlora_merge(None, A16, A16, A16, 4, 64, A16, A16, 8, f, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, None, A16, 8, f, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, A16, A16, 8, f, MIS, None) == _lib.QLORA_EINVAL
-    assert L.qlora_merge(A16, A16, A16, A16, 4, 100, A16, A16, 8, f, A16, None) == _lib.QLORA_ESHAPE
-    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, A16, A16, 129, f, A16, None) == _lib.QLORA_ESHAPE
-    assert L.qlora_merge(A16, A16, A16, A16, 4, 64, A16, A16, -1, f, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_merge(None, None, None, None, 0, 64, None, None, 8, f, None, None) == _lib.QLORA_OK
+    assert L.qlora_merge(None, A16, A16, A16, 0, 4, 64, A16, A16, 8, f, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(A16, A16, A16, A16, 0, 4, 64, None, A16, 8, f, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(A16, A16, A16, A16, 0, 4, 64, A16, A16, 8, f, MIS, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(A16, A16, A16, A16, 0, 4, 100, A16, A16, 8, f, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_merge(A16, A16, A16, A16, 0, 4, 64, A16, A16, 129, f, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_merge(A16, A16, A16, A16, 0, 4, 64, A16, A16, -1, f, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_merge(None, None, None, None, 0, 0, 64, None, None, 8, f, None, None) == _lib.QLORA_OK
 
 
 def test_double_quant_validation():
@@ -110,20 +113,21 @@ def test_double_quant_validation():
 
 def test_dequant_validation():
     L = _lib.lib()
-    assert L.qlora_nf4_dequant(None, A16, A16, A16, 4, 64, A16, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_dequant(A16, A16, A16, A16, 4, 64, MIS, None) == _lib.QLORA_EINVAL
-    assert L.qlora_nf4_dequant(A16, A16, A16, A16, 4, 100, A16, None) == _lib.QLORA_ESHAPE
+    assert L.qlora_nf4_dequant(None, A16, A16, A16, 0, 4, 64, A16, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_dequant(A16, A16, A16, A16, 0, 4, 64, MIS, None) == _lib.QLORA_EINVAL
+    assert L.qlora_nf4_dequant(A16, A16, A16, A16, 0, 4, 100, A16, None) == _lib.QLORA_ESHAPE
 
 
 def _fwd(L, **kw):
     a = dict(X=A16, M=4, N=64, K=64, codes=A16, c2=A16, c1=A16, mean=A16, A=A16, B=A16, r=8, alpha=16.0,
-             Y=A16, H=None, ws=A16, wsb=None)
+             Y=A16, H=None, ws=A16, wsb=None, table=0)
     a.update(kw)
     if a["wsb"] is None:
         a["wsb"] = L.qlora_linear_fwd_workspace(max(a["M"], 0), max(a["N"], 0), max(a["K"], 0),
                                                 min(max(a["r"], 0), 128))
     return L.qlora_linear_fwd(a["X"], a["M"], a["N"], a["K"], a["codes"], a["c2"], a["c1"], a["mean"],
-                              a["A"], a["B"], a["r"], a["alpha"], a["Y"], a["H"], a["ws"], a["wsb"], None)
+                              a["table"], a["A"], a["B"], a["r"], a["alpha"], a["Y"], a["H"], a["ws"], a["wsb"],
+                              None)
 
 
 def test_fwd_validation():
@@ -141,6 +145,7 @@ def test_fwd_validation():
     assert _fwd(L, X=MIS) == _lib.QLORA_EINVAL
     assert _fwd(L, codes=MIS) == _lib.QLORA_EINVAL
     assert _fwd(L, mean=None) == _lib.QLORA_EINVAL
+    assert _fwd(L, table=3) == _lib.QLORA_EINVAL
     assert _fwd(L, ws=None) == _lib.QLORA_EINVAL
     assert _fwd(L, ws=A16 + 16) == _lib.QLORA_EINVAL          # workspace must be 256-B aligned
     assert _fwd(L, wsb=1) == _lib.QLORA_EINVAL
@@ -160,11 +165,11 @@ def test_bwd_validation():
 
     def call(**kw):
         a = dict(dY=A16, X=A16, M=32, N=64, K=128, codes=A16, c2=A16, c1=A16, mean=A16, A=A16, B=A16, r=8,
-                 alpha=16.0, H=None, dX=A16, dA=A16, dB=A16, ws=A16, wsb=need)
+                 alpha=16.0, H=None, dX=A16, dA=A16, dB=A16, ws=A16, wsb=need, table=0)
         a.update(kw)
         return L.qlora_linear_bwd(a["dY"], a["X"], a["M"], a["N"], a["K"], a["codes"], a["c2"], a["c1"],
-                                  a["mean"], a["A"], a["B"], a["r"], a["alpha"], a["H"], a["dX"], a["dA"],
-                                  a["dB"], a["ws"], a["wsb"], None)
+                                  a["mean"], a["table"], a["A"], a["B"], a["r"], a["alpha"], a["H"], a["dX"],
+                                  a["dA"], a["dB"], a["ws"], a["wsb"], None)
 
     assert call(K=100) == _lib.QLORA_ESHAPE
     assert call(r=200) == _lib.QLORA_ESHAPE
@@ -174,6 +179,8 @@ def test_bwd_validation():
     assert call(dX=MIS) == _lib.QLORA_EINVAL
     assert call(wsb=need - 1) == _lib.QLORA_EINVAL
     assert call(A=None) == _lib.QLORA_EINVAL
+    assert call(table=3) == _lib.QLORA_EINVAL
+    assert call(table=-1) == _lib.QLORA_EINVAL
     # no adapter and an empty batch: nothing to compute, nothing queued
     assert call(r=0, A=None, B=None, dA=None, dB=None, M=0, dY=None, X=None) == _lib.QLORA_OK
 
