@@ -1266,8 +1266,8 @@ struct BwdPlan {
 static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   BwdPlan b;
   b.s_dh = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), (N + BK - 1) / BK);
-  b.s_db = pick_splits((int64_t)cdiv(N, 64) * cdiv(2 * r, 128), (M + BK - 1) / BK);
-  b.s_da = pick_splits((int64_t)cdiv(2 * r, 128) * cdiv(K, 64), (M + BK - 1) / BK);
+  b.s_db = pick_splits((int64_t)cdiv(N, 128) * cdiv(2 * r, 128), (M + BK - 1) / BK);
+  b.s_da = pick_splits((int64_t)cdiv(2 * r, 128) * cdiv(K, 128), (M + BK - 1) / BK);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   b.off_H = 0;
   b.off_dH = al((size_t)M * r * 4);
@@ -1321,11 +1321,11 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     }
     // dB = s dY^T H : rows n, cols j, reduction m; H as [hi; lo] (2r columns)
     if (a.N > 0) {
-      SColsBf16<64> la;
+      SColsBf16<128> la;
       la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
       SRowsBf16<128> lb;
       lb.src = Ht; lb.ld = a.M; lb.red = (int)a.M; lb.vec = m_vec;
-      if ((e = launch_skinny<64, 128>(la, lb, a.N, 2 * a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
+      if ((e = launch_skinny<128, 128>(la, lb, a.N, 2 * a.r, a.M, plan.s_db, part, s)) != hipSuccess) return e;
       hipLaunchKernelGGL(reduce_hilo_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, part, plan.s_db,
                          (int64_t)(a.N * 2 * a.r), a.N, a.r, 2 * a.r, a.r, a.scale, a.dB);
     }
@@ -1333,9 +1333,9 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     {
       SRowsBf16<128> la;
       la.src = dHt; la.ld = a.M; la.red = (int)a.M; la.vec = m_vec;
-      SColsBf16<64> lb;
+      SColsBf16<128> lb;
       lb.src = a.X; lb.ld = a.K; lb.red = (int)a.M; lb.vec = true;
-      if ((e = launch_skinny<128, 64>(la, lb, 2 * a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
+      if ((e = launch_skinny<128, 128>(la, lb, 2 * a.r, a.K, a.M, plan.s_da, part, s)) != hipSuccess) return e;
       hipLaunchKernelGGL(reduce_hilo_kernel, dim3(cdiv(a.r * a.K, 256)), dim3(256), 0, s, part, plan.s_da,
                          (int64_t)(2 * a.r * a.K), a.r, a.K, a.K, a.r * a.K, 1.0f, a.dA);
     }
