@@ -250,6 +250,48 @@ def bench_decoder(torch, qa, reps, seed=5):
         log(f"[bench] decoder pass M={M}: {ms:.3f} ms")
         del xs, ys, ws
     del layers
+    res["fused"] = bench_decoder_fused(torch, qa, reps, gen)
+    return res
+
+
+def bench_decoder_fused(torch, qa, reps, gen):
+    """The same decoder with q|k|v and gate|up concatenated along N (128
+    launches per pass instead of 224; the q and v adapters as one rank-32
+    adapter with block-structured B), one pass at M = 1 and M = 512."""
+    import synth
+    layers = []
+    for _ in range(synth.DECODER_LAYERS):
+        for mod, N, K, r in synth.DECODER_FUSED:
+            W = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+            q = qa.quantize(W)
+            del W
+            A = B = None
+            if r:
+                A = (torch.randn((r, K), generator=gen, device="cuda") / K).to(torch.bfloat16)
+                B = (torch.randn((N, r), generator=gen, device="cuda") * 0.01)
+                B = (B * torch.from_numpy(synth.fused_qkv_b_mask(N, r)).to("cuda")).to(torch.bfloat16)
+            layers.append((q, A, B, N, K, r))
+    res = {"launches_per_pass": len(layers)}
+    for M in (1, 512):
+        xs = {K: torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16) for K in (4096, 11008)}
+        ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N in (4096, 12288, 22016)}
+        need = max(qa.qlora_linear_fwd_workspace(M, N, K, r) for _, N, K, r in synth.DECODER_FUSED)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+
+        def one_pass(i):
+            for q, A, B, N, K, r in layers:
+                qa.qlora_linear_fwd(xs[K], q.codes, q.c2, q.c1, q.mean, A, B,
+                                    synth.FUSED_QKV_ALPHA if r else 16.0, ys[N], None, ws, N)
+
+        ms = (timed_graph if M == 1 else timed_eager)(torch, one_pass, reps, 1)
+        byts = sum(fwd_bytes(M, N, K, r) for _, _, _, N, K, r in layers)
+        fl = sum(fwd_flops(M, N, K, r) for _, _, _, N, K, r in layers)
+        res[f"m{M}"] = {"ms": ms, "GBps": byts / ms / 1e6, "TFLOPs": fl / ms / 1e9,
+                        "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS,
+                        "mfma_frac": fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+        log(f"[bench] fused decoder pass M={M}: {ms:.3f} ms")
+        del xs, ys, ws
+    del layers
     return res
 
 
@@ -395,6 +437,10 @@ def main():
         log(f"[bench] 7B decoder: quantize {res['params'] / 1e9:.2f}B params in {res['quantize_ms']:.1f} ms; "
             f"fwd M=1 {res['m1']['ms']:.3f} ms ({res['m1']['GBps']:.0f} GB/s), "
             f"M=512 {res['m512']['ms']:.3f} ms ({res['m512']['TFLOPs']:.0f} TFLOP/s)")
+        fu = res["fused"]
+        log(f"[bench] 7B decoder, q|k|v and gate|up fused ({fu['launches_per_pass']} launches): "
+            f"fwd M=1 {fu['m1']['ms']:.3f} ms ({fu['m1']['GBps']:.0f} GB/s), "
+            f"M=512 {fu['m512']['ms']:.3f} ms ({fu['m512']['TFLOPs']:.0f} TFLOP/s)")
         torch.cuda.empty_cache()
 
     traffic = recorded_traffic("qlora_gemv_kernel_decode_4096x4096_m1.md", ["gemv.hip", "decode_common.h"])

@@ -123,3 +123,23 @@ DECODER_LAYERS = 32
 
 def decoder_seed(layer: int, module: int) -> int:
     return 1000 + 10 * layer + module
+
+
+# The same decoder with the linears that read the same input concatenated
+# along N (q|k|v and gate|up): one quantized weight and one launch per group.
+# The q and v adapters (r = 16 each) become one rank-32 adapter of the group:
+# A stacks A_q over A_v, and B is block-structured -- q's rows use columns
+# 0..15, v's rows columns 16..31, k's rows are zero -- with alpha = 32 so that
+# alpha / r stays 1.
+DECODER_FUSED = (("qkv", 12288, 4096, 32), ("o", 4096, 4096, 0), ("gate_up", 22016, 4096, 0),
+                 ("down", 4096, 11008, 0))
+FUSED_QKV_ALPHA = 32.0
+
+
+def fused_qkv_b_mask(N: int = 12288, r: int = 32) -> np.ndarray:
+    """Where the fused q|k|v adapter's B [N, r] may be non-zero (bool)."""
+    seg = N // 3
+    mask = np.zeros((N, r), dtype=bool)
+    mask[:seg, : r // 2] = True          # q rows: q's 16 adapter columns
+    mask[2 * seg:, r // 2:] = True       # v rows: v's 16 adapter columns
+    return mask

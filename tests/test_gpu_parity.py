@@ -558,6 +558,31 @@ def test_train65b_layer_full_size_sampled():
     check_close(bf16_f64(host_bf16_bits(dB))[rows], g2["dB"], "dB (sampled rows)")
 
 
+def test_decoder_fused_qkv_full_size_sampled():
+    """The decoder's q|k|v group as one 12288 x 4096 weight with the
+    block-structured rank-32 adapter (q rows on columns 0..15, v rows on
+    16..31, k rows zero), at M = 1 and M = 512: constants in full and 256
+    sampled output columns spread over the three segments, against the
+    oracle."""
+    N, K, r = 12288, 4096, 32
+    rows = np.sort(np.concatenate([np.random.default_rng(77 + i).choice(4096, 85 + (i == 0), replace=False) + 4096 * i
+                                   for i in range(3)]))
+    q = ref = None
+    for M in (1, 512):
+        sh = synth.LayerShape(f"decoder_qkv_m{M}", M=M, N=N, K=K, r=r, seed_offset=1777)
+        say(f"[decoder fused] {sh.name}")
+        d = synth.make_layer(sh)
+        d["B"] = np.where(synth.fused_qkv_b_mask(N, r), d["B"], np.uint16(0))
+        if q is None:
+            ref = oracle_sampled(d["W"], rows)
+            q = gpu_quantize(d["W"])
+            check_quantized(q, ref, rows)
+        A, B = adapter(d, r)
+        Y, H = qa.linear_fwd(dev_bf16(d["X"]), q, A, B, synth.FUSED_QKV_ALPHA)
+        torch.cuda.synchronize()
+        check_fwd_sampled(d, ref, rows, Y, H, synth.FUSED_QKV_ALPHA, r, sh.name)
+
+
 @pytest.mark.parametrize("layer", [0, synth.DECODER_LAYERS - 1])
 def test_decoder_layer_full_size_sampled(layer):
     """One layer of the 7B-shaped decoder (q, k, v, o, gate, up, down; LoRA
