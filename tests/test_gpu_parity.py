@@ -268,6 +268,9 @@ FWD_CASES = [
     (1, 96, 11008, 64), (12, 40, 1280, 40),
     (17, 130, 192, 16), (33, 257, 128, 1), (130, 300, 448, 72), (256, 512, 1024, 64), (64, 64, 64, 64),
     (600, 700, 1536, 16), (513, 2304, 512, 64),
+    # larger M: 128 x 128 tiles with split-K, a ragged M and r, one whole
+    # round of 256 x 256 tiles
+    (1024, 300, 448, 72), (1100, 600, 1280, 33), (2048, 8192, 256, 8),
     # 16 x 18 tiles of 256: one whole round on 256 x 256 tiles, a ragged
     # tail of 296 columns on 128 x 128 tiles
     (4096, 4392, 128, 16),
