@@ -957,55 +957,55 @@ __global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
 // per weight (codes in, bf16 out), a few percent of the product's time at
 // M >= 512; below that the fused dx_gemm_kernel reads the codes directly.
 constexpr int64_t kDxtMinM = 512;
-constexpr int kDtN = 64, kDtK = 128;   // tile of the transposing expansion (n x k)
+constexpr int kDtN = 128, kDtK = 256;   // tile of the transposing expansion (n x k)
 
-// W_deq^T tile: thread t takes rows n0 + 2 (t % 32) + {0, 1} and the 16
-// columns k0 + 16 (t / 32) .. +15 (one block of each row, so one constant
-// per row), expands them to bf16 (fp32 level * c_hat, bit-exact with W_deq),
-// and stores (n, n+1) pairs per column into an LDS tile [k][n]; the tile then
-// leaves as 128-byte rows of the output.
-__global__ void __launch_bounds__(256) nf4_dequant_t_kernel(const uint8_t* __restrict__ codes,
+// W_deq^T tile: thread t takes rows n0 + 2 (t % 64) + {0, 1} and the 32
+// columns k0 + 32 (t / 64) .. +31 (half a block of each row, so one constant
+// per row): one 16-byte code load per row, 8 threads covering 128
+// contiguous code bytes of a row.  It expands them to bf16 (fp32 level *
+// c_hat, bit-exact with W_deq) and stores (n, n+1) pairs per column into an
+// LDS tile [k][n]; the tile leaves as 256-byte rows of the output.
+__global__ void __launch_bounds__(512) nf4_dequant_t_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ c2,
                                                             const float* __restrict__ c1,
                                                             const float* __restrict__ mean, int64_t N, int64_t K,
                                                             int64_t ldt, uint16_t* __restrict__ out, Nf4Table tab) {
   __shared__ float lut[16];
-  __shared__ __attribute__((aligned(16))) uint32_t t[kDtK * kDtN / 2];   // [k][n pair], 16 KiB
+  __shared__ __attribute__((aligned(16))) uint32_t t[kDtK * kDtN / 2];   // [k][n pair], 64 KiB
   load_lut(lut, tab);
-  const int64_t ntiles = ldt / kDtN;
+  const int64_t ntiles = (ldt + kDtN - 1) / kDtN;
   const int64_t n0 = (int64_t)(blockIdx.x % ntiles) * kDtN, k0 = (int64_t)(blockIdx.x / ntiles) * kDtK;
-  const int np = threadIdx.x & 31, kg = threadIdx.x >> 5;
-  const int64_t kc = k0 + 16 * kg;
+  const int np = threadIdx.x & 63, kg = threadIdx.x >> 6;
+  const int64_t kc = k0 + 32 * kg;
   const float mu = *mean;
-  uint32_t w[2][2];
+  u32x4 w[2];
   float chat[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t n = n0 + 2 * np + h;
     if (n < N && kc < K) {
-      const uint8_t* src = codes + n * (K / 2) + kc / 2;
-      w[h][0] = *reinterpret_cast<const uint32_t*>(src);
-      w[h][1] = *reinterpret_cast<const uint32_t*>(src + 4);
+      w[h] = ld16(codes + n * (K / 2) + kc / 2);
       const int64_t bi = n * (K / 64) + kc / 64;
       chat[h] = dequant_constant(c2[bi], c1[bi >> 8], mu);
     } else {   // rows past N (and columns past K) expand to zero
-      w[h][0] = w[h][1] = 0u;
+      w[h] = u32x4{0u, 0u, 0u, 0u};
       chat[h] = 0.f;
     }
   }
   __syncthreads();   // the level table
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < 32; ++e) {
     const float lo = __fmul_rn(lut[(w[0][e >> 3] >> (4 * (e & 7))) & 15u], chat[0]);
     const float hi = __fmul_rn(lut[(w[1][e >> 3] >> (4 * (e & 7))) & 15u], chat[1]);
-    t[(16 * kg + e) * (kDtN / 2) + np] = pack_bf16x2(lo, hi);
+    t[(32 * kg + e) * (kDtN / 2) + np] = pack_bf16x2(lo, hi);
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kDtK * kDtN / 8 / 256; ++i) {
-    const int c = threadIdx.x + i * 256, kr = c >> 3, j = c & 7;
-    const int64_t k = k0 + kr;
-    if (k < K) *reinterpret_cast<u32x4*>(out + k * ldt + n0 + 8 * j) = *reinterpret_cast<const u32x4*>(&t[kr * 32 + 4 * j]);
+  for (int i = 0; i < kDtK * kDtN / 8 / 512; ++i) {
+    const int c = threadIdx.x + i * 512, kr = c >> 4, j = c & 15;
+    const int64_t k = k0 + kr, n = n0 + 8 * j;
+    if (k < K && n < ldt)
+      *reinterpret_cast<u32x4*>(out + k * ldt + n) = *reinterpret_cast<const u32x4*>(&t[kr * (kDtN / 2) + 4 * j]);
   }
 }
 
@@ -1343,7 +1343,7 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
   // dX = dY W_deq + dH A
   if (a.dX && a.M > 0 && plan.dxt) {
     uint16_t* wt = reinterpret_cast<uint16_t*>(ws + plan.off_wt);
-    hipLaunchKernelGGL(nf4_dequant_t_kernel, dim3((unsigned)((plan.ldt / kDtN) * cdiv(a.K, kDtK))), dim3(256), 0, s,
+    hipLaunchKernelGGL(nf4_dequant_t_kernel, dim3(cdiv(plan.ldt, kDtN) * cdiv(a.K, kDtK)), dim3(512), 0, s,
                        a.w.codes, a.w.c2, a.w.c1, a.w.mean, a.N, a.K, plan.ldt, wt, code_table(a.w.table));
     DxtParams p;
     p.dY = a.dY;

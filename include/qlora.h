@@ -93,8 +93,8 @@ int qlora_nf4_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* n_c2, in
 
 /*
  * Host-only.  Copies the 16 levels of code table `table` (fp32, ascending,
- * code i -> levels[i]) into host memory `levels16`.  For QLORA_TABLE_NF4:  The table is built from the
- * quantile construction on the itwiki "QLoRA" page (NF4 section): standard
+ * code i -> levels[i]) into host memory `levels16`.  QLORA_TABLE_NF4's levels
+ * come from the quantile construction on the itwiki "QLoRA" page (NF4 section): standard
  * normal quantiles at 8 probabilities spaced evenly from 0.5 (excluded) to the
  * offset 0.9677083 for the positive half, 7 for the negative half, an exact 0,
  * normalized by the largest magnitude.
