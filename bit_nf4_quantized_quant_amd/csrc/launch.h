@@ -44,9 +44,6 @@ struct FwdArgs {
   void* workspace;  // remaining workspace past H
 };
 
-size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
-hipError_t launch_linear_fwd(const FwdArgs& a, hipStream_t s);
-
 struct BwdArgs {
   const uint16_t* dY;
   const uint16_t* X;
@@ -62,7 +59,6 @@ struct BwdArgs {
   void* workspace;
 };
 
-size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s);
 
 }  // namespace qlora
