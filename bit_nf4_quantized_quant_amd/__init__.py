@@ -50,6 +50,37 @@ def quantize(W, stream=None, table: int = 0) -> QuantizedWeight:
     return QuantizedWeight(N, K, codes, absmax, c2, c1, mean, table)
 
 
+def save_quantized(q: QuantizedWeight, path: str) -> None:
+    """Write a quantized weight (codes, constants, mean, shape, table) to an
+    uncompressed .npz file; plain arrays only, nothing pickled."""
+    import numpy as np
+
+    def arr(t):
+        return None if t is None else t.detach().cpu().numpy()
+    fields = {"N": np.int64(q.N), "K": np.int64(q.K), "table": np.int64(q.table), "codes": arr(q.codes),
+              "c2": arr(q.c2), "c1": arr(q.c1), "mean": arr(q.mean)}
+    if q.absmax is not None:
+        fields["absmax"] = arr(q.absmax)
+    np.savez(path, **fields)
+
+
+def load_quantized(path: str, device="cuda") -> QuantizedWeight:
+    """Read a weight written by save_quantized onto `device` (no pickle)."""
+    import numpy as np
+    import torch
+    with np.load(path, allow_pickle=False) as z:
+        N, K, table = int(z["N"]), int(z["K"]), int(z["table"])
+        code_bytes, n_c2, n_c1 = qlora_nf4_sizes(N, K)
+        codes, c2, c1, mean = z["codes"], z["c2"], z["c1"], z["mean"]
+        if (codes.dtype != np.uint8 or codes.shape != (N, K // 2) or c2.dtype != np.uint8 or c2.shape != (n_c2,)
+                or c1.dtype != np.float32 or c1.size < max(n_c1, 1) or mean.dtype != np.float32
+                or mean.shape != (1,) or table not in (0, 1, 2)):
+            raise ValueError(f"{path}: not a quantized [{N}, {K}] weight")
+        absmax = torch.from_numpy(z["absmax"]).to(device) if "absmax" in z.files else None
+        return QuantizedWeight(N, K, torch.from_numpy(codes).to(device), absmax, torch.from_numpy(c2).to(device),
+                               torch.from_numpy(c1).to(device), torch.from_numpy(mean).to(device), table)
+
+
 def dequantize(q: QuantizedWeight, stream=None):
     """bf16 [N, K] weight (returned as int16 bit patterns viewed as bfloat16)."""
     import torch

@@ -190,3 +190,30 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def test_save_load_quantized_round_trip(tmp_path):
+    """The quantized tensor is the artifact: it round-trips through .npz bit
+    for bit (host tensors here; the device copies are plain transfers), and a
+    file of the wrong shape is refused."""
+    import torch
+    import bit_nf4_quantized_quant_amd as qa
+    N, K = 5, 192
+    rng = np.random.default_rng(3)
+    code_bytes, n_c2, n_c1 = _lib.qlora_nf4_sizes(N, K)
+    q = qa.QuantizedWeight(N, K, torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)),
+                           torch.from_numpy(rng.random(n_c2, dtype=np.float32)),
+                           torch.from_numpy(rng.integers(0, 256, n_c2, dtype=np.uint8)),
+                           torch.from_numpy(rng.random(n_c1, dtype=np.float32)),
+                           torch.tensor([0.125], dtype=torch.float32), 2)
+    path = str(tmp_path / "w.npz")
+    qa.save_quantized(q, path)
+    r = qa.load_quantized(path, device="cpu")
+    assert (r.N, r.K, r.table) == (N, K, 2)
+    for a, b in ((q.codes, r.codes), (q.absmax, r.absmax), (q.c2, r.c2), (q.c1, r.c1), (q.mean, r.mean)):
+        assert a.dtype == b.dtype and torch.equal(a, b)
+    bad = str(tmp_path / "bad.npz")
+    np.savez(bad, N=np.int64(N), K=np.int64(K + 64), table=np.int64(0), codes=q.codes.numpy(), c2=q.c2.numpy(),
+             c1=q.c1.numpy(), mean=q.mean.numpy())
+    with pytest.raises(ValueError):
+        qa.load_quantized(bad, device="cpu")

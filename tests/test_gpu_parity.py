@@ -212,6 +212,22 @@ def test_code_tables_forward_backward(table, name, M, N, K, r):
     check_close(bf16_f64(host_bf16_bits(dB)), g["dB"], "dB", bf16_floor=M == 1)
 
 
+def test_saved_weight_reloads_to_the_same_layer(tmp_path):
+    """A quantized weight written to .npz and read back onto the GPU gives the
+    same W_deq and the same forward output, bit for bit."""
+    d = synth.make_layer(synth.LayerShape("t", M=3, N=130, K=320, r=8, seed_offset=5151))
+    q = gpu_quantize(d["W"])
+    path = str(tmp_path / "w.npz")
+    qa.save_quantized(q, path)
+    q2 = qa.load_quantized(path, device="cuda")
+    X, A, B = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"])
+    assert torch.equal(qa.dequantize(q).view(torch.int16), qa.dequantize(q2).view(torch.int16))
+    Y1, _ = qa.linear_fwd(X, q, A, B, 16.0)
+    Y2, _ = qa.linear_fwd(X, q2, A, B, 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("N,K", [(256, 256), (5, 192), (33, 1088)])
 def test_dequant_bitexact(N, K):
     W = special_weight(N, K, seed=3 * N + K)
