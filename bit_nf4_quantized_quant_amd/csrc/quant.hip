@@ -201,9 +201,10 @@ __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint4* __restric
 // Bound by the fp64 multiply-adds (r per weight).  A workgroup takes 64
 // columns and 256 rows (two chunks of 128); thread (row group, column group)
 // holds 4 rows x 8 columns of sums.  A's 64 columns and the chunk's B rows sit
-// in LDS as fp32 (exact for bf16); B rows are padded to 129 so that the 32
-// row groups of one j fall on distinct banks.
-constexpr int kMgCols = 64, kMgRows = 128, kMgChunks = 2, kMgMaxR = 128, kMgPitch = kMgMaxR + 1;
+// in LDS as fp32 (exact for bf16), sized by r (dynamic LDS: 49 KB at r = 64,
+// three workgroups per CU); B rows are padded to r + 1 so that the row groups
+// of one j spread over the banks.
+constexpr int kMgCols = 64, kMgRows = 128, kMgChunks = 2, kMgMaxR = 128;
 
 // fp64 -> bf16, rounded to nearest even in effect: the fp64 value is first
 // rounded to fp32 by round-to-odd (truncate, then set the last bit if
@@ -228,8 +229,12 @@ __global__ void __launch_bounds__(256) nf4_merge_kernel(const uint8_t* __restric
                                                         const uint16_t* __restrict__ B, int r, float s,
                                                         uint16_t* __restrict__ out, Nf4Table tab) {
   __shared__ float lut[16];
-  __shared__ __attribute__((aligned(16))) float at[kMgMaxR * kMgCols];     // A[j][k0 ..]
-  __shared__ float bt[kMgRows * kMgPitch];                                  // B[n][j] of the chunk
+  // sized by r (dynamic), so that at the common ranks several workgroups
+  // share a CU: A[j][k0 ..] (r x 64), then B[n][j] of the chunk (128 x (r + 1))
+  extern __shared__ __attribute__((aligned(16))) float mg_smem[];
+  const int pitch = r + 1;
+  float* at = mg_smem;
+  float* bt = mg_smem + r * kMgCols;
   const int64_t k0 = (int64_t)blockIdx.x * kMgCols;
   const int64_t nbase = (int64_t)blockIdx.y * (kMgRows * kMgChunks);
   if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
@@ -245,7 +250,7 @@ __global__ void __launch_bounds__(256) nf4_merge_kernel(const uint8_t* __restric
     __syncthreads();   // (A and the level table; the previous chunk's B rows are no longer read)
     for (int i = threadIdx.x; i < kMgRows * r; i += 256) {
       const int row = i / r, j = i - row * r;
-      bt[row * kMgPitch + j] = n0 + row < N ? __uint_as_float((uint32_t)B[(n0 + row) * r + j] << 16) : 0.f;
+      bt[row * pitch + j] = n0 + row < N ? __uint_as_float((uint32_t)B[(n0 + row) * r + j] << 16) : 0.f;
     }
     __syncthreads();
     double acc[4][8];
@@ -259,7 +264,7 @@ __global__ void __launch_bounds__(256) nf4_merge_kernel(const uint8_t* __restric
       const double a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const double b = (double)bt[(4 * rg + i) * kMgPitch + j];
+        const double b = (double)bt[(4 * rg + i) * pitch + j];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[i][e] = __fma_rn(b, a[e], acc[i][e]);
       }
@@ -345,7 +350,16 @@ hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float
                             int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float s, uint16_t* out,
                             hipStream_t st) {
   const dim3 grid((unsigned)(K / kMgCols), (unsigned)((N + kMgRows * kMgChunks - 1) / (kMgRows * kMgChunks)));
-  hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), 0, st, codes, c2, c1, mean, N, K, A, B, (int)r, s, out,
+  const size_t lds = (size_t)(r * kMgCols + kMgRows * (r + 1)) * sizeof(float);
+  static bool raised = false;   // the limit is raised once, for r = kMgMaxR
+  if (!raised) {
+    const size_t max_lds = (size_t)(kMgMaxR * kMgCols + kMgRows * (kMgMaxR + 1)) * sizeof(float);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(nf4_merge_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), lds, st, codes, c2, c1, mean, N, K, A, B, (int)r, s, out,
                      code_table(table));
   return hipGetLastError();
 }
