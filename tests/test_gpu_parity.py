@@ -19,7 +19,7 @@ from gpu_util import bf16_f64, check_close, dev_bf16, dev_f32, host, host_bf16_b
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-if not torch.cuda.is_available():  # pragma: no cover - the GPU suite runs on the GPU machine
+if not torch.cuda.is_available():  # pragma: no cover - the GPU suite needs an MI355X
     pytest.skip("no GPU", allow_module_level=True)
 
 import bit_nf4_quantized_quant_amd as qa  # noqa: E402  (raises if libqlora.so is missing)
