@@ -1263,11 +1263,20 @@ struct BwdPlan {
   size_t off_H, off_dH, off_Ht, off_dHt, off_part, off_wt, bytes;
 };
 
+// Split-K of a 128 x 128 skinny product: as many splits as keep all its
+// workgroups in one round (two per CU at 74 KB of LDS each), at least 1, at
+// most 64 and no more than the reduction's steps.  (A second, partly empty
+// round cost the 65B-scale layer's dB product 6 us.)
+static int one_round_splits(int64_t tiles, int64_t ksteps) {
+  const int64_t slots = 2 * (int64_t)cu_count();
+  return (int)std::max<int64_t>(1, std::min<int64_t>({64, slots / std::max<int64_t>(tiles, 1), ksteps}));
+}
+
 static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   BwdPlan b;
   b.s_dh = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), (N + BK - 1) / BK);
-  b.s_db = pick_splits((int64_t)cdiv(N, 128) * cdiv(2 * r, 128), (M + BK - 1) / BK);
-  b.s_da = pick_splits((int64_t)cdiv(2 * r, 128) * cdiv(K, 128), (M + BK - 1) / BK);
+  b.s_db = one_round_splits((int64_t)cdiv(N, 128) * cdiv(2 * r, 128), (M + BK - 1) / BK);
+  b.s_da = one_round_splits((int64_t)cdiv(2 * r, 128) * cdiv(K, 128), (M + BK - 1) / BK);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   b.off_H = 0;
   b.off_dH = al((size_t)M * r * 4);
