@@ -377,6 +377,9 @@ def main():
                          "(for per-dispatch counter collection)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--train65b-only", action="store_true",
+                    help="only the 65B-scale layer's forward and backward, --steps calls each, no JSON line "
+                         "(for matrix-core counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -390,6 +393,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
+
+    if args.train65b_only:
+        import synth
+        sh = synth.TRAIN65B
+        f = bench_fwd(torch, qa, sh.M, sh.N, sh.K, sh.r, args.steps, 1, 1, graph=False)
+        b = bench_bwd(torch, qa, sh.M, sh.N, sh.K, sh.r, args.steps, 1)
+        log(f"[bench] {sh.name}: fwd {f['ms']:.3f} ms ({f['TFLOPs']:.0f} TFLOP/s), "
+            f"bwd {b['ms']:.3f} ms ({b['TFLOPs']:.0f} TFLOP/s)")
+        return
 
     N, K, r = 4096, 4096, 64
     copies = max(2, int(2 * MALL_BYTES / fwd_bytes(1, N, K, r)) + 1)
