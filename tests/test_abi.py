@@ -217,3 +217,15 @@ def test_save_load_quantized_round_trip(tmp_path):
              c1=q.c1.numpy(), mean=q.mean.numpy())
     with pytest.raises(ValueError):
         qa.load_quantized(bad, device="cpu")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; asked for more it says so and exits with 2."""
+    import json
+    import subprocess
+    import sys
+    run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert run.returncode == 2
+    msg = json.loads(run.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
