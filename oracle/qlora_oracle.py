@@ -82,14 +82,33 @@ def uniform4_levels_f32() -> np.ndarray:
     return f32(np.linspace(-1.0, 1.0, 16))
 
 
+E2M1_EXP_BITS, E2M1_MAN_BITS, E2M1_BIAS = 2, 1, 1   # the 4-bit float format (E2M1)
+
+
+def e2m1_value(bits: int) -> float:
+    """Value of a 4-bit float bit pattern: sign, 2 exponent bits with bias 1,
+    1 mantissa bit; exponent field 0 is subnormal (0 or 0.5); no infinity or
+    NaN encodings."""
+    sign = -1.0 if (bits >> (E2M1_EXP_BITS + E2M1_MAN_BITS)) & 1 else 1.0
+    e = (bits >> E2M1_MAN_BITS) & ((1 << E2M1_EXP_BITS) - 1)
+    m = bits & ((1 << E2M1_MAN_BITS) - 1)
+    frac = m / (1 << E2M1_MAN_BITS)
+    if e == 0:
+        return sign * frac * 2.0 ** (1 - E2M1_BIAS)
+    return sign * (1.0 + frac) * 2.0 ** (e - E2M1_BIAS)
+
+
 def fp4_levels_f32() -> np.ndarray:
     """FP4 as a 16-entry table (a reading: the pages name FP4 -- irregular6612
     "QLoRA - Efficient Finetuning of Quantized LLMs" and itwiki "QLoRA" compare
-    NF4 with it -- but give no grid): the 4-bit float with 2 exponent and 1
-    mantissa bits, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, divided by 6 so that
-    it spans [-1, 1]; ascending, with its two zeros at codes 7 and 8 (both +0)."""
-    mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]) / 6.0
-    return f32(np.concatenate([-mag[:0:-1], [0.0, 0.0], mag[1:]]))
+    NF4 with it -- but give no grid): the values of all 16 bit patterns of the
+    4-bit float E2M1, sorted ascending and divided by the largest magnitude so
+    that they span [-1, 1].  Its two zeros (+0 and -0) sit at codes 7 and 8;
+    both are stored as +0 (reading: a code that means zero dequantizes to +0)."""
+    vals = np.array([e2m1_value(b) for b in range(16)], dtype=F64)
+    vals = np.sort(vals) / np.max(np.abs(vals))
+    vals[vals == 0.0] = 0.0                  # -0 -> +0
+    return f32(vals)
 
 
 # ---------------------------------------------------------------------------

@@ -279,6 +279,65 @@ def test_e4m3_encode_matches_torch_and_bruteforce():
         assert o.e4m3_encode(np.array([x], np.float32))[0] == code
 
 
+# ---------------------------------------------------------------- FP4 (E2M1) table
+
+def _minifloat_by_code(exp_bits, man_bits, bias, specials):
+    """Value of every bit pattern of a small binary float format, written from
+    the general sign / biased exponent / fraction layout (None where the
+    pattern is not a finite number).  specials: "ieee" (the top exponent is
+    infinity and NaN), "fn" (only the all-ones pattern is NaN), "none"."""
+    out = []
+    top = (1 << exp_bits) - 1
+    for code in range(1 << (1 + exp_bits + man_bits)):
+        sign = -1 if code >> (exp_bits + man_bits) else 1
+        e = (code >> man_bits) & top
+        f = Fraction(code & ((1 << man_bits) - 1), 1 << man_bits)
+        if (specials == "ieee" and e == top) or (specials == "fn" and e == top and f == 1 - Fraction(1, 1 << man_bits)):
+            out.append(None)
+            continue
+        mag = f * Fraction(2) ** (1 - bias) if e == 0 else (1 + f) * Fraction(2) ** (e - bias)
+        out.append(sign * mag)
+    return out
+
+
+def test_minifloat_enumerator_matches_torch_fp8():
+    """The general enumerator above reproduces torch's two 8-bit float
+    formats code by code, so it can stand as the reference for E2M1."""
+    torch = pytest.importorskip("torch")
+    for dtype, e, m, bias, sp in ((torch.float8_e4m3fn, 4, 3, 7, "fn"), (torch.float8_e5m2, 5, 2, 15, "ieee")):
+        ref = torch.arange(256, dtype=torch.uint8).view(dtype).to(torch.float64).numpy()
+        ours = _minifloat_by_code(e, m, bias, sp)
+        for code in range(256):
+            if ours[code] is None:
+                assert not np.isfinite(ref[code]), (dtype, code)
+            else:
+                assert Fraction(float(ref[code])) == ours[code], (dtype, code)
+
+
+def test_fp4_levels_from_e2m1_definition():
+    """The FP4 table (reading: the E2M1 4-bit float) against the published
+    E2M1 parameters (tests/golden/fp4_e2m1_format.txt) through the enumerator
+    pinned on torch's fp8 formats: every bit pattern's value, sorted and
+    divided by the largest magnitude; the two zeros at codes 7 and 8, both +0."""
+    _, g = _golden_numbers("fp4_e2m1_format.txt")
+    ref = _minifloat_by_code(int(g["exp_bits"]), int(g["man_bits"]), int(g["bias"]), "none")
+    assert len(ref) == 16 and all(v is not None for v in ref)
+    pos = sorted(v for v in ref if v > 0)
+    assert max(pos) == Fraction(g["max_normal"]) and min(pos) == Fraction(g["min_subnormal"])
+    assert min(v for v in pos if v >= 1) == Fraction(g["min_normal"])
+    assert max(v for v in pos if v < Fraction(g["min_normal"])) == Fraction(g["max_subnormal"])
+    top = max(abs(v) for v in ref)
+    expect = np.array([float(v / top) for v in sorted(ref)], dtype=np.float64)
+    expect[expect == 0.0] = 0.0
+    L = o.fp4_levels_f32()
+    assert L.dtype == np.float32 and len(L) == 16
+    assert np.array_equal(L.view(np.uint32), expect.astype(np.float32).view(np.uint32))
+    assert L.view(np.uint32)[7] == 0 and L.view(np.uint32)[8] == 0      # +0 twice
+    assert np.all(np.diff(L) >= 0) and int(np.sum(np.diff(L) == 0)) == 1
+    # the oracle's per-pattern decode agrees with the reference pattern by pattern
+    assert all(Fraction(o.e2m1_value(b)) == ref[b] for b in range(16))
+
+
 # ---------------------------------------------------------------- mean / double quant
 
 def _check_rne(result, exact):
@@ -544,6 +603,43 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(qo, "_nearest_level", real_near)
 
 
+def test_planted_mistakes_in_code_tables_and_merge_are_caught(monkeypatch):
+    """A wrong E2M1 magnitude, a subnormal read with an implicit leading one,
+    and the merge rounded through fp32 before bf16 each fail their pin."""
+    import oracle.qlora_oracle as qo
+    real_e2m1 = qo.e2m1_value
+
+    def wrong_top(bits):
+        return 5.0 * (-1 if bits & 8 else 1) if bits & 7 == 7 else real_e2m1(bits)
+
+    def implicit_one(bits):
+        v = real_e2m1(bits)
+        return v + (-1.0 if bits & 8 else 1.0) if (bits >> 1) & 3 == 0 else v
+
+    for bad in (wrong_top, implicit_one):
+        monkeypatch.setattr(qo, "e2m1_value", bad)
+        with pytest.raises(AssertionError):
+            test_fp4_levels_from_e2m1_definition()
+    monkeypatch.setattr(qo, "e2m1_value", real_e2m1)
+
+    real_merge = qo.merge_weight
+
+    def via_fp32(Wdeq_bits, A_bits, B_bits, alpha, r):
+        s = np.float64(qo.lora_scale(alpha, r))
+        A = qo.bf16_to_f64(A_bits).reshape(r, -1)
+        B = qo.bf16_to_f64(B_bits).reshape(-1, r)
+        W = qo.bf16_to_f64(Wdeq_bits).reshape(B.shape[0], A.shape[1])
+        acc = np.zeros_like(W)
+        for j in range(r):
+            acc = acc + B[:, j:j + 1] * A[j:j + 1, :]
+        return qo.bf16_round(qo.f32(W + s * acc))
+
+    monkeypatch.setattr(o, "merge_weight", via_fp32)
+    with pytest.raises(AssertionError):
+        test_merge_weight_against_exact_rational_rounding()
+    monkeypatch.setattr(o, "merge_weight", real_merge)
+
+
 def test_bf16_weight_quantization_is_the_widened_fp32_quantization():
     """A bf16 weight quantizes as the fp32 number it widens to: known bit
     patterns decode to their values (1, -1, 0.5, the smallest subnormal, -0),
@@ -628,6 +724,72 @@ def test_merge_weight_special_cases_and_exact_sums():
         for k in range(K):
             v = Fraction(W[n, k]) + s * sum(Fraction(B[n, j]) * Fraction(A[j, k]) for j in range(r))
             assert got[n, k] == _bf16_rne_exact(v), (n, k)
+
+
+def _bf16_tie_distance(v):
+    """Distance of the rational v from the nearest bf16 rounding midpoint."""
+    import math
+    a = abs(Fraction(v))
+    if a == 0:
+        return Fraction(1)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, -126) - 7)
+    q = a / ulp
+    return abs((q - math.floor(q)) - Fraction(1, 2)) * ulp
+
+
+def _merge_exact(Wb, Ab, Bb, alpha, r):
+    """bf16 bits of W + s sum_j B A in rational arithmetic, one rounding, with a
+    mask of the elements that lie within 2^-40 (relative) of a bf16 midpoint."""
+    W, A, B = (o.bf16_to_f64(x) for x in (Wb, Ab, Bb))
+    s = Fraction(o.lora_scale(alpha, r))
+    N, K = W.shape
+    out = np.zeros((N, K), np.uint16)
+    near = np.zeros((N, K), bool)
+    for n in range(N):
+        for k in range(K):
+            v = Fraction(W[n, k]) + s * sum(Fraction(B[n, j]) * Fraction(A[j, k]) for j in range(r))
+            out[n, k] = _bf16_rne_exact(v)
+            near[n, k] = _bf16_tie_distance(v) <= Fraction(2) ** -40 * abs(v)
+    return out, near
+
+
+def test_merge_weight_against_exact_rational_rounding():
+    """merge_weight on random bf16 operands whose sums are not exact in fp64
+    (s = fp32(16/6) is not a power of two) equals W + s B A computed in
+    rational arithmetic and rounded once to bf16, except where the exact value
+    lies within 2^-40 of a bf16 midpoint (there the fp64 summation order may
+    decide); and on operands built to sit just off a midpoint, where rounding
+    through fp32 first would land on the midpoint and round the other way."""
+    rng = np.random.default_rng(21)
+
+    def bf(x):
+        return o.bf16_round(np.asarray(x, np.float32))
+
+    N, K, r, alpha = 12, 64, 6, 16.0
+    Wb = bf(rng.standard_normal((N, K)) * 0.02)
+    Ab = bf(rng.standard_normal((r, K)) / K)
+    Bb = bf(rng.standard_normal((N, r)) * 0.01)
+    got = o.merge_weight(Wb, Ab, Bb, alpha, r)
+    exp, near = _merge_exact(Wb, Ab, Bb, alpha, r)
+    assert int(near.sum()) < N * K // 100
+    assert np.array_equal(got[~near], exp[~near])
+
+    # s = 1 (alpha = r = 2): W = +-1, B A = 2^-8 + 2^-30 (just above the
+    # midpoint between 1 and 1 + 2^-7), exactly 2^-8 (a tie: to even), 3 2^-8
+    # (a tie: to even, upwards), and 2^-8 - 2^-30 (just below)
+    one, e8, e15 = 0x3F80, 0x3B80, 0x3800
+    Wb = np.array([[one] * 4, [0xBF80] * 4], np.uint16)
+    Ab = np.array([[0x3F80, 0x3F80, 0x4040, 0x3F80], [e15, 0, 0, 0xB800]], np.uint16)
+    Bb = np.array([[e8, e15], [0xBB80, 0xB800]], np.uint16)
+    got = o.merge_weight(Wb, Ab, Bb, 2.0, 2)
+    exp, near = _merge_exact(Wb, Ab, Bb, 2.0, 2)
+    # columns 1 and 2 are exact midpoints; every sum here is exact in fp64
+    assert not near[:, [0, 3]].any() and near[:, [1, 2]].all()
+    assert list(exp[0]) == [0x3F81, 0x3F80, 0x3F82, 0x3F80]
+    assert np.array_equal(got, exp)
 
 
 # ---------------------------------------------------------------- the parity tolerance itself
