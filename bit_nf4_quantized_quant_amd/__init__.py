@@ -13,7 +13,8 @@ import dataclasses
 from . import _lib
 from ._lib import (QLoraError, lib, qlora_double_quant, qlora_double_quant_workspace,  # noqa: F401
                    qlora_linear_bwd, qlora_linear_bwd_workspace, qlora_linear_fwd,
-                   qlora_linear_fwd_workspace, qlora_merge, qlora_nf4_dequant, qlora_nf4_levels,
+                   qlora_linear_fwd_wait_counter_offset, qlora_linear_fwd_workspace, qlora_merge,
+                   qlora_nf4_dequant, qlora_nf4_levels,
                    qlora_nf4_quantize, qlora_nf4_quantize_bf16, qlora_nf4_sizes)
 
 
@@ -98,10 +99,30 @@ def merge(q: QuantizedWeight, A, B, alpha: float, stream=None):
 
 
 def fwd_workspace(M: int, N: int, K: int, r: int, device):
-    """A zero-filled forward workspace (the kernels leave it zero-filled after each call)."""
+    """A forward workspace, zero-filled as the library requires before its first
+    use.  The kernels keep launch counters and partial sums in it between calls,
+    so after a call it is not zero: reuse it as it is (any shapes it is large
+    enough for), and do not write to it except to clear the wait counter."""
     import torch
     n = max(qlora_linear_fwd_workspace(M, N, K, r), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def fwd_wait_count(workspace) -> int:
+    """The forward workspace's wait counter (qlora_linear_fwd_wait_counter_offset):
+    how many lanes of decode-size launches (M <= 16) gave up waiting for the
+    launch's LoRA-down products and computed them themselves.  Results stay
+    correct either way; nonzero means the slow fallback ran.  Synchronizes
+    with the device (the read is a device-to-host copy)."""
+    import torch
+    off = qlora_linear_fwd_wait_counter_offset()
+    return int(workspace[off:off + 4].view(torch.int32).item())
+
+
+def clear_fwd_wait_count(workspace) -> None:
+    """Zero the forward workspace's wait counter (a 4-byte fill on the current stream)."""
+    off = qlora_linear_fwd_wait_counter_offset()
+    workspace[off:off + 4].zero_()
 
 
 def linear_fwd(X, q: QuantizedWeight, A, B, alpha: float, workspace=None, want_h: bool = True, stream=None):

@@ -36,6 +36,7 @@ SIGNATURES = {
     "qlora_linear_fwd_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "qlora_linear_fwd": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _i64, _f, _p,
                                         _p, _p, _sz, _p]),
+    "qlora_linear_fwd_wait_counter_offset": (_sz, []),
     "qlora_linear_bwd_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "qlora_linear_bwd": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _i64, _f,
                                         _p, _p, _p, _p, _p, _sz, _p]),
@@ -160,6 +161,10 @@ def qlora_linear_fwd(X, codes, c2, c1, mean, A, B, alpha: float, Y, H_out, works
                                   _ptr(B), r, float(alpha), _ptr(Y), _ptr(H_out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "qlora_linear_fwd")
+
+
+def qlora_linear_fwd_wait_counter_offset() -> int:
+    return lib().qlora_linear_fwd_wait_counter_offset()
 
 
 def qlora_linear_bwd_workspace(M: int, N: int, K: int, r: int) -> int:

@@ -10,6 +10,7 @@
 
 namespace qlora {
 size_t decode_workspace_bytes(int64_t M, int64_t r);
+size_t decode_wait_counter_offset();
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s);
 size_t gemm_fwd_scratch_bytes(int64_t M, int64_t N, int64_t K);
@@ -28,6 +29,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;     // elements of any one tenso
 constexpr int64_t kDecodeMaxM = 16;
 constexpr int64_t kMaxRowLen = int64_t(1) << 23;        // K, N: 256 rows of a tile within 4 GiB
 constexpr int64_t kMaxWeightBytes = int64_t(1) << 32;   // packed codes of one weight
+constexpr int64_t kMaxGridRows = int64_t(65535) * 128;  // M, N: 128-row tiles along a grid's y axis
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -44,6 +46,8 @@ int check_layer(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return QLORA_ESHAPE;
   // the products address a tile's rows and the packed weight with 32-bit offsets
   if (K >= kMaxRowLen || N >= kMaxRowLen || N * K / 2 >= kMaxWeightBytes) return QLORA_ESHAPE;
+  // the LoRA products launch 128-row tiles of M and of N along a grid's y axis
+  if (M > kMaxGridRows || N > kMaxGridRows) return QLORA_ESHAPE;
   return QLORA_OK;
 }
 
@@ -214,6 +218,8 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
   }
   return status_of(launch_gemm_fwd(a, scratch, s));
 }
+
+size_t qlora_linear_fwd_wait_counter_offset(void) { return decode_wait_counter_offset(); }
 
 size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (check_layer(M, N, K, r)) return 0;

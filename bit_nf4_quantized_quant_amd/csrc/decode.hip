@@ -302,16 +302,23 @@ __device__ void weight_tile(const DecodeParams& p, int tile, char* lut, uint32_t
   __syncthreads();
 
   // this launch's LoRA-down partials (tag = epoch + 1), polled until present
+  // or, past the deadline, computed here
   const uint32_t tag = *tag_lds;
+  uint64_t deadline = 0;   // set at the first miss
 #pragma unroll
   for (int u = 0; u < kHPer; ++u) {
     const int i = threadIdx.x + u * kThreads;
     if (i < mr) {
       const int m = i / p.r, j = i - m * p.r;
       float h = 0.f;
+      bool got = true;
 #pragma unroll
-      for (int ks = 0; ks < kHSplit; ++ks)
-        h += poll_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j], hp[u][ks], tag, p.ws);
+      for (int ks = 0; ks < kHSplit; ++ks) {
+        float v = 0.f;
+        got = got && poll_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j], hp[u][ks], tag, deadline, &v);
+        h += v;
+      }
+      if (!got) h = lane_lora_down(p.X, p.A, p.K, m, j, p.ws);
       *spare(lut, kHsOff + m * 128 + j) = h;
       if (tile == 0 && p.H) p.H[i] = h;
     }
@@ -409,6 +416,7 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
 }  // namespace dec
 
 size_t decode_workspace_bytes(int64_t M, int64_t r) { return dec::decode_workspace_bytes(M, r); }
+size_t decode_wait_counter_offset() { return (size_t)dec::kGiveupCounter; }
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) { return dec::launch_decode_fwd(a, s); }
 
 }  // namespace qlora

@@ -9,8 +9,11 @@
 // which compute H = X A^T in parts and publish them; they never wait.  The
 // remaining workgroups are weight tiles, which stream the NF4 codes, wait
 // (bounded spin) for this launch's H, add s H B^T in fp32 and store bf16 Y.
-// Workgroups are dispatched in index order, so the LoRA-down tiles are
-// running or done before any weight tile waits.
+// Workgroups are dispatched in index order on this hardware, so the
+// LoRA-down tiles are running or done before any weight tile waits; nothing
+// depends on that for correctness: a wait that reaches its deadline (about
+// 1 ms) gives up, the waiting lane computes its H value itself from X and A,
+// and a give-up counter in the workspace records it for the caller.
 //
 // Launch epochs: every launch adds exactly 2^20 to each of the counters of a
 // group, however many workgroups share a counter, so a workgroup's own
@@ -24,7 +27,7 @@
 // weight stream.
 //
 // Workspace layout (bytes): [128*(1+s)] weight counter s (u64, s < 8),
-// [128*9] timeout flag (u32), [128*(10+s)] LoRA-down counter s (u64, s < 8),
+// [128*9] give-up counter (u32), [128*(10+s)] LoRA-down counter s (u64, s < 8),
 // [kHpartOff..] tagged partial sums (u64: tag << 32 | fp32 bits).  Counters
 // sit 128 bytes apart so that their atomics do not queue on one cache line.
 #pragma once
@@ -41,9 +44,12 @@ constexpr int kRows = 16;          // output rows per weight tile
 constexpr int kHSplit = 4;         // K slices per LoRA-down row group
 constexpr int kSlots = 8;          // weight-tile epoch counters
 constexpr uint64_t kEpoch = uint64_t(1) << 20;
-constexpr unsigned kSpinLimit = 1u << 20;  // ~50 ms per polled word, a safety net only
+// Deadline of a weight tile's wait for the LoRA-down products, in ticks of
+// the 100 MHz real-time counter (1 ms; the products normally arrive within a
+// few microseconds of the launch).
+constexpr uint64_t kWaitTicks = 100000;
 constexpr size_t kHpartOff = 4096;
-constexpr int kTimeoutFlag = 128 * 9;
+constexpr int kGiveupCounter = 128 * 9;
 
 struct DecodeParams {
   const uint16_t* X;
@@ -129,22 +135,54 @@ __device__ __forceinline__ uint64_t take_down_ticket(const DecodeParams& p, int 
   return take_slot_ticket(p.ws, kDownCtr, (uint32_t)tile, (uint32_t)p.n_htiles);
 }
 
+__device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memrealtime(); }
+
 // Polls a tagged partial until it carries `tag` (first: the word already
-// read); returns its value.  The spin is bounded: past the limit the timeout
-// flag is raised and whatever was read last is used.
-__device__ __forceinline__ float poll_tagged(const uint64_t* src, uint64_t first, uint32_t tag, char* ws) {
+// read) and stores its value in *out.  The lane's deadline (0 = not yet set)
+// is set at its first miss; returns false, leaving *out alone, once the
+// real-time counter passes it.
+// (The poll count is bounded too, at kMaxPolls reads per word, each at
+// least one memory round trip.)
+constexpr unsigned kMaxPolls = 1u << 16;
+__device__ __forceinline__ bool poll_tagged(const uint64_t* src, uint64_t first, uint32_t tag, uint64_t& deadline,
+                                            float* out) {
   uint64_t v = first;
-  unsigned spins = 0;
+  unsigned polls = 0;
   while ((uint32_t)(v >> 32) != tag) {
+    const uint64_t now = realtime();
+    if (deadline == 0)
+      deadline = now + kWaitTicks;
+    else if (now > deadline || ++polls > kMaxPolls)
+      return false;
     __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) {
-      __hip_atomic_store(reinterpret_cast<unsigned*>(ws + kTimeoutFlag), 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
     v = ld_tagged(src);
   }
-  return __uint_as_float((uint32_t)v);
+  *out = __uint_as_float((uint32_t)v);
+  return true;
+}
+
+// H[m][j] = sum_k X[m][k] A[j][k] by one lane, for a wait that gave up: the
+// same fp32 sums of bf16 pair products the LoRA-down tiles form (in another
+// order), and one count on the workspace's give-up counter.
+__device__ __attribute__((noinline)) float lane_lora_down(const uint16_t* X, const uint16_t* A, int K, int m, int j,
+                                                        char* ws) {
+  __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(ws + kGiveupCounter), 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  const rsrc_t rx = make_rsrc(X + (size_t)m * K, (uint32_t)K * 2);
+  const rsrc_t ra = make_rsrc(A + (size_t)j * K, (uint32_t)K * 2);
+  float acc = 0.f;
+  for (int k = 0; k < K; k += 8) {
+    const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)k * 2, 0, 0));
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)k * 2, 0, 0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t xq = x[q], aq = a[q];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short __attribute__((ext_vector_type(2))), aq),
+                                            __builtin_bit_cast(short __attribute__((ext_vector_type(2))), xq), acc,
+                                            false);
+    }
+  }
+  return acc;
 }
 
 // The weight's mean (read-only during a launch) through the scalar cache: a

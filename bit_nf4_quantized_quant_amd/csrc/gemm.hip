@@ -26,7 +26,10 @@
 // A transposed source is read as 4 x 8 patches (4 rows of 8 contiguous
 // elements) and written to LDS as 8 rows of 4 reduction elements.
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -1129,25 +1132,12 @@ size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r) {
   return splits == 1 ? 0 : (size_t)splits * M * r * sizeof(float);
 }
 
-// Launch a tiled kernel with dynamic LDS (raising the per-kernel limit once).
+// Launch a tiled kernel with dynamic LDS (its limit raised once per device).
 template <class Kern, class P>
 hipError_t launch_tiled(Kern kern, int threads, size_t lds, int mtiles, int ntiles, int splits, P& p,
                         hipStream_t s) {
-  // the LDS limit is raised once per kernel (several kernels can share this
-  // instantiation: remember which ones; setting it twice is harmless)
-  static const void* done[8] = {};
-  const void* kp = reinterpret_cast<const void*>(kern);
-  bool seen = false;
-  for (const void* d : done) seen = seen || d == kp;
-  if (!seen) {
-    hipError_t e = hipFuncSetAttribute(kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    for (const void*& d : done)
-      if (!d) {
-        d = kp;
-        break;
-      }
-  }
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds);
+  if (e != hipSuccess) return e;
   p.mtiles = mtiles;
   p.ntiles = ntiles;
   p.gm = mtiles >= 8 ? mtiles / 8 : 1;
@@ -1184,17 +1174,35 @@ size_t gemm_fwd_scratch_bytes(int64_t M, int64_t N, int64_t K) {
   return g.splits > 1 ? (size_t)g.splits * M * N * sizeof(float) : 0;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; thread-safe).
 int cu_count() {
-  static int cus[64] = {};
+  static std::mutex mu;
+  static std::map<int, int> cus;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cus.find(dev);
+  if (it != cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cus[dev] = n;
+  return n;
+}
+
+// Raises `kernel`'s dynamic-LDS limit to at least `bytes` on the current
+// device, once per (device, kernel, size) (thread-safe).
+hipError_t ensure_lds_limit(const void* kernel, size_t bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> raised;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = raised[{dev, kernel}];
+  if (have >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
 }
 
 // The forward product over output columns [n0, n0 + nn) of the layer (rows n0..

@@ -292,13 +292,16 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
 
   if (lora) {
     const uint32_t tag = *tag_lds;
+    uint64_t deadline = 0;   // set at the first miss
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int j = lane + 64 * h;
       if (j >= p.r) continue;
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float hval = poll_tagged(&p.Hpart[(size_t)m * r16 + j], hv[m][h], tag, p.ws);
+        float hval;
+        if (!poll_tagged(&p.Hpart[(size_t)m * r16 + j], hv[m][h], tag, deadline, &hval))
+          hval = lane_lora_down(p.X, p.A, p.K, m, j, p.ws);
         if (tile == 0 && grp == 0 && p.H) p.H[m * p.r + j] = hval;
         const float sh = p.scale * hval;
 #pragma unroll

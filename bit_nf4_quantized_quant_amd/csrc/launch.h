@@ -8,6 +8,12 @@
 
 namespace qlora {
 
+// Compute units of the current device (cached per device).
+int cu_count();
+// Raises a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device, once per device and kernel.
+hipError_t ensure_lds_limit(const void* kernel, size_t bytes);
+
 // table: the code table (0 NF4, 1 uniform 4-bit, 2 FP4; checked by the caller)
 hipError_t launch_nf4_quantize(const float* W, int64_t N, int64_t K, int table, uint8_t* codes, float* absmax,
                                hipStream_t s);

@@ -84,18 +84,26 @@ Nf4Table build_uniform4() {
   return t;
 }
 
-// FP4: the 4-bit float with 2 exponent and 1 mantissa bits (magnitudes 0,
-// 0.5, 1, 1.5, 2, 3, 4, 6), scaled by 1/6 to span [-1, 1] like the other
-// tables; its two zeros are codes 7 and 8 (both +0), so code 7 stays the zero
-// level.  The pages name FP4 (irregular6612 "QLoRA - Efficient Finetuning of
-// Quantized LLMs"; itwiki "QLoRA": bitsandbytes' default 4-bit type) but give
-// no grid: this one is a reading.
+// FP4: the 4-bit float E2M1 -- sign, 2 exponent bits with bias 1, 1
+// mantissa bit, subnormals at exponent field 0, no infinity or NaN -- with
+// every magnitude pattern 0..7 decoded as its significand (in halves) times a
+// power of two, scaled by the largest magnitude (6) to span [-1, 1] like the
+// other tables.  Ascending order puts -0 and +0 at codes 7 and 8; both are
+// stored as +0, so code 7 stays the zero level.  The pages name FP4
+// (irregular6612 "QLoRA - Efficient Finetuning of Quantized LLMs"; itwiki
+// "QLoRA": bitsandbytes' default 4-bit type) but give no grid: this one is a
+// reading.
 Nf4Table build_fp4() {
-  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double mag[8];
+  for (int c = 0; c < 8; ++c) {
+    const int e = c >> 1, m = c & 1;
+    // subnormal: m/2 * 2^(1-1); normal: (2 + m)/2 * 2^(e-1)
+    mag[c] = e == 0 ? std::ldexp((double)m, -1) : std::ldexp((double)(2 + m), e - 2);
+  }
   Nf4Table t;
   for (int i = 0; i < 8; ++i) {
-    t.level[7 - i] = i == 0 ? 0.0f : (float)(-mag[i] / 6.0);
-    t.level[8 + i] = (float)(mag[i] / 6.0);
+    t.level[7 - i] = i == 0 ? 0.0f : (float)(-mag[i] / mag[7]);
+    t.level[8 + i] = (float)(mag[i] / mag[7]);
   }
   set_thresholds(t);
   return t;

@@ -351,14 +351,10 @@ hipError_t launch_nf4_merge(const uint8_t* codes, const uint8_t* c2, const float
                             hipStream_t st) {
   const dim3 grid((unsigned)(K / kMgCols), (unsigned)((N + kMgRows * kMgChunks - 1) / (kMgRows * kMgChunks)));
   const size_t lds = (size_t)(r * kMgCols + kMgRows * (r + 1)) * sizeof(float);
-  static bool raised = false;   // the limit is raised once, for r = kMgMaxR
-  if (!raised) {
-    const size_t max_lds = (size_t)(kMgMaxR * kMgCols + kMgRows * (kMgMaxR + 1)) * sizeof(float);
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(nf4_merge_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
-    if (e != hipSuccess) return e;
-    raised = true;
-  }
+  // the limit is raised once per device, for r = kMgMaxR
+  const size_t max_lds = (size_t)(kMgMaxR * kMgCols + kMgRows * (kMgMaxR + 1)) * sizeof(float);
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(nf4_merge_kernel), max_lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(nf4_merge_kernel, grid, dim3(256), lds, st, codes, c2, c1, mean, N, K, A, B, (int)r, s, out,
                      code_table(table));
   return hipGetLastError();

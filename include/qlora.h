@@ -23,9 +23,12 @@
  *     workspaces sized by the *_workspace helpers).  The library never
  *     allocates, frees or synchronizes; it validates arguments on the host and
  *     queues kernels on `stream` (a hipStream_t; NULL = the null stream).
- *   - Return value: QLORA_OK or an error code.  On an error nothing has been
- *     queued.  Faults inside kernels surface at the caller's next
- *     synchronization, as for any HIP kernel.
+ *   - Return value: QLORA_OK or an error code.  Every argument and shape check
+ *     runs before the first launch, so on QLORA_EINVAL or QLORA_ESHAPE nothing
+ *     has been queued.  QLORA_EHIP reports a launch the HIP runtime refused;
+ *     kernels of the same call queued before it may already be on the stream,
+ *     and the call's outputs are then unspecified.  Faults inside kernels
+ *     surface at the caller's next synchronization, as for any HIP kernel.
  *   - Inputs must be finite; non-finite inputs give unspecified results.
  *   - Zero-sized problems (N, M or K equal to 0, as allowed per entry point)
  *     are accepted; they queue nothing except where an output is a sum over
@@ -33,9 +36,11 @@
  *   - Alignment: pointers to fp32/bf16 matrices and to the packed codes must be
  *     16-byte aligned; absmax, c1, mean and H need 4-byte alignment; c2 and B
  *     need only their natural alignment.
- *   - Calls are thread-safe and keep no state between calls, except the
- *     launch counters the forward keeps in its workspace.  Two calls that
- *     share a workspace must not run concurrently.
+ *   - Calls may be made from several host threads at once (the library's only
+ *     host-side state, per-device caches of the CU count and of raised kernel
+ *     LDS limits, is guarded by a mutex).  The forward keeps launch counters
+ *     in its workspace between calls; two calls that share a workspace must
+ *     not run concurrently on the device.
  *
  * Storage of one quantized weight W [N,K] (P = N*K, K % 64 == 0):
  *   codes  uint8 [N, K/2]       code of element 2i in the low nibble of byte i,
@@ -199,14 +204,29 @@ size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  *                                256-B aligned, zero-filled once before its first
  *                                use.  The library keeps launch counters in it
  *                                between calls (any shapes may share one workspace
- *                                as long as it is large enough); do not modify it,
- *                                and zero it again after a call that faulted.
- * Requires K % 64 == 0.
+ *                                as long as it is large enough); do not modify it
+ *                                (except the wait counter below), and zero it again
+ *                                after a call that faulted.  Its contents after a
+ *                                call are not zero.
+ * Requires K % 64 == 0; M and N at most 65535 * 128.
  */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
                      const uint8_t* c2, const float* c1, const float* mean, int table, const uint16_t* A,
                      const uint16_t* B, int64_t r, float alpha, uint16_t* Y, float* H_out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Byte offset, inside the forward workspace, of a uint32 counter.  For
+ * M <= 16 one launch computes H = X A^T in some workgroups while the others
+ * stream the weight and then wait, up to about 1 ms, for H; a wait that
+ * reaches that deadline gives up, the waiting lanes compute their H values
+ * themselves from X and A (Y and H_out stay correct), and the counter goes up
+ * by one per lane that did so.  A nonzero count therefore means a launch ran
+ * that slow fallback, e.g. because other work held the compute units.  The
+ * library never resets the counter; the caller may zero these 4 bytes
+ * between calls (read them after synchronizing the stream).
+ */
+size_t qlora_linear_fwd_wait_counter_offset(void);
 
 /* Workspace bytes needed by qlora_linear_bwd. */
 size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
@@ -226,6 +246,7 @@ size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
  *   Empty sums give zeros: M = 0 writes dA = dB = 0; N = 0 writes dX = dA = 0
  *   workspace  qlora_linear_bwd_workspace(M,N,K,r) bytes, 256-B aligned
  *              (contents on entry do not matter)
+ * Requires K % 64 == 0; M and N at most 65535 * 128.
  */
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t N, int64_t K,
                      const uint8_t* codes, const uint8_t* c2, const float* c1, const float* mean, int table,

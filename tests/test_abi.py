@@ -31,7 +31,7 @@ def _declared():
 
 def test_header_declarations_are_exported():
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -152,10 +152,24 @@ def test_fwd_validation():
     assert _fwd(L, H=A16 + 2) == _lib.QLORA_EINVAL
     assert _fwd(L, M=0, X=None, Y=None) == _lib.QLORA_OK     # empty batch queues nothing
     assert _fwd(L, N=0) == _lib.QLORA_OK
+    # M and N beyond 65535 * 128 rows are rejected before any launch
+    assert _fwd(L, M=65535 * 128 + 1) == _lib.QLORA_ESHAPE
+    assert _fwd(L, N=65535 * 128 + 1) == _lib.QLORA_ESHAPE
     assert L.qlora_linear_fwd_workspace(4, 64, 96, 8) == 0   # invalid shapes report 0
     # decode-sized and large batches both need a workspace
     assert L.qlora_linear_fwd_workspace(1, 4096, 4096, 64) > 256
     assert L.qlora_linear_fwd_workspace(4096, 22016, 8192, 64) >= 4096 * 64 * 4
+
+
+def test_fwd_wait_counter_inside_every_forward_workspace():
+    """The wait counter is a 4-byte word at a fixed offset that every forward
+    workspace covers (decode-size and tiled shapes alike)."""
+    L = _lib.lib()
+    off = _lib.qlora_linear_fwd_wait_counter_offset()
+    assert off % 4 == 0
+    for shape in ((1, 64, 64, 0), (1, 4096, 4096, 64), (16, 11008, 4096, 64), (17, 64, 64, 1),
+                  (4096, 22016, 8192, 64)):
+        assert L.qlora_linear_fwd_workspace(*shape) >= off + 4, shape
 
 
 def test_bwd_validation():

@@ -271,9 +271,14 @@ def oracle_layer(d, alpha, r):
 
 
 def run_fwd(d, q, alpha, r, ws=None):
+    """One forward; also checks that no bounded wait of the launch gave up."""
     X, A, B = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"])
+    if ws is None:
+        ws = qa.fwd_workspace(X.shape[0], q.N, q.K, r, "cuda")
+    before = qa.fwd_wait_count(ws)
     Y, H = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)
     torch.cuda.synchronize()
+    assert qa.fwd_wait_count(ws) == before, "a wait for the LoRA-down products gave up"
     return Y, H
 
 
@@ -375,8 +380,94 @@ def test_forward_deterministic_and_workspace_reusable():
                 assert (H is None) == (r == 0)
                 if r:
                     assert torch.equal(H, first[key][1]), key
-    # the decode kernel's bounded wait never timed out
-    assert int(ws[128 * 9:128 * 9 + 4].view(torch.int32)[0]) == 0
+    # the decode kernels' bounded waits never gave up
+    assert qa.fwd_wait_count(ws) == 0
+
+
+def test_forward_graph_replay_matches_oracle_and_eager():
+    """The mode the benchmark times: many forwards captured in one HIP graph,
+    rotating over weight copies, all sharing one workspace.  52 calls (M = 1,
+    4, 16 and 64 interleaved, 4 weight copies, each call its own X and Y),
+    replayed three times with eager work and synchronizations between the
+    replays; every Y of every replay equals the eager result bit for bit and
+    meets the tolerance against the oracle, and no wait gave up."""
+    N, K, r, alpha, copies = 1024, 1024, 16, 16.0, 4
+    layers = []
+    for c in range(copies):
+        d = synth.make_layer(synth.LayerShape("t", M=1, N=N, K=K, r=r, seed_offset=4400 + c))
+        _, wd = oracle_layer(d, alpha, r)
+        layers.append((d, wd, gpu_quantize(d["W"]), dev_bf16(d["A"]), dev_bf16(d["B"])))
+    Ms = (1, 4, 16, 64)
+    calls = []
+    for i in range(52):
+        M = Ms[i % 4]
+        xb = synth.f32_to_bf16_bits(synth.normal_f32(5000 + i, (M, K), 1.0))
+        calls.append((i % copies, xb, dev_bf16(xb), torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    ws = qa.fwd_workspace(64, N, K, r, "cuda")
+
+    def run_all():
+        for c, _, X, Y in calls:
+            _, _, q, A, B = layers[c]
+            qa.qlora_linear_fwd(X, q.codes, q.c2, q.c1, q.mean, A, B, alpha, Y, None, ws, N)
+
+    run_all()                                   # eager reference
+    torch.cuda.synchronize()
+    eager = [Y.clone() for *_, Y in calls]
+    for (c, xb, _, _), Ye in zip(calls, eager):
+        d, wd = layers[c][0], layers[c][1]
+        Yr, _ = oracle.linear_fwd(xb, wd, d["A"], d["B"], alpha, r)
+        check_close(bf16_f64(host_bf16_bits(Ye)), Yr, f"Y eager copy {c} M={xb.shape[0]}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run_all()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for *_, Y in calls:
+            Y.fill_(0)                          # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((c, xb, _, Y), Ye) in enumerate(zip(calls, eager)):
+            assert torch.equal(Y.view(torch.int16), Ye.view(torch.int16)), (rep, i)
+    assert qa.fwd_wait_count(ws) == 0
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_forward_wait_gives_up_and_stays_correct(M):
+    """Forced from the host: the workspace's LoRA-down launch counters are set
+    5 launches ahead of the weight counters, so the weight workgroups never see
+    this launch's tag on the published H partials.  Every wait reaches its
+    deadline (about 1 ms), the waiting lanes compute H themselves, every kernel
+    ends normally, Y and H still match the oracle, and the wait counter says
+    the fallback ran.  (Counter layout: eight 64-bit LoRA-down counters 128
+    bytes apart from byte 1280 of the workspace.)"""
+    N, K, r, alpha = 512, 1024, 16, 16.0
+    d = synth.make_layer(synth.LayerShape("t", M=M, N=N, K=K, r=r, seed_offset=4500 + M))
+    _, wd = oracle_layer(d, alpha, r)
+    q = gpu_quantize(d["W"])
+    X, A, B = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"])
+    ws = qa.fwd_workspace(M, N, K, r, "cuda")
+    Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], alpha, r)
+    Y, H = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)     # one consistent launch first
+    torch.cuda.synchronize()
+    assert qa.fwd_wait_count(ws) == 0
+    for s in range(8):
+        ctr = ws[1280 + 128 * s:1280 + 128 * s + 8].view(torch.int64)
+        ctr += 5 << 20
+    torch.cuda.synchronize()
+    say(f"[wait give-up] M={M}: launching with desynchronized counters")
+    for rep in range(2):
+        Y, H = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)
+        torch.cuda.synchronize()
+        check_close(bf16_f64(host_bf16_bits(Y)), Yr, f"Y after give-up, launch {rep}")
+        check_close(host(H), Hr, f"H after give-up, launch {rep}")
+    assert qa.fwd_wait_count(ws) > 0
+    qa.clear_fwd_wait_count(ws)
+    torch.cuda.synchronize()
+    assert qa.fwd_wait_count(ws) == 0
 
 
 @pytest.mark.parametrize("shape", synth.DECODE, ids=lambda sh: sh.name)
