@@ -56,6 +56,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+CALIB_SOURCE = "calib.hip"
+CALIB_PATH = os.path.join(PKG, "libqlora_calib.so")
+
+
+def build_calib(verbose: bool = False) -> str:
+    """The benchmark's reference kernels (empty kernel, plain streaming read),
+    linked separately from the layer's library as libqlora_calib.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = _compile(CALIB_SOURCE, verbose)
+    tmp = CALIB_PATH + ".tmp"
+    res = subprocess.run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", obj, "-o", tmp],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, CALIB_PATH)
+    return CALIB_PATH
+
+
 def build_library(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link libqlora.so next to this file."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -72,3 +90,4 @@ def build_library(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    print(build_calib(verbose="-v" in sys.argv))
