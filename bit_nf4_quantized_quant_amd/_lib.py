@@ -36,6 +36,8 @@ SIGNATURES = {
     "qlora_linear_fwd_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "qlora_linear_fwd": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _i64, _f, _p,
                                         _p, _p, _sz, _p]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _i64, _f,
+                                                _p, _p, _p]),
     "qlora_linear_fwd_wait_counter_offset": (_sz, []),
     "qlora_linear_bwd_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "qlora_linear_bwd": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _i64, _f,
@@ -161,6 +163,17 @@ def qlora_linear_fwd(X, codes, c2, c1, mean, A, B, alpha: float, Y, H_out, works
                                   _ptr(B), r, float(alpha), _ptr(Y), _ptr(H_out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "qlora_linear_fwd")
+
+
+def qlora_linear_fwd_noalloc(X, codes, c2, c1, mean, A, B, alpha: float, Y, H_out, N: int, stream=None,
+                             table: int = 0):
+    """qlora_linear_fwd with the library's static per-GPU scratch instead of a workspace."""
+    _need_cuda(X, codes, c2, c1, mean, A, B, Y, H_out)
+    M, K = X.shape
+    r = 0 if A is None else A.shape[0]
+    _check(lib().qlora_linear_fwd_noalloc(_ptr(X), M, N, K, _ptr(codes), _ptr(c2), _ptr(c1), _ptr(mean), table,
+                                          _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(H_out),
+                                          _stream(stream)), "qlora_linear_fwd_noalloc")
 
 
 def qlora_linear_fwd_wait_counter_offset() -> int:

@@ -3,6 +3,8 @@
 // rejected call touches neither the device nor the stream.
 #include <algorithm>
 #include <cstring>
+#include <map>
+#include <mutex>
 
 #include "../../include/qlora.h"
 #include "launch.h"
@@ -74,6 +76,77 @@ size_t fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   // and then by the main product's split-K partials
   const size_t scratch = std::max(lora_down_scratch_bytes(M, K, r), gemm_fwd_scratch_bytes(M, N, K));
   return kFwdReserved + round256((size_t)M * r * sizeof(float)) + round256(scratch);
+}
+
+// Checks of the forward's arguments other than its workspace.
+int check_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes, const uint8_t* c2,
+              const float* c1, const float* mean, int table, const uint16_t* A, const uint16_t* B, int64_t r,
+              const uint16_t* Y, const float* H_out) {
+  int st = check_layer(M, N, K, r);
+  if (!st && !table_ok(table)) st = QLORA_EINVAL;
+  if (st) return st;
+  if (K == 0) return QLORA_ESHAPE;
+  if (M == 0 || N == 0) return QLORA_OK;
+  if ((st = check_weight(codes, c2, c1, mean))) return st;
+  if (!X || !Y) return QLORA_EINVAL;
+  if (r > 0 && (!A || !B)) return QLORA_EINVAL;
+  if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(Y, 2)) return QLORA_EINVAL;
+  if (H_out && !aligned(H_out, 4)) return QLORA_EINVAL;
+  return QLORA_OK;
+}
+
+// The forward's launches over a workspace of at least fwd_ws(M, N, K, r) bytes.
+int launch_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes, const uint8_t* c2,
+               const float* c1, const float* mean, int table, const uint16_t* A, const uint16_t* B, int64_t r,
+               float alpha, uint16_t* Y, float* H_out, void* workspace, hipStream_t s) {
+  FwdArgs a;
+  a.X = X;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.r = r;
+  a.w = Nf4Weight{codes, c2, c1, mean, table};
+  a.A = A;
+  a.B = B;
+  a.scale = r > 0 ? alpha / (float)r : 0.f;
+  a.Y = Y;
+  a.H = r > 0 ? H_out : nullptr;
+  a.workspace = workspace;
+  if (use_decode(M, N, K)) return status_of(launch_decode_fwd(a, s));
+  char* ws = reinterpret_cast<char*>(workspace) + kFwdReserved;
+  float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
+  if (r > 0) {
+    float* H = H_out ? H_out : reinterpret_cast<float*>(ws);
+    a.H = H;
+    if (launch_lora_down(X, M, K, A, r, H, scratch, s) != hipSuccess) return QLORA_EHIP;
+  }
+  return status_of(launch_gemm_fwd(a, scratch, s));
+}
+
+// The no-allocation forward's scratch: a file-scope device array, one copy
+// per GPU, zero at load (the decode launch counters start consistent) and
+// kept between calls.  Host code uses it only through the device address
+// hipGetSymbolAddress gives for the current device, taken once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static_assert(kNoAllocScratchBytes == QLORA_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> ptrs;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    it = ptrs.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -181,42 +254,25 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
                      const float* c1, const float* mean, int table, const uint16_t* A, const uint16_t* B,
                      int64_t r, float alpha, uint16_t* Y, float* H_out, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  int st = check_layer(M, N, K, r);
-  if (!st && !table_ok(table)) st = QLORA_EINVAL;
-  if (st) return st;
-  if (K == 0) return QLORA_ESHAPE;
+  int st = check_fwd(X, M, N, K, codes, c2, c1, mean, table, A, B, r, Y, H_out);
+  if (st != QLORA_OK) return st;
   if (M == 0 || N == 0) return QLORA_OK;
-  if ((st = check_weight(codes, c2, c1, mean))) return st;
-  if (!X || !Y || !workspace) return QLORA_EINVAL;
-  if (r > 0 && (!A || !B)) return QLORA_EINVAL;
-  if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(Y, 2) || !aligned(workspace, 256))
-    return QLORA_EINVAL;
-  if (H_out && !aligned(H_out, 4)) return QLORA_EINVAL;
+  if (!workspace || !aligned(workspace, 256)) return QLORA_EINVAL;
   if (workspace_bytes < fwd_ws(M, N, K, r)) return QLORA_EINVAL;
+  return launch_fwd(X, M, N, K, codes, c2, c1, mean, table, A, B, r, alpha, Y, H_out, workspace,
+                    (hipStream_t)stream);
+}
 
-  FwdArgs a;
-  a.X = X;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.r = r;
-  a.w = Nf4Weight{codes, c2, c1, mean, table};
-  a.A = A;
-  a.B = B;
-  a.scale = r > 0 ? alpha / (float)r : 0.f;
-  a.Y = Y;
-  a.H = r > 0 ? H_out : nullptr;
-  a.workspace = workspace;
-  hipStream_t s = (hipStream_t)stream;
-  if (use_decode(M, N, K)) return status_of(launch_decode_fwd(a, s));
-  char* ws = reinterpret_cast<char*>(workspace) + kFwdReserved;
-  float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
-  if (r > 0) {
-    float* H = H_out ? H_out : reinterpret_cast<float*>(ws);
-    a.H = H;
-    if (launch_lora_down(X, M, K, A, r, H, scratch, s) != hipSuccess) return QLORA_EHIP;
-  }
-  return status_of(launch_gemm_fwd(a, scratch, s));
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                             const uint8_t* c2, const float* c1, const float* mean, int table, const uint16_t* A,
+                             const uint16_t* B, int64_t r, float alpha, uint16_t* Y, float* H_out, void* stream) {
+  int st = check_fwd(X, M, N, K, codes, c2, c1, mean, table, A, B, r, Y, H_out);
+  if (st != QLORA_OK) return st;
+  if (M == 0 || N == 0) return QLORA_OK;
+  if (fwd_ws(M, N, K, r) > kNoAllocScratchBytes) return QLORA_ESHAPE;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return QLORA_EHIP;
+  return launch_fwd(X, M, N, K, codes, c2, c1, mean, table, A, B, r, alpha, Y, H_out, ws, (hipStream_t)stream);
 }
 
 size_t qlora_linear_fwd_wait_counter_offset(void) { return decode_wait_counter_offset(); }

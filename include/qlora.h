@@ -215,6 +215,31 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
                      const uint16_t* B, int64_t r, float alpha, uint16_t* Y, float* H_out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the no-allocation forward's scratch, per GPU (16 MiB). */
+#define QLORA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing: its scratch (the
+ * decode path's launch counters and H partials, the tiled path's H and
+ * split-K partials) is a static device array of QLORA_NOALLOC_SCRATCH_BYTES
+ * inside the library, one copy per GPU, held until the process ends; its
+ * device address is looked up once per device, on the first call made with
+ * that device current.  Arguments, results and status codes are those of
+ * qlora_linear_fwd; a shape whose forward workspace
+ * (qlora_linear_fwd_workspace) exceeds QLORA_NOALLOC_SCRATCH_BYTES is
+ * rejected with QLORA_ESHAPE (every shape with M <= 16 fits, needing under
+ * 70 KiB; so does, e.g., M = 64 with N = K = 4096, r = 64, at 8 MiB).
+ * Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (concurrent streams, or host threads that
+ * use the same device) race and must not be made.  The scratch keeps the
+ * last call's contents; nothing in it needs clearing between calls.
+ */
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                             const uint8_t* c2, const float* c1, const float* mean, int table, const uint16_t* A,
+                             const uint16_t* B, int64_t r, float alpha, uint16_t* Y, float* H_out, void* stream);
+
 /*
  * Byte offset, inside the forward workspace, of a uint32 counter.  For
  * M <= 16 one launch computes H = X A^T in some workgroups while the others

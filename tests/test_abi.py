@@ -31,7 +31,7 @@ def _declared():
 
 def test_header_declarations_are_exported():
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -159,6 +159,28 @@ def test_fwd_validation():
     # decode-sized and large batches both need a workspace
     assert L.qlora_linear_fwd_workspace(1, 4096, 4096, 64) > 256
     assert L.qlora_linear_fwd_workspace(4096, 22016, 8192, 64) >= 4096 * 64 * 4
+
+
+def test_fwd_noalloc_validation():
+    """The no-allocation forward rejects bad arguments and shapes whose
+    workspace exceeds its 16 MiB scratch before any device call."""
+    L = _lib.lib()
+    f = L.qlora_linear_fwd_noalloc
+    base = dict(X=A16, M=4, N=64, K=64, codes=A16, c2=A16, c1=A16, mean=A16, table=0, A=A16, B=A16, r=8,
+                alpha=16.0, Y=A16, H=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["X"], a["M"], a["N"], a["K"], a["codes"], a["c2"], a["c1"], a["mean"], a["table"], a["A"],
+                 a["B"], a["r"], a["alpha"], a["Y"], a["H"], None)
+
+    assert call(K=96) == _lib.QLORA_ESHAPE
+    assert call(X=None) == _lib.QLORA_EINVAL
+    assert call(X=MIS) == _lib.QLORA_EINVAL
+    assert call(table=5) == _lib.QLORA_EINVAL
+    assert call(M=0, X=None, Y=None) == _lib.QLORA_OK           # empty batch: nothing queued
+    assert L.qlora_linear_fwd_workspace(256, 4096, 4096, 64) > (16 << 20)
+    assert call(M=256, N=4096, K=4096, r=64) == _lib.QLORA_ESHAPE
 
 
 def test_fwd_wait_counter_inside_every_forward_workspace():
