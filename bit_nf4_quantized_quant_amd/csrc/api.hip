@@ -6,7 +6,7 @@
 #include <map>
 #include <mutex>
 
-#include "../../include/qlora.h"
+#include "qlora.h"
 #include "launch.h"
 #include "nf4_table.h"
 

@@ -137,6 +137,14 @@ __device__ __forceinline__ uint64_t take_down_ticket(const DecodeParams& p, int 
 
 __device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
+// A workgroup-uniform value moved to a scalar register (integer division runs
+// on the vector unit), so that offsets derived from it stay scalar.
+__device__ __forceinline__ int uniform_int(int v) {
+  int r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+  return r;
+}
+
 // Polls a tagged partial until it carries `tag` (first: the word already
 // read) and stores its value in *out.  The lane's deadline (0 = not yet set)
 // is set at its first miss; returns false, leaving *out alone, once the

@@ -484,7 +484,7 @@ __device__ __forceinline__ void mma_tile(const lds_t* sa, const lds_t* sb, Acc<B
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc.c[i][j], 0, 0, 0);
   }
 }
 
@@ -540,7 +540,7 @@ __device__ __forceinline__ void mma_step_store(const lds_t* sa, const lds_t* sb,
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p & 1][i], fb[p & 1][j], acc.c[i][j], 0, 0, 0);
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[p & 1][j], fa[p & 1][i], acc.c[i][j], 0, 0, 0);
     la.template store_part<S, p>(da);
     lb.template store_part<S, p>(db);
   };
@@ -582,9 +582,13 @@ __device__ __forceinline__ void run_pipelined(LA& la, LB& lb, int kt0, int kt1, 
   }
 }
 
-// Lane l of a 32x32 accumulator holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4.
+// The products run with the weight-side fragment as the MFMA's first operand,
+// so a 32x32 accumulator holds the transposed tile: lane l has output row
+// l % 32 and, in register group g (values 4 g .. 4 g + 3), the four
+// consecutive output columns 8 g + 4 (l / 32) .. + 3, which leave as one
+// 8-byte (bf16) or 16-byte (fp32) store.
 template <int BM, int BN, int WN, class F>
-__device__ __forceinline__ void for_each_out(const Acc<BM, BN, WN>& acc, F f) {
+__device__ __forceinline__ void for_each_out4(const Acc<BM, BN, WN>& acc, F f) {
   constexpr int TM = Acc<BM, BN, WN>::TM, TN = Acc<BM, BN, WN>::TN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -593,11 +597,40 @@ __device__ __forceinline__ void for_each_out(const Acc<BM, BN, WN>& acc, F f) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = wn * (BN / WN) + j * 32 + (lane & 31);
-        f(row, col, acc.c[i][j][v]);
+      for (int g = 0; g < 4; ++g) {
+        const int row = wm * (BM / 2) + i * 32 + (lane & 31);
+        const int col = wn * (BN / WN) + j * 32 + 8 * g + 4 * (lane >> 5);
+        f(row, col, f32x4{acc.c[i][j][4 * g], acc.c[i][j][4 * g + 1], acc.c[i][j][4 * g + 2], acc.c[i][j][4 * g + 3]});
       }
+}
+
+// Four consecutive outputs (row m, columns n .. n + 3) of a row-major matrix
+// with row stride ld: one vector store when `vec` (the four are 8- or 16-byte
+// aligned whenever n % 4 == 0) and all four are inside [M, N), else one store
+// per element inside the extent.
+__device__ __forceinline__ void store4_bf16(uint16_t* base, int64_t ld, int64_t m, int64_t n, int64_t M, int64_t N,
+                                            const f32x4& v, bool vec) {
+  if (m >= M) return;
+  uint16_t* q = base + m * ld + n;
+  if (vec && n + 3 < N) {
+    *reinterpret_cast<u32x2*>(q) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (n + e < N) q[e] = (uint16_t)(pack_bf16x2(v[e], 0.f) & 0xFFFFu);
+}
+__device__ __forceinline__ void store4_f32(float* base, int64_t ld, int64_t m, int64_t n, int64_t M, int64_t N,
+                                           const f32x4& v, bool vec) {
+  if (m >= M) return;
+  float* q = base + m * ld + n;
+  if (vec && n + 3 < N) {
+    *reinterpret_cast<f32x4*>(q) = v;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (n + e < N) q[e] = v[e];
 }
 
 template <int BM, int BN, int WN>
@@ -637,7 +670,7 @@ __device__ __forceinline__ void lora_tail(Acc<BM, BN, WN>& acc, int kr, FA fa, F
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc.c[i][j], 0, 0, 0);
   }
 }
 
@@ -728,6 +761,7 @@ struct FwdGemmParams {
   float scale;
   uint16_t* Y;
   int64_t ldy;          // elements between rows of Y (N, or more for a column range)
+  bool y_vec;           // Y 8-byte aligned and ldy % 4 == 0: four outputs per store
   float* part;          // split-K partials [splits][M][N] (splits > 1, ldy = N)
   int splits, steps_per_split;
   int mtiles, ntiles, gm;
@@ -765,15 +799,13 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
         [&](int i, int k0) { return frag_f32_row(p.H, p.r, m0 + i, p.M, k0, p.r, p.scale); },
         [&](int j, int k0) { return frag_bf16_row(p.B, p.r, n0 + j, p.N, k0, p.r, p.b_vec); });
   if (p.splits == 1) {
-    for_each_out(acc, [&](int i, int j, float v) {
-      const int64_t m = m0 + i, n = n0 + j;
-      if (m < p.M && n < p.N) p.Y[m * p.ldy + n] = to_bf16(v);
+    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+      store4_bf16(p.Y, p.ldy, m0 + i, n0 + j, p.M, p.N, v, p.y_vec);
     });
   } else {
     float* out = p.part + (int64_t)split * p.M * p.N;
-    for_each_out(acc, [&](int i, int j, float v) {
-      const int64_t m = m0 + i, n = n0 + j;
-      if (m < p.M && n < p.N) out[m * p.N + n] = v;
+    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+      store4_f32(out, p.N, m0 + i, n0 + j, p.M, p.N, v, (p.N & 3) == 0);
     });
   }
 }
@@ -805,20 +837,43 @@ __global__ void __launch_bounds__(NT) skinny_kernel(SkinnyParams<BM, BN, LA, LB>
   const int kt1 = min(p.ksteps, kt0 + p.steps_per_split);
   run_phase<BM, BN, 2>(la, lb, kt0, kt1, sa, sb, acc);
   float* out = p.out + (int64_t)blockIdx.z * p.rows * p.cols;
-  for_each_out(acc, [&](int i, int j, float v) {
-    const int64_t a = i0 + i, b = j0 + j;
-    if (a < p.rows && b < p.cols) out[a * p.cols + b] = v;
+  for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+    store4_f32(out, p.cols, i0 + i, j0 + j, p.rows, p.cols, v, (p.cols & 3) == 0);
   });
 }
 
 // Sum split-K partials: out = scale * sum_s part[s]; bf16 or fp32 output.
+// Four consecutive values per thread (16-byte partial loads) when count % 4
+// == 0 and the outputs allow 8-byte (bf16) or 16-byte (fp32) stores; the
+// split order is fixed, so the sums are deterministic.
 __global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restrict__ part, int splits,
                                                             int64_t count, float scale,
                                                             uint16_t* __restrict__ out_bf16,
                                                             float* __restrict__ out_f32) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool vec = (count & 3) == 0 && (reinterpret_cast<uintptr_t>(out_bf16) & 7) == 0 &&
+                   (reinterpret_cast<uintptr_t>(out_f32) & 15) == 0;
+  if (vec) {
+    const int64_t n4 = count >> 2;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int k = 0; k < splits; ++k) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)k * count + 4 * i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += v[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] *= scale;
+      if (out_bf16)
+        *reinterpret_cast<u32x2*>(out_bf16 + 4 * i) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      if (out_f32) *reinterpret_cast<f32x4*>(out_f32 + 4 * i) = acc;
+    }
+    return;
+  }
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
     float s = 0.f;
+#pragma unroll 4
     for (int k = 0; k < splits; ++k) s += part[(int64_t)k * count + i];
     s *= scale;
     if (out_bf16) out_bf16[i] = to_bf16(s);
@@ -937,16 +992,15 @@ __global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
         acc, p.r,
         [&](int i, int kk) { return frag_f32_row(p.dH, p.r, m0 + i, p.M, kk, p.r, 1.0f); },
         [&](int j, int kk) { return frag_bf16_col(p.A, p.K, k0 + j, p.K, kk, p.r); });
+  // (dX is 16-byte aligned and K % 64 == 0: every group of four is aligned)
   if (p.splits == 1) {
-    for_each_out(acc, [&](int i, int j, float v) {
-      const int64_t m = m0 + i, k = k0 + j;
-      if (m < p.M && k < p.K) p.dX[m * p.K + k] = to_bf16(v);
+    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+      store4_bf16(p.dX, p.K, m0 + i, k0 + j, p.M, p.K, v, true);
     });
   } else {
     float* out = p.part + (int64_t)split * p.M * p.K;
-    for_each_out(acc, [&](int i, int j, float v) {
-      const int64_t m = m0 + i, k = k0 + j;
-      if (m < p.M && k < p.K) out[m * p.K + k] = v;
+    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+      store4_f32(out, p.K, m0 + i, k0 + j, p.M, p.K, v, true);
     });
   }
 }
@@ -1056,16 +1110,15 @@ __global__ void __launch_bounds__(128 * WN) dxt_gemm_kernel(DxtParams p) {
         acc, p.r,
         [&](int i, int kk) { return frag_f32_row(p.dH, p.r, m0 + i, p.M, kk, p.r, 1.0f); },
         [&](int j, int kk) { return frag_bf16_col(p.A, p.K, k0 + j, p.K, kk, p.r); });
+  // (dX is 16-byte aligned and K % 64 == 0: every group of four is aligned)
   if (p.splits == 1) {
-    for_each_out(acc, [&](int i, int j, float v) {
-      const int64_t m = m0 + i, k = k0 + j;
-      if (m < p.M && k < p.K) p.dX[m * p.K + k] = to_bf16(v);
+    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+      store4_bf16(p.dX, p.K, m0 + i, k0 + j, p.M, p.K, v, true);
     });
   } else {
     float* out = p.part + (int64_t)split * p.M * p.K;
-    for_each_out(acc, [&](int i, int j, float v) {
-      const int64_t m = m0 + i, k = k0 + j;
-      if (m < p.M && k < p.K) out[m * p.K + k] = v;
+    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+      store4_f32(out, p.K, m0 + i, k0 + j, p.M, p.K, v, true);
     });
   }
 }
@@ -1100,9 +1153,13 @@ hipError_t launch_skinny(const LA& la, const LB& lb, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
+// Split-K of a skinny product: double the splits while the workgroups number
+// under 512 and every split keeps at least 8 of the 64-deep steps (a split of
+// one or two steps spends its time on the prologue, and its partial costs
+// the reduction a round trip), at most 64.
 int pick_splits(int64_t tiles, int64_t ksteps) {
   int s = 1;
-  while (tiles * s < 512 && s * 2 <= ksteps && s < 64) s *= 2;
+  while (tiles * s < 512 && s * 2 * 8 <= ksteps && s < 64) s *= 2;
   return s;
 }
 
@@ -1226,6 +1283,7 @@ hipError_t launch_fwd_cols(const FwdArgs& a, int64_t n0, int64_t nn, int tile, i
   p.scale = a.scale;
   p.Y = a.Y + n0;
   p.ldy = a.N;
+  p.y_vec = (reinterpret_cast<uintptr_t>(p.Y) % 8) == 0 && (a.N % 4) == 0;
   p.part = scratch;
   p.splits = splits;
   p.steps_per_split = steps_per_split;
