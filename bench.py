@@ -192,7 +192,7 @@ def bench_fwd(torch, qa, M, N, K, r, steps, warmup, copies, seed=0, graph=True):
     # no decode launch fell back to computing H itself (that would be the slow path)
     giveups = qa.fwd_wait_count(ws)
     if giveups:
-        raise RuntimeError(f"M={M} {N}x{K}: {giveups} lanes gave up waiting for the LoRA-down products")
+        raise RuntimeError(f"M={M} {N}x{K}: {giveups} waits for partial results gave up (slow fallback ran)")
     byts = fwd_bytes(M, N, K, r)
     fl = fwd_flops(M, N, K, r)
     del sets, xs

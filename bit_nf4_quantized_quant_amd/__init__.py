@@ -110,10 +110,11 @@ def fwd_workspace(M: int, N: int, K: int, r: int, device):
 
 def fwd_wait_count(workspace) -> int:
     """The forward workspace's wait counter (qlora_linear_fwd_wait_counter_offset):
-    how many lanes of decode-size launches (M <= 16) gave up waiting for the
-    launch's LoRA-down products and computed them themselves.  Results stay
-    correct either way; nonzero means the slow fallback ran.  Synchronizes
-    with the device (the read is a device-to-host copy)."""
+    how many values decode-size launches (M <= 16) computed themselves after a
+    wait for another workgroup's partial result (a part of H, or a K slice's
+    partial product) gave up.  Results stay correct either way; nonzero means
+    the slow fallback ran.  Synchronizes with the device (the read is a
+    device-to-host copy)."""
     import torch
     off = qlora_linear_fwd_wait_counter_offset()
     return int(workspace[off:off + 4].view(torch.int32).item())

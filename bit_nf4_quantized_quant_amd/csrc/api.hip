@@ -11,7 +11,8 @@
 #include "nf4_table.h"
 
 namespace qlora {
-size_t decode_workspace_bytes(int64_t M, int64_t r);
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t r);
 size_t decode_wait_counter_offset();
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s);
@@ -65,13 +66,13 @@ int check_weight(const uint8_t* codes, const uint8_t* c2, const float* c1, const
 // kFwdReserved bytes whatever M is, so one workspace can serve both paths.
 constexpr size_t kFwdReserved = 4096;
 
-bool use_decode(int64_t M, int64_t N, int64_t K) {
-  // the decode kernel addresses the codes with 32-bit byte offsets
-  return M <= kDecodeMaxM && N * K / 2 < (int64_t(1) << 31);
+bool use_decode(int64_t M, int64_t N, int64_t K, int64_t r) {
+  // the decode kernels address the codes with 32-bit byte offsets
+  return M <= kDecodeMaxM && N * K / 2 < (int64_t(1) << 31) && decode_supported(M, N, K, r);
 }
 
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
-  if (use_decode(M, N, K)) return round256(decode_workspace_bytes(M, r));
+  if (use_decode(M, N, K, r)) return round256(decode_workspace_bytes(M, N, K, r));
   // H, then one scratch region used first by the LoRA-down split-K partials
   // and then by the main product's split-K partials
   const size_t scratch = std::max(lora_down_scratch_bytes(M, K, r), gemm_fwd_scratch_bytes(M, N, K));
@@ -112,7 +113,7 @@ int launch_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t
   a.Y = Y;
   a.H = r > 0 ? H_out : nullptr;
   a.workspace = workspace;
-  if (use_decode(M, N, K)) return status_of(launch_decode_fwd(a, s));
+  if (use_decode(M, N, K, r)) return status_of(launch_decode_fwd(a, s));
   char* ws = reinterpret_cast<char*>(workspace) + kFwdReserved;
   float* scratch = reinterpret_cast<float*>(ws + round256((size_t)M * r * sizeof(float)));
   if (r > 0) {

@@ -11,18 +11,34 @@
 // inference-speed discussion); here the packed codes are streamed once and
 // expanded in registers straight into bf16 matrix-core operands.
 //
-//   * LoRA-down tiles: 16 rows of A times a quarter of K, partial sums of
-//     H = X A^T, published as tagged words.
-//   * Weight tiles: 16 output rows, all of K, split over the 8 waves.  Each
-//     64-element NF4 block is one scaling unit: the levels enter bf16
-//     16x16x32 MFMAs as bf16(level) and the block's fp32 constant c_hat
-//     scales the block's partial product in fp32 afterwards, i.e. the weight
-//     used is bf16(level) * c_hat rather than bf16(level * c_hat): the same
-//     size of rounding, one place earlier.  A code byte indexes the pair
-//     table of bf16 levels in LDS.  Each lane loads the X values of its own
-//     MFMA operands (only lanes whose X row exists), so no wave waits for
-//     another before its products.
-#include <type_traits>
+// Work split.  A workgroup takes 64 output rows (four 16-row MFMA groups)
+// over one of S equal slices of K; its 8 waves split the slice's NF4 blocks
+// (at most 4 each).  A wave holds the X values of its blocks in registers and
+// uses each X fragment for all four row groups, so X crosses the L2 once per
+// 64 weight rows and K slice (at M = 16 as many bytes as the codes) instead
+// of once per 16 rows.  S is chosen so that the slices fill the chip.
+//
+// LoRA.  The workgroups also form H = X A^T, each from the X already in its
+// registers: workgroup (g, s) computes the slice-s partial of columns
+// j = g, g + G, ... of H (G = row groups), right after its X arrives, and
+// publishes it as tagged words.  Slice s adds s H[:, J_s] B[:, J_s]^T for
+// its share J_s of the r columns to its partial product, reading the S
+// partials of those columns after its stream (they were published long
+// before).  The slices then exchange their partial products: each owns
+// 64 / S rows, publishes the other rows and sums the S partials of its own
+// rows in slice order (so results do not depend on arrival order).
+//
+// Every wait is bounded (about 1 ms): a lane whose H partial or product
+// partial does not arrive computes the value itself from X, A, B and the
+// packed weight, and counts the fallback in the workspace's give-up counter.
+//
+// Each 64-element NF4 block is one scaling unit: the levels enter bf16
+// 16x16x32 MFMAs as bf16(kappa level) and the block's fp32 constant c_hat
+// scales the block's partial product in fp32 afterwards, i.e. the weight used
+// is bf16(level) * c_hat rather than bf16(level * c_hat): the same size of
+// rounding, one place earlier.  A code byte indexes the pair table of bf16
+// levels in LDS.
+#include <algorithm>
 
 #include "decode_common.h"
 
@@ -30,392 +46,487 @@ namespace qlora {
 namespace dec {
 namespace {
 
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+constexpr int kTileRows = 64;                  // output rows per workgroup
+constexpr int kGroups = kTileRows / 16;        // 16-row MFMA groups
+constexpr int kMaxWaveBlocks = 4;              // NF4 blocks per wave (X held in registers)
+constexpr int kMaxSlices = 16;
+constexpr int kMaxHCols = 16;                  // LoRA-down columns per workgroup
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 ld128(const rsrc_t& rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
 
-// Float f of the scratch space in the unused upper halves of the pair-table
-// entries (bytes 128..255 of each 256-byte entry): 32 floats per entry,
-// consecutive floats on consecutive banks.  Up to 256 * 32 floats.
+// LDS scratch in the pair table: the upper halves of its 256-byte entries
+// (bytes 128..255, never read by the lookups) hold 8192 floats at any time;
+// the lower halves hold 8192 more once the weight stream is over.
 __device__ __forceinline__ float* spare(char* lut, int f) {
   return reinterpret_cast<float*>(lut + ((f >> 5) << 8) + 128 + ((f & 31) << 2));
 }
-constexpr int kRedOff = 0;              // [kWaves][256] wave partials
-constexpr int kHsOff = kWaves * 256;    // [16][128] H rows
-static_assert(kHsOff + 16 * 128 <= 256 * 32, "scratch floats exceed the spare table halves");
+__device__ __forceinline__ float* lower(char* lut, int f) {
+  return reinterpret_cast<float*>(lut + ((f >> 5) << 8) + ((f & 31) << 2));
+}
+constexpr int kHredOff = 0;       // spare: [8 waves][16 m][16 cols] LoRA-down wave partials
+constexpr int kHpartsOff = 2048;  // spare: [S][M][nj] LoRA-down partials read back (<= 2048)
+constexpr int kYredOff = 0;       // spare: [8 waves][1024] product wave partials (after the LoRA-up)
+constexpr uint32_t kMissing = 0xFFFFFFFFu;   // a partial that never came (a NaN pattern)
 
-// ---------------------------------------------------------------- LoRA-down tile
-// Rows j0..j0+15 of A over a quarter of K; each wave takes a contiguous run of
-// 32-wide steps and issues the loads of 8 steps at a time.  MFMA rows past M
-// (lanes whose X row does not exist) carry zeros; their outputs are dropped.
-constexpr int kHBatch = 8;
-
-// ticket: thread 0's LoRA-down counter update (its epoch names this launch).
-__device__ void lora_down_tile(const DecodeParams& p, int tile, float* red, uint32_t* tag_lds, uint64_t ticket) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rg = tile / kHSplit, ks = tile % kHSplit;
-  const int j0 = rg * kRows;
-  const int jl = lane & 15, g = lane >> 4;
-  const int steps = p.K / 32;
-  const int per_split = (steps + kHSplit - 1) / kHSplit;
-  const int s_lo = ks * per_split, s_hi = min(steps, s_lo + per_split);
-  const int per_wave = (s_hi - s_lo + kWaves - 1) / kWaves;
-  const int s_beg = s_lo + wave * per_wave, s_end = min(s_hi, s_beg + per_wave);
-  const rsrc_t ra = make_rsrc(p.A, (uint32_t)p.r * p.K * 2);
-  const rsrc_t rx = make_rsrc(p.X, (uint32_t)p.M * p.K * 2);
-  const uint32_t a_off = ((uint32_t)(j0 + jl) * p.K + 8 * g) * 2;   // rows >= r read as 0
-  const uint32_t x_off = ((uint32_t)jl * p.K + 8 * g) * 2;
-  const bool xrow = jl < p.M;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  u32x4 xv[kHBatch];
-#pragma unroll
-  for (int i = 0; i < kHBatch; ++i) xv[i] = u32x4{0u, 0u, 0u, 0u};
-  for (int s0 = s_beg; s0 < s_end; s0 += kHBatch) {
-    u32x4 av[kHBatch];
-#pragma unroll
-    for (int i = 0; i < kHBatch; ++i) {
-      const uint32_t k2 = (uint32_t)min(s0 + i, s_end - 1) * 64;   // 32 elements * 2 bytes
-      if (xrow) xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off + k2, 0, 0));
-      av[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + k2, 0, 0));
+// Y[m][row] * kappa computed by one lane from X, the packed weight, A and B,
+// for an exchange whose partial never came; counted on the give-up counter.
+// lev: the 16 levels bf16(kappa level[c]) as floats (LDS).
+__device__ __attribute__((noinline)) float lane_output(const uint16_t* X, const uint8_t* codes, const uint8_t* c2,
+                                                     const float* c1, float mu, const float* lev,
+                                                     const uint16_t* A, const uint16_t* B, int K, int r, float scale,
+                                                     int m, int row, char* ws) {
+  __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(ws + kGiveupCounter), 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  const int nblk = K / 64;
+  float y = 0.f;
+  for (int b = 0; b < nblk; ++b) {
+    const size_t flat = (size_t)row * nblk + b;
+    const float chat = dequant_constant(c2[flat], c1[flat >> 8], mu);
+    float part = 0.f;
+    for (int k = 0; k < 64; ++k) {
+      const uint32_t byte = codes[(size_t)row * (K / 2) + b * 32 + (k >> 1)];
+      const uint32_t c = (k & 1) ? (byte >> 4) : (byte & 15u);
+      part = __builtin_fmaf(__uint_as_float((uint32_t)X[(size_t)m * K + b * 64 + k] << 16), lev[c], part);
     }
-#pragma unroll
-    for (int i = 0; i < kHBatch; ++i)
-      if (s0 + i < s_end) acc = mfma16(as_bf16x8(xv[i]), as_bf16x8(av[i]), acc);
+    y = __builtin_fmaf(chat, part, y);
   }
-  // acc[v] = partial H[m = 4g + v][j0 + jl]; reduce over the waves
-#pragma unroll
-  for (int v = 0; v < 4; ++v) red[wave * 256 + (4 * g + v) * 16 + jl] = acc[v];
-  if (threadIdx.x == 0) *tag_lds = (uint32_t)(ticket >> 20) + 1u;
-  __syncthreads();
-  if (threadIdx.x < 256) {
-    const int m = threadIdx.x >> 4, jj = threadIdx.x & 15;
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += red[w * 256 + threadIdx.x];
-    const int r16 = (p.r + 15) & ~15;
-    if (m < p.M) st_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j0 + jj], *tag_lds, sum);
+  for (int j = 0; j < r; ++j) {
+    float h = 0.f;   // H[m][j], here in plain fp32 multiply-adds
+    for (int k = 0; k < K; ++k)
+      h = __builtin_fmaf(__uint_as_float((uint32_t)X[(size_t)m * K + k] << 16),
+                         __uint_as_float((uint32_t)A[(size_t)j * K + k] << 16), h);
+    y = __builtin_fmaf(scale * h, __uint_as_float((uint32_t)B[(size_t)row * r + j] << 16), y);
   }
+  return y;
 }
 
-// ---------------------------------------------------------------- weight tile
-// Lane (nl, g) = (lane % 16, lane / 16) holds, per block, 8 code bytes of row
-// n0 + nl (elements 16 g .. 16 g + 15 of the block: the MFMA B operand of the
-// block's two 32-wide steps) and the matching X values of batch row m = nl
-// (the A operand).  Loads of kBatch consecutive blocks are issued together
-// and the next batch is in flight while the current one is multiplied.
-constexpr int kBatch = 4;
-
-template <bool kC2Vec>
-struct Batch {
-  u32x4 x0[kBatch], x1[kBatch];  // X for the block's two steps (lanes with nl < M)
-  u32x2 cw[kBatch];              // 8 code bytes per block
-  // c2 of the batch's blocks: one aligned dword (rows of c2 dword aligned),
-  // else one byte load each
-  typename std::conditional<kC2Vec, uint32_t, uint8_t[kBatch]>::type c2;
-  float c1a, c1b;                // c1 of the batch's first and last block
-};
-
-struct Ctx {
-  rsrc_t rc, r2, r1, rx;
-  uint32_t code_off;   // byte offset of this lane's codes in block 0
-  uint32_t blk0;       // block index of (row, block 0)
-  uint32_t x_off;      // byte offset of this lane's X row at k = 16 g
-  uint32_t n_c2;
-  int b_end;
-  bool xrow;
-};
-
-// X first (used first), then codes and constants.  A batch starts at a
-// multiple of 4 blocks, so that with c2_vec its c2 bytes form one aligned
-// dword.  Lanes without an X row load no X and keep the zeros they hold.
-template <bool kC2Vec>
-__device__ __forceinline__ void load_batch(const DecodeParams& p, const Ctx& c, Batch<kC2Vec>& L, int b0) {
-  if (c.xrow) {
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const uint32_t b = (uint32_t)min(b0 + i, c.b_end - 1);
-      L.x0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.x_off + 128 * b, 0, 0));
-      L.x1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.x_off + 128 * b + 16, 0, 0));
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
-    const uint32_t b = (uint32_t)min(b0 + i, c.b_end - 1);
-    L.cw[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(c.rc, c.code_off + 32 * b, 0, 0));
-  }
-  if constexpr (kC2Vec) {
-    L.c2 = __builtin_amdgcn_raw_buffer_load_b32(c.r2, c.blk0 + (uint32_t)b0, 0, 0);
-  } else {
-    // plain byte loads, which widen for free, on a clamped index
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const uint32_t blk = c.blk0 + (uint32_t)min(b0 + i, c.b_end - 1);
-      L.c2[i] = p.c2[blk < c.n_c2 ? blk : c.n_c2 - 1u];
-    }
-  }
-  L.c1a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.r1, ((c.blk0 + b0) >> 8) * 4, 0, 0));
-  L.c1b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.r1, ((c.blk0 + b0 + kBatch - 1) >> 8) * 4, 0, 0));
-}
-
-template <bool kC2Vec>
-__device__ __forceinline__ void mul_batch(const Ctx& c, const Batch<kC2Vec>& L, int b0, float mu, const char* lut,
-                                          uint32_t lane4, f32x4& acc) {
-#pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
-    if (b0 + i >= c.b_end) break;
-    const uint32_t blk = c.blk0 + (uint32_t)(b0 + i);
-    const float c1 = ((blk >> 8) == ((c.blk0 + b0) >> 8)) ? L.c1a : L.c1b;
-    float chat;
-    if constexpr (kC2Vec)
-      chat = i == 0 ? dequant_constant_byte<0>(L.c2, c1, mu)
-           : i == 1 ? dequant_constant_byte<1>(L.c2, c1, mu)
-           : i == 2 ? dequant_constant_byte<2>(L.c2, c1, mu)
-                    : dequant_constant_byte<3>(L.c2, c1, mu);
-    else
-      chat = dequant_constant(L.c2[i], c1, mu);
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t w = L.cw[i][h];
-      u32x4 wv;
-      wv[0] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<0>(w, lane4));
-      wv[1] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<1>(w, lane4));
-      wv[2] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<2>(w, lane4));
-      wv[3] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<3>(w, lane4));
-      t = mfma16(as_bf16x8(h ? L.x1[i] : L.x0[i]), as_bf16x8(wv), t);
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(chat, t[v], acc[v]);
-  }
-}
-
-// kNB: batches per wave (the launcher's exact count), or 0 for any count.
-template <bool kC2Vec, int kNB>
-__device__ void weight_tile(const DecodeParams& p, int tile, char* lut, uint32_t* tag_lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = tile * kRows;
-  const int nl = lane & 15, g = lane >> 4;
-  const int nblk = p.K / 64;
+// kNB: NF4 blocks per wave at most (the launcher's bound for this shape).
+template <int kNB>
+__global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams p) {
+  // pair table (64 KiB); its spare halves hold the reductions
+  __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];
+  __shared__ float lev[16];
+  __shared__ uint32_t tag_lds;
+  QLORA_FETCH_ARGS(p);
+  asm volatile("" ::"s"(p.G), "s"(p.S), "s"(p.hcols), "s"(p.Ypart), "s"(p.Hpart));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 15, g4 = lane >> 4;
+  const int S = p.S;
+  const int bid = (int)blockIdx.x;
+  // workgroup -> (row group g, slice s): a row group's slices are adjacent
+  const int g = __builtin_amdgcn_readfirstlane(bid / S), s = bid - g * S;
+  const int n0 = g * kTileRows;
+  const int K = p.K, N = p.N, M = p.M, r = p.r;
+  const int nblk = K >> 6;
   const float mu = load_mean(p);
-  // this launch's epoch: thread 0's counter update goes out first, and its
-  // reply, which comes back ahead of every later load, is used only at the
-  // end (no other thread reads the variable)
-  uint64_t ticket;
-  if (threadIdx.x == 0) ticket = take_weight_ticket(p, tile);
+  // this launch's epoch: wave 0 reads this workgroup's counter ahead of
+  // every other load, and only then does thread 0 add the workgroup's share
+  // (a read after it could see the launch's last share and the next epoch);
+  // the tag, epoch + 1, reaches the other waves through LDS
+  uint32_t epoch = 0;
+  if (wave == 0) epoch = slot_epoch(p.ws, kWeightCtr, (uint32_t)bid);
+  if (threadIdx.x == 0) (void)take_weight_ticket(p, bid);
 
-  Ctx c;
-  const uint32_t n_c2 = (uint32_t)p.N * nblk;
-  c.rc = make_rsrc(p.codes, n_c2 * 32u);
-  c.r2 = make_rsrc(p.c2, n_c2);
-  c.r1 = make_rsrc(p.c1, ((n_c2 + 255u) / 256u) * 4u);
-  c.rx = make_rsrc(p.X, (uint32_t)p.M * p.K * 2);
-  const uint32_t row = (uint32_t)(n0 + nl);             // rows >= N read as zero codes
-  c.code_off = row * (uint32_t)(p.K / 2) + 8u * g;
-  c.blk0 = row * (uint32_t)nblk;
-  c.x_off = ((uint32_t)nl * p.K + 16u * g) * 2u;
-  c.n_c2 = n_c2;
-  c.xrow = nl < p.M;
-  // each wave takes a run of whole batches (multiples of 4 blocks)
-  const int per = ((nblk + kWaves - 1) / kWaves + kBatch - 1) / kBatch * kBatch;
-  const int b_beg = min(nblk, wave * per);
-  c.b_end = min(nblk, b_beg + per);
+  // this wave's blocks: the slice [sb0, sb1) split over the 8 waves
+  const int sb0 = s * nblk / S, sb1 = (s + 1) * nblk / S;
+  const int len = sb1 - sb0, per = len >> 3, rem = len & 7;
+  const int wb0 = sb0 + wave * per + min(wave, rem);
+  const int nbw = per + (wave < rem ? 1 : 0);
+  int blk[kNB];   // clamped: every load is issued whatever the wave's share
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) blk[i] = min(wb0 + min(i, max(nbw - 1, 0)), nblk - 1);
 
-  Batch<kC2Vec> La = {}, Lb = {};
-  const uint32_t lane4 = (uint32_t)(lane & 31) * 4u;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (kNB > 0) {
-    // A known batch count: every load is issued whatever the wave's share
-    // (offsets are clamped, reads past the end return zero, multiplies past
-    // the share are skipped), so each wait counts exactly the loads issued
-    // after the one it waits for.  Two batches in flight.
-    load_batch(p, c, La, b_beg);
-    if constexpr (kNB > 1) load_batch(p, c, Lb, b_beg + kBatch);
-    build_pair_table<kThreads>(p, lut);   // while the loads are in flight
-    __syncthreads();
+  const rsrc_t rx = make_rsrc(p.X, (uint32_t)M * K * 2);         // rows >= M read as zero
+  const rsrc_t ra = make_rsrc(p.A, (uint32_t)r * K * 2);         // rows >= r read as zero
+  const rsrc_t rc = make_rsrc(p.codes, (uint32_t)N * (K / 2));   // rows >= N read as zero
+  const rsrc_t r2 = make_rsrc(p.c2, (uint32_t)N * nblk);
+  const rsrc_t r1 = make_rsrc(p.c1, (uint32_t)((N * nblk + 255) / 256) * 4u);
+
+  // LoRA-down columns of this workgroup: j = g hc + c, c < count (<= 16)
+  const int hc = p.hcols;
+  const int count = r > 0 ? max(0, min(hc, r - g * hc)) : 0;
+  const uint32_t jrow = nl < count ? (uint32_t)(g * hc + nl) : (uint32_t)r;   // r: reads zero
+
+  // Loads: X, then (workgroups that produce H) A, the LoRA-down operands,
+  // then codes and the block constants.  Lane (nl, g4) holds, per block,
+  // elements 16 g4 .. 16 g4 + 15: the MFMA operands of the block's two
+  // 32-wide steps (X row nl as the A operand, weight row or A row nl as the
+  // B operand).
+  u32x4 x[kNB][2];
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) {
+    const uint32_t kb = (uint32_t)blk[i] * 128u + 32u * g4;
+    x[i][0] = ld128(rx, (uint32_t)nl * K * 2 + kb);
+    x[i][1] = ld128(rx, (uint32_t)nl * K * 2 + kb + 16);
+  }
+  u32x4 a[kNB][2];
+  if (count > 0) {
 #pragma unroll
     for (int i = 0; i < kNB; ++i) {
-      Batch<kC2Vec>& cur = (i & 1) ? Lb : La;
-      mul_batch(c, cur, b_beg + i * kBatch, mu, lut, lane4, acc);
-      if (i + 2 < kNB) load_batch(p, c, cur, b_beg + (i + 2) * kBatch);
+      const uint32_t kb = (uint32_t)blk[i] * 128u + 32u * g4;
+      a[i][0] = ld128(ra, jrow * (uint32_t)K * 2 + kb);
+      a[i][1] = ld128(ra, jrow * (uint32_t)K * 2 + kb + 16);
     }
-  } else {
-    const bool work = b_beg < c.b_end;
-    if (work) {
-      load_batch(p, c, La, b_beg);
-      if (b_beg + kBatch < c.b_end) load_batch(p, c, Lb, b_beg + kBatch);
-    }
-    build_pair_table<kThreads>(p, lut);   // while the loads are in flight
-    __syncthreads();
-    if (work) {
-      for (int b0 = b_beg; b0 < c.b_end; b0 += 2 * kBatch) {
-        if (b0 != b_beg && b0 + kBatch < c.b_end) load_batch(p, c, Lb, b0 + kBatch);
-        mul_batch(c, La, b0, mu, lut, lane4, acc);
-        if (b0 + 2 * kBatch < c.b_end) load_batch(p, c, La, b0 + 2 * kBatch);
-        if (b0 + kBatch < c.b_end) mul_batch(c, Lb, b0 + kBatch, mu, lut, lane4, acc);
+  }
+  u32x2 cw[kNB][kGroups];
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const uint32_t row = (uint32_t)(n0 + 16 * q + nl);
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      cw[i][q] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, row * (uint32_t)(K / 2) + (uint32_t)blk[i] * 32u + 8u * g4, 0, 0));
+  }
+  // Block constants with one lane per tile row (row n0 + lane): the c2 byte
+  // of each of the wave's blocks, and c1 of its first and last block (a run
+  // of <= 4 blocks crosses at most one 256-block boundary of the flattened
+  // constant index).  They reach the MFMA layout by lane permutes.
+  const uint32_t f0 = (uint32_t)(n0 + lane) * (uint32_t)nblk + (uint32_t)blk[0];
+  uint32_t c2r[kNB];
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) c2r[i] = __builtin_amdgcn_raw_buffer_load_b8(r2, f0 + (uint32_t)i, 0, 0);
+  const float c1a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (f0 >> 8) * 4u, 0, 0));
+  const float c1b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ((f0 + kNB - 1) >> 8) * 4u, 0, 0));
+  build_pair_table<kThreads>(p, lut);   // while the loads are in flight
+  if (threadIdx.x < 16) {
+    uint32_t hv = 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) hv = (int)threadIdx.x == c ? p.hi[c] : hv;
+    lev[threadIdx.x] = __uint_as_float(hv << 16);
+  }
+
+  // LoRA-down: this wave's part of H_s[m][j] for the workgroup's columns
+  if (count > 0) {
+    f32x4 th = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      if (i < nbw) {
+        th = mfma16(x[i][0], a[i][0], th);
+        th = mfma16(x[i][1], a[i][1], th);
       }
     }
-  }
-  // Epilogue.  The LoRA term s H B^T goes through the matrix cores too: wave
-  // w < ceil(r / 32) takes j = 32 w .. 32 w + 31, with B[n0 + nl][j ..] read
-  // straight as the B operand and s H[m][j ..] as the A operand, split into
-  // bf16 high and low parts (two products: fp32 accuracy).  Its product
-  // joins the wave's partial sums, and the 8 waves' sums meet in LDS.
-  // B and this thread's LoRA-down partials are read right after the stream,
-  // so their replies come back during the barrier.
-  const int r16 = (p.r + 15) & ~15;
-  const bool lwave = wave * 32 < p.r;
-  const int jb = wave * 32 + 8 * g;                  // this lane's first j
-  u32x4 bop = {0u, 0u, 0u, 0u};
-  if (lwave && jb < p.r) {
-    const rsrc_t rb = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);   // rows past N read as 0
-    const uint32_t off = ((uint32_t)(n0 + nl) * p.r + jb) * 2;
-    if (p.b_vec) {   // r % 8 == 0: all 8 entries exist
-      bop = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
-    } else {
-      uint16_t e[8];
+    // th[v] = partial H[m = 4 g4 + v][column nl]
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        e[q] = jb + q < p.r ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, off + 2 * q, 0, 0) : (uint16_t)0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bop[q] = (uint32_t)e[2 * q] | ((uint32_t)e[2 * q + 1] << 16);
-    }
-  }
-  constexpr int kHPer = 16 * 128 / kThreads;   // up to M*r = 2048 sums per tile
-  const int mr = p.M * p.r;
-  uint64_t hp[kHPer][kHSplit];
-#pragma unroll
-  for (int u = 0; u < kHPer; ++u) {
-    const int i = threadIdx.x + u * kThreads;
-    if (i < mr) {
-      const int m = i / p.r, j = i - m * p.r;
-#pragma unroll
-      for (int ks = 0; ks < kHSplit; ++ks) hp[u][ks] = ld_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j]);
-    }
+    for (int v = 0; v < 4; ++v) *spare(lut, kHredOff + wave * 256 + (4 * g4 + v) * 16 + nl) = th[v];
   }
   if (threadIdx.x == 0) {
-    // (the empty asm keeps the use of the reply here, at the end)
-    asm volatile("" : "+v"(ticket));
-    *tag_lds = (uint32_t)(ticket >> 20) + 1u;
+    asm volatile("" : "+v"(epoch));   // (keeps the use of the counter's value, and its wait, here)
+    tag_lds = epoch + 1u;
   }
   __syncthreads();
-
-  // this launch's LoRA-down partials (tag = epoch + 1), polled until present
-  // or, past the deadline, computed here
-  const uint32_t tag = *tag_lds;
-  uint64_t deadline = 0;   // set at the first miss
-#pragma unroll
-  for (int u = 0; u < kHPer; ++u) {
-    const int i = threadIdx.x + u * kThreads;
-    if (i < mr) {
-      const int m = i / p.r, j = i - m * p.r;
+  const uint32_t tag = tag_lds;
+  if (count > 0 && threadIdx.x < 256) {
+    const int m = threadIdx.x >> 4, col = threadIdx.x & 15;
+    if (m < M && col < count) {
       float h = 0.f;
-      bool got = true;
 #pragma unroll
-      for (int ks = 0; ks < kHSplit; ++ks) {
-        float v = 0.f;
-        got = got && poll_tagged(&p.Hpart[((size_t)ks * p.M + m) * r16 + j], hp[u][ks], tag, deadline, &v);
+      for (int w = 0; w < kWaves; ++w) h += *spare(lut, kHredOff + w * 256 + threadIdx.x);
+      st_tagged(&p.Hpart[((size_t)s * M + m) * r + g * hc + col], tag, h);
+    }
+  }
+
+  // The weight stream: per block and row group, two MFMAs on bf16 levels and
+  // the block constant applied to their sum in fp32.
+  const uint32_t lane4 = (uint32_t)(lane & 31) * 4u;
+  f32x4 acc[kGroups];
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) {
+    if (i >= nbw) break;
+    // this row lane's c_hat of block i, then the MFMA layout's: row 16 q + nl
+    uint32_t c2 = c2r[i];
+    asm volatile("" : "+v"(c2));   // (keeps any widening here, not next to the load)
+    const float chat_row = dequant_constant(c2, ((f0 + i) >> 8) == (f0 >> 8) ? c1a : c1b, mu);
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const float chat = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * q + nl), __float_as_int(chat_row)));
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w = cw[i][q][h];
+        u32x4 wv;
+        wv[0] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<0>(w, lane4));
+        wv[1] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<1>(w, lane4));
+        wv[2] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<2>(w, lane4));
+        wv[3] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<3>(w, lane4));
+        t = mfma16(x[i][h], wv, t);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[q][v] = __builtin_fmaf(chat, t[v], acc[q][v]);
+    }
+  }
+
+  // LoRA-up of this slice's columns J_s = [jl, jl + nj): read the S partials
+  // of H[:, J_s] (thread: one (slice, m, j) word each, up to 4) and the
+  // wave's B operands, all issued before any wait.
+  const int jl = s * r / S, nj = (s + 1) * r / S - jl;
+  const int nsteps = (nj + 31) >> 5;
+  const int nwords = S * M * nj;   // <= M r <= 2048
+  uint64_t hw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = threadIdx.x + u * kThreads;
+    if (idx < nwords) {
+      const int sp = idx / (M * nj), rest = idx - sp * (M * nj);
+      const int m = rest / nj, jj = rest - m * nj;
+      hw[u] = ld_tagged(&p.Hpart[((size_t)sp * M + m) * r + jl + jj]);
+    }
+  }
+  // B operands: items (row group q, 32-wide step st) with q = wave % 4 and
+  // st = wave / 4 + 2 u
+  const int qb = wave & 3;
+  u32x4 bop[2];
+  {
+    const rsrc_t rb = make_rsrc(p.B, (uint32_t)N * r * 2);   // rows past N read as zero
+    const uint32_t brow = (uint32_t)(n0 + 16 * qb + nl);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bop[u] = u32x4{0u, 0u, 0u, 0u};
+      const int jj0 = 32 * ((wave >> 2) + 2 * u) + 8 * g4;
+      if (jj0 < nj) {
+        const uint32_t off = (brow * (uint32_t)r + (uint32_t)(jl + jj0)) * 2u;
+        if (p.b_vec && (jl % 8) == 0 && (nj % 8) == 0) {
+          bop[u] = ld128(rb, off);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            e[q] = jj0 + q < nj ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, off + 2 * q, 0, 0) : 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bop[u][q] = e[2 * q] | (e[2 * q + 1] << 16);
+        }
+      }
+    }
+  }
+  // partials, polled, into LDS (a missing one as kMissing)
+  {
+    uint64_t deadline = 0;   // set at the first miss
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = threadIdx.x + u * kThreads;
+      if (idx < nwords) {
+        const int sp = idx / (M * nj), rest = idx - sp * (M * nj);
+        const int m = rest / nj, jj = rest - m * nj;
+        float v;
+        if (!poll_tagged(&p.Hpart[((size_t)sp * M + m) * r + jl + jj], hw[u], tag, deadline, &v))
+          v = __uint_as_float(kMissing);
+        *spare(lut, kHpartsOff + idx) = v;
+      }
+    }
+  }
+  __syncthreads();   // every wave's stream is over: the table's lower halves are free
+  // H[m][j] for j in J_s: the S partials in slice order (or, if one is
+  // missing, computed here), scaled by s into the lower halves
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = threadIdx.x + u * kThreads;
+    if (idx < M * nj) {
+      const int m = idx / nj, jj = idx - m * nj;
+      float h = 0.f;
+      bool missing = false;
+      for (int sp = 0; sp < S; ++sp) {
+        const float v = *spare(lut, kHpartsOff + sp * M * nj + idx);
+        missing = missing || __float_as_uint(v) == kMissing;
         h += v;
       }
-      if (!got) h = lane_lora_down(p.X, p.A, p.K, m, j, p.ws);
-      *spare(lut, kHsOff + m * 128 + j) = h;
-      if (tile == 0 && p.H) p.H[i] = h;
+      if (missing) h = lane_lora_down(p.X, p.A, K, m, jl + jj, p.ws);
+      if (g == 0 && p.H) p.H[(size_t)m * r + jl + jj] = h;
+      *lower(lut, m * 128 + jj) = p.scale * h;
     }
   }
   __syncthreads();
-
-  if (lwave) {
-    // A operand: s H[m = nl][jb .. jb + 7] as bf16 hi + lo (zeros past M or r)
-    u32x4 ahi = {0u, 0u, 0u, 0u}, alo = {0u, 0u, 0u, 0u};
-    if (nl < p.M) {
+  if (nj > 0) {
+    // A operand: s H[m = nl][jl + jj0 .. + 7] as bf16 high + low parts (two
+    // products: fp32 accuracy); zero past M or nj
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[2];
+    for (int u = 0; u < 2; ++u) {
+      const int st = (wave >> 2) + 2 * u;
+      if (st >= nsteps) break;
+      const int jj0 = 32 * st + 8 * g4;
+      u32x4 ahi = {0u, 0u, 0u, 0u}, alo = {0u, 0u, 0u, 0u};
+      if (nl < M) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = jb + 2 * q + e;
-          v[e] = j < p.r ? p.scale * *spare(lut, kHsOff + nl * 128 + j) : 0.f;
+        for (int q = 0; q < 4; ++q) {
+          float v[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int jj = jj0 + 2 * q + e;
+            v[e] = jj < nj ? *lower(lut, nl * 128 + jj) : 0.f;
+          }
+          const uint32_t hi = pack_bf16x2(v[0], v[1]);
+          ahi[q] = hi;
+          alo[q] = pack_bf16x2(v[0] - bf16_lo(hi), v[1] - bf16_hi(hi));
         }
-        const uint32_t hi = pack_bf16x2(v[0], v[1]);
-        ahi[q] = hi;
-        alo[q] = pack_bf16x2(v[0] - bf16_lo(hi), v[1] - bf16_hi(hi));
+      }
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) {
+        if (q == qb) {
+          acc[q] = mfma16(ahi, bop[u], acc[q]);
+          acc[q] = mfma16(alo, bop[u], acc[q]);
+        }
       }
     }
-    acc = mfma16(as_bf16x8(ahi), as_bf16x8(bop), acc);
-    acc = mfma16(as_bf16x8(alo), as_bf16x8(bop), acc);
   }
-  // acc[v] = partial Y[m = 4g + v][n0 + nl]: the 8 waves' sums meet
+  // acc[q][v] = partial Y[m = 4 g4 + v][row 16 q + nl]: the waves' sums meet
 #pragma unroll
-  for (int v = 0; v < 4; ++v) *spare(lut, kRedOff + wave * 256 + (4 * g + v) * 16 + nl) = acc[v];
+  for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) *spare(lut, kYredOff + wave * 1024 + q * 256 + (4 * g4 + v) * 16 + nl) = acc[q][v];
   __syncthreads();
-  if ((int)threadIdx.x < 16 * p.M) {
-    const int o = threadIdx.x, m = o >> 4, n = n0 + (o & 15);
+
+  // Exchange.  Output o = 256 q + 16 m + nl (row rt = 16 q + nl of the
+  // tile); the thread holds o = t and t + 512.  Slice s owns rows
+  // [os(s), os(s + 1)), os(s) = 64 s / S: it publishes the other rows'
+  // partials and sums its own.  Layout per (row group, owner, source slice):
+  // RS = ceil(64 / S) rows of M words.
+  const int RS = (kTileRows + S - 1) / S;
+  const size_t ybase = (size_t)g * S * S * RS * M;
+  float own[2];
+  bool owns[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int o = threadIdx.x + u * kThreads;
+    const int q = o >> 8, m = (o >> 4) & 15, rt = 16 * q + (o & 15);
     float y = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) y += *spare(lut, kRedOff + w * 256 + o);
+    for (int w = 0; w < kWaves; ++w) y += *spare(lut, kYredOff + w * 1024 + o);
+    own[u] = y;
+    owns[u] = false;
+    if (m >= M || n0 + rt >= N) continue;
+    const int owner = (rt * S + S - 1) / kTileRows;
+    if (owner != s) {
+      const int lr = rt - owner * kTileRows / S;
+      st_tagged(&p.Ypart[ybase + ((size_t)(owner * S + s) * RS + lr) * M + m], tag, y);
+    } else {
+      owns[u] = true;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (!owns[u]) continue;
+    const int o = threadIdx.x + u * kThreads;
+    const int q = o >> 8, m = (o >> 4) & 15, rt = 16 * q + (o & 15);
+    const int lr = rt - s * kTileRows / S;
+    const uint64_t* src = &p.Ypart[ybase + ((size_t)(s * S) * RS + lr) * M + m];   // + sp RS M
+    const size_t step = (size_t)RS * M;
+    uint64_t wv[kMaxSlices];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSlices; ++sp)
+      if (sp < S && sp != s) wv[sp] = ld_tagged(src + sp * step);
+    uint64_t deadline = 0;
+    float y = 0.f;
+    bool ok = true;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSlices; ++sp) {
+      if (sp >= S) break;
+      float v = own[u];
+      if (sp != s) ok = ok && poll_tagged(src + sp * step, wv[sp], tag, deadline, &v);
+      y += v;
+    }
+    if (!ok)
+      y = lane_output(p.X, p.codes, p.c2, p.c1, mu, lev, p.A, p.B, K, r, p.scale, m, n0 + rt, p.ws);
     y *= p.inv_kappa;
-    if (n < p.N) p.Y[(size_t)m * p.N + n] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
+    p.Y[(size_t)m * N + n0 + rt] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
   }
-}
-
-template <bool kC2Vec, int kNB>
-__global__ void __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(4))) qlora_decode_kernel(DecodeParams p) {
-  // pair table; its entries' upper halves hold the tile's scratch floats
-  __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];   // 64 KiB
-  __shared__ uint32_t tag;
-  const int tile = (int)blockIdx.x;
-  QLORA_FETCH_ARGS(p);
-  if (tile < p.n_htiles) {
-    uint64_t hticket = 0;
-    if (threadIdx.x == 0) hticket = take_down_ticket(p, tile);
-    lora_down_tile(p, tile, reinterpret_cast<float*>(lut), &tag, hticket);
-    return;
-  }
-  weight_tile<kC2Vec, kNB>(p, tile - p.n_htiles, lut, &tag);
 }
 
 typedef void (*DecodeKernel)(DecodeParams);
-template <bool kC2Vec>
 DecodeKernel decode_kernel(int nb) {
   switch (nb) {
-    case 1: return qlora_decode_kernel<kC2Vec, 1>;
-    case 2: return qlora_decode_kernel<kC2Vec, 2>;
-    case 3: return qlora_decode_kernel<kC2Vec, 3>;
-    case 4: return qlora_decode_kernel<kC2Vec, 4>;
-    case 5: return qlora_decode_kernel<kC2Vec, 5>;
-    case 6: return qlora_decode_kernel<kC2Vec, 6>;
-    case 7: return qlora_decode_kernel<kC2Vec, 7>;
-    case 8: return qlora_decode_kernel<kC2Vec, 8>;
-    default: return qlora_decode_kernel<kC2Vec, 0>;
+    case 1: return qlora_decode_kernel<1>;
+    case 2: return qlora_decode_kernel<2>;
+    case 3: return qlora_decode_kernel<3>;
+    default: return qlora_decode_kernel<4>;
   }
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(int64_t M, int64_t r) {
+// Slices of K: the count that minimises the heaviest compute unit's share
+// (workgroups per unit, rounded up, times blocks per workgroup), keeping
+// every wave within kMaxWaveBlocks blocks and, where K allows, every wave
+// busy (slices of at least 8 blocks); the fewest slices among equals.
+int decode_slices(int64_t N, int64_t K) {
+  const int64_t G = (N + kTileRows - 1) / kTileRows, nblk = K / 64, cus = cu_count();
+  const int64_t most = std::max<int64_t>(1, std::min<int64_t>(kMaxSlices, nblk / kWaves));
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int S = 1; S <= most; ++S) {
+    const int64_t slice = (nblk + S - 1) / S;
+    if (slice > (int64_t)kWaves * kMaxWaveBlocks) continue;
+    const int64_t cost = (G * S + cus - 1) / cus * slice;
+    if (best == 0 || cost < best_cost) {
+      best = S;
+      best_cost = cost;
+    }
+  }
+  return best == 0 ? kMaxSlices : best;
+}
+
+// LoRA-down columns per producing workgroup: as few as the row groups allow,
+// and enough that every producer (workgroups g < ceil(r / hcols) of every
+// slice) lies among the first cu_count() workgroups, which are resident
+// from the start: a consumer never waits for a workgroup that is waiting
+// for a free compute unit.
+int decode_hcols(int64_t N, int64_t r, int S) {
+  if (r == 0) return 1;
+  const int64_t G = (N + kTileRows - 1) / kTileRows, cus = cu_count();
+  int64_t hc = std::max<int64_t>(1, (r + G - 1) / G);
+  // producers: row groups g < P = ceil(r / hc) of every slice, workgroups below P S
+  while (hc < kMaxHCols && (r + hc - 1) / hc * S > cus) ++hc;
+  return (int)hc;
+}
+
+bool decode_supported(int64_t N, int64_t K, int64_t r) {
+  const int64_t nblk = K / 64;
+  const int S = decode_slices(N, K);
+  return (nblk + S - 1) / S <= (int64_t)kWaves * kMaxWaveBlocks && decode_hcols(N, r, S) <= kMaxHCols;
+}
+
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t r16 = (r + 15) & ~15;
-  return kHpartOff + (size_t)(kHSplit * M * r16) * sizeof(uint64_t);
+  if (M <= 4) return kHpartOff + (size_t)(M * r16) * sizeof(uint64_t);   // the GEMV path
+  const int64_t S = decode_slices(N, K), G = (N + kTileRows - 1) / kTileRows;
+  const int64_t RS = (kTileRows + S - 1) / S;
+  const size_t hpart = ((size_t)(S * M * r) * sizeof(uint64_t) + 255) & ~(size_t)255;
+  const size_t ypart = S > 1 ? (size_t)(G * S * S * RS * M) * sizeof(uint64_t) : 0;
+  return kHpartOff + hpart + ypart;
 }
 
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   DecodeParams p = decode_params(a);
   if (a.M <= 4) return launch_gemv_fwd(p, s);
-  const int64_t r16 = (a.r + 15) & ~15;
-  p.n_htiles = (int)(r16 / kRows) * kHSplit;
-  // batches of kBatch blocks per wave (the weight tile's split of K)
-  const int nblk = (int)(a.K / 64);
-  const int per = ((nblk + kWaves - 1) / kWaves + kBatch - 1) / kBatch * kBatch;
-  const int nb = per / kBatch;
-  const DecodeKernel k = p.c2_vec ? decode_kernel<true>(nb) : decode_kernel<false>(nb);
-  const dim3 grid(p.n_htiles + p.n_wtiles);
-  hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, p);
+  const int S = decode_slices(a.N, a.K);
+  p.G = (int)((a.N + kTileRows - 1) / kTileRows);
+  p.S = S;
+  p.hcols = decode_hcols(a.N, a.r, S);
+  p.n_htiles = 0;
+  p.n_wtiles = p.G * S;
+  const size_t hpart = ((size_t)(S * a.M * a.r) * sizeof(uint64_t) + 255) & ~(size_t)255;
+  p.Ypart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff + hpart);
+  const int64_t nblk = a.K / 64, slice = (nblk + S - 1) / S;
+  const int nb = (int)((slice + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(decode_kernel(nb), dim3(p.n_wtiles), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace dec
 
-size_t decode_workspace_bytes(int64_t M, int64_t r) { return dec::decode_workspace_bytes(M, r); }
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  return dec::decode_workspace_bytes(M, N, K, r);
+}
+bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t r) {
+  return M <= 4 || dec::decode_supported(N, K, r);
+}
 size_t decode_wait_counter_offset() { return (size_t)dec::kGiveupCounter; }
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) { return dec::launch_decode_fwd(a, s); }
 

@@ -5,31 +5,32 @@
 // Y = bf16( X W_deq^T + s (X A^T) B^T )   (itwiki "QLoRA", section on the
 // computation; minnong511 "quantization", y = W x + (alpha/r) B A x).
 //
-// One launch does everything.  Its first workgroups are "LoRA-down" tiles,
-// which compute H = X A^T in parts and publish them; they never wait.  The
-// remaining workgroups are weight tiles, which stream the NF4 codes, wait
-// (bounded spin) for this launch's H, add s H B^T in fp32 and store bf16 Y.
-// Workgroups are dispatched in index order on this hardware, so the
-// LoRA-down tiles are running or done before any weight tile waits; nothing
-// depends on that for correctness: a wait that reaches its deadline (about
-// 1 ms) gives up, the waiting lane computes its H value itself from X and A,
-// and a give-up counter in the workspace records it for the caller.
+// One launch does everything.  Workgroups publish partial results (parts of
+// H = X A^T, and on the matrix-core path partial products of K slices) as
+// tagged words, and other workgroups of the same launch read them after
+// their own weight stream, polling (bounded spin) until the words carry this
+// launch's tag.  Workgroups are dispatched in index order on this hardware
+// and every producer publishes without waiting for anyone, so the words are
+// normally there; nothing depends on that for correctness: a wait that
+// reaches its deadline (about 1 ms) gives up, the waiting lane computes the
+// value itself from the layer's inputs, and a give-up counter in the
+// workspace records it for the caller.
 //
 // Launch epochs: every launch adds exactly 2^20 to each of the counters of a
 // group, however many workgroups share a counter, so a workgroup's own
 // counter update returns (epoch << 20) + something < 2^20, which names the
 // launch (the same epoch on every counter, whatever mix of shapes, with or
-// without adapter, used the workspace before).  LoRA-down tiles store each
+// without adapter, used the workspace before).  Producers store each
 // partial as one 64-bit word (epoch tag, value), so a partial is valid
 // exactly when its tag is this launch's; nothing has to be reset or waited
-// for on the producer side.  A weight tile's counter update goes out first
-// and its result is used only at the end, so its latency hides behind the
-// weight stream.
+// for on the producer side.  A workgroup's counter update goes out ahead of
+// its weight loads, so its latency hides behind them.
 //
 // Workspace layout (bytes): [128*(1+s)] weight counter s (u64, s < 8),
 // [128*9] give-up counter (u32), [128*(10+s)] LoRA-down counter s (u64, s < 8),
-// [kHpartOff..] tagged partial sums (u64: tag << 32 | fp32 bits).  Counters
-// sit 128 bytes apart so that their atomics do not queue on one cache line.
+// [kHpartOff..] tagged partial sums (u64: tag << 32 | fp32 bits) of H, then
+// (matrix-core path) of the K slices' products.  Counters sit 128 bytes
+// apart so that their atomics do not queue on one cache line.
 #pragma once
 
 #include "common.h"
@@ -40,8 +41,7 @@ namespace dec {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 16;          // output rows per weight tile
-constexpr int kHSplit = 4;         // K slices per LoRA-down row group
+constexpr int kRows = 16;          // output rows per GEMV weight tile
 constexpr int kSlots = 8;          // weight-tile epoch counters
 constexpr uint64_t kEpoch = uint64_t(1) << 20;
 // Deadline of a weight tile's wait for the LoRA-down products, in ticks of
@@ -66,10 +66,15 @@ struct DecodeParams {
   float scale;
   uint16_t* Y;
   float* H;        // H [M, r] for the caller, or null
-  uint64_t* Hpart; // [kHSplit][M][r16] tagged partial sums (r16 = r rounded up to 16)
+  uint64_t* Hpart; // tagged partial sums of H: GEMV [M][r16] (r16 = r rounded up to 16),
+                   // matrix-core path [S][M][r] (per K slice)
+  uint64_t* Ypart; // matrix-core path: tagged partial products exchanged between K slices
   char* ws;
-  int n_htiles;
-  int n_wtiles;
+  int n_htiles;    // GEMV: LoRA-down workgroups ahead of the weight tiles
+  int n_wtiles;    // workgroups that take a weight ticket
+  int G;           // matrix-core path: 64-row groups of N
+  int S;           // matrix-core path: K slices
+  int hcols;       // matrix-core path: LoRA-down columns per producing workgroup
   int c2_vec;      // rows of c2 start 4-byte aligned (K % 256 == 0): dword c2 loads
   int b_vec;       // r % 8 == 0 and B 16-byte aligned: 16-byte B loads
   uint32_t hi[16]; // bf16(kappa * level) per code
@@ -129,6 +134,15 @@ __device__ __forceinline__ uint64_t take_weight_ticket(const DecodeParams& p, in
   if (p.n_htiles == 0 && wt == 0)
     for (int s = 0; s < kSlots; ++s) add_ctr(reinterpret_cast<uint64_t*>(p.ws + kDownCtr + 128 * s), kEpoch);
   return ticket;
+}
+
+// This launch's epoch as workgroup i sees it without waiting on an atomic:
+// its counter's value shifted by 20.  Every launch adds exactly 2^20 to each
+// counter in shares, so while a launch runs each counter lies within
+// [epoch 2^20, (epoch + 1) 2^20) until its last share is added: a workgroup
+// reads its counter before adding its own share.
+__device__ __forceinline__ uint32_t slot_epoch(char* ws, int base, uint32_t i) {
+  return (uint32_t)(ld_ctr(reinterpret_cast<const uint64_t*>(ws + base + 128 * (i % kSlots))) >> 20);
 }
 
 __device__ __forceinline__ uint64_t take_down_ticket(const DecodeParams& p, int tile) {
@@ -304,8 +318,12 @@ inline DecodeParams decode_params(const FwdArgs& a) {
   p.Y = a.Y;
   p.ws = reinterpret_cast<char*>(a.workspace);
   p.Hpart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff);
+  p.Ypart = nullptr;
   p.H = a.H;
   p.n_htiles = 0;
+  p.G = 0;
+  p.S = 1;
+  p.hcols = 1;
   p.n_wtiles = (int)((a.N + kRows - 1) / kRows);
   p.c2_vec = (a.K % 256 == 0) && (reinterpret_cast<uintptr_t>(a.w.c2) % 4 == 0);
   p.b_vec = (a.r % 8 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 16 == 0);

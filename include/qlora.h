@@ -229,8 +229,10 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
  * that device current.  Arguments, results and status codes are those of
  * qlora_linear_fwd; a shape whose forward workspace
  * (qlora_linear_fwd_workspace) exceeds QLORA_NOALLOC_SCRATCH_BYTES is
- * rejected with QLORA_ESHAPE (every shape with M <= 16 fits, needing under
- * 70 KiB; so does, e.g., M = 64 with N = K = 4096, r = 64, at 8 MiB).
+ * rejected with QLORA_ESHAPE.  For M <= 4 the forward needs under 70 KiB;
+ * for 5 <= M <= 16 about 8 S N M bytes, S the K slices of that path (1 to
+ * 16): 2 MiB at M = 16 with N = K = 4096, 22 MiB (rejected here) for the
+ * 22016 x 8192 layer; M = 64 with N = K = 4096, r = 64 needs 8 MiB.
  * Every call on one GPU shares that GPU's scratch:
  * calls that overlap on one GPU (concurrent streams, or host threads that
  * use the same device) race and must not be made.  The scratch keeps the
@@ -242,11 +244,12 @@ int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M, int64_t N, int64_t K,
 
 /*
  * Byte offset, inside the forward workspace, of a uint32 counter.  For
- * M <= 16 one launch computes H = X A^T in some workgroups while the others
- * stream the weight and then wait, up to about 1 ms, for H; a wait that
- * reaches that deadline gives up, the waiting lanes compute their H values
- * themselves from X and A (Y and H_out stay correct), and the counter goes up
- * by one per lane that did so.  A nonzero count therefore means a launch ran
+ * M <= 16 the workgroups of one launch hand partial results to each other
+ * (parts of H = X A^T and, for 5 <= M <= 16, partial products of slices of
+ * K) and wait, up to about 1 ms, for the ones they need; a wait that reaches
+ * that deadline gives up, the waiting lane computes the value itself from
+ * the layer's inputs (Y and H_out stay correct), and the counter goes up by
+ * one per value so computed.  A nonzero count therefore means a launch ran
  * that slow fallback, e.g. because other work held the compute units.  The
  * library never resets the counter; the caller may zero these 4 bytes
  * between calls (read them after synchronizing the stream).

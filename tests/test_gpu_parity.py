@@ -278,7 +278,7 @@ def run_fwd(d, q, alpha, r, ws=None):
     before = qa.fwd_wait_count(ws)
     Y, H = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)
     torch.cuda.synchronize()
-    assert qa.fwd_wait_count(ws) == before, "a wait for the LoRA-down products gave up"
+    assert qa.fwd_wait_count(ws) == before, "a wait for a partial result gave up"
     return Y, H
 
 
@@ -350,13 +350,20 @@ def test_forward_one_hot_rows_select_weight_columns():
             assert np.max(np.abs(got - exp)) <= 1
 
 
+def shared_workspace(shapes):
+    """One zeroed forward workspace large enough for every (M, N, K, r)."""
+    need = max(qa.qlora_linear_fwd_workspace(*sh) for sh in shapes)
+    return torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+
+
 def test_forward_deterministic_and_workspace_reusable():
     """Repeated calls give identical bits, and one workspace serves any mix of
     shapes, ranks and layers without adapter (r = 0)."""
-    ws = qa.fwd_workspace(64, 2048, 1024, 72, "cuda")
+    shapes = ((1, 512, 512, 16), (16, 512, 512, 16), (64, 512, 512, 16), (3, 2048, 1024, 72),
+              (1, 100, 128, 8), (2, 512, 512, 0), (16, 2048, 1024, 72), (5, 300, 256, 0))
+    ws = shared_workspace(shapes)
     layers = {}
-    for M, N, K, r in ((1, 512, 512, 16), (16, 512, 512, 16), (64, 512, 512, 16), (3, 2048, 1024, 72),
-                       (1, 100, 128, 8), (2, 512, 512, 0), (16, 2048, 1024, 72), (5, 300, 256, 0)):
+    for M, N, K, r in shapes:
         d = synth.make_layer(synth.LayerShape("t", M=M, N=N, K=K, r=r, seed_offset=900 + M + N + r))
         layers[(M, N, K, r)] = (d, gpu_quantize(d["W"]))
     first = {}
@@ -403,7 +410,7 @@ def test_forward_graph_replay_matches_oracle_and_eager():
         M = Ms[i % 4]
         xb = synth.f32_to_bf16_bits(synth.normal_f32(5000 + i, (M, K), 1.0))
         calls.append((i % copies, xb, dev_bf16(xb), torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
-    ws = qa.fwd_workspace(64, N, K, r, "cuda")
+    ws = shared_workspace([(M, N, K, r) for M in Ms])
 
     def run_all():
         for c, _, X, Y in calls:
@@ -437,13 +444,18 @@ def test_forward_graph_replay_matches_oracle_and_eager():
 
 @pytest.mark.parametrize("M", [1, 8])
 def test_forward_wait_gives_up_and_stays_correct(M):
-    """Forced from the host: the workspace's LoRA-down launch counters are set
-    5 launches ahead of the weight counters, so the weight workgroups never see
-    this launch's tag on the published H partials.  Every wait reaches its
-    deadline (about 1 ms), the waiting lanes compute H themselves, every kernel
-    ends normally, Y and H still match the oracle, and the wait counter says
-    the fallback ran.  (Counter layout: eight 64-bit LoRA-down counters 128
-    bytes apart from byte 1280 of the workspace.)"""
+    """Forced from the host: launch counters of the workspace are set 5
+    launches ahead of the others, so some workgroups never see the tag they
+    wait for on the published partials.  At M = 1 (GEMV) the LoRA-down
+    counters move ahead of the weight counters: the weight workgroups never
+    see this launch's H.  At M = 8 (matrix-core path) half of the weight
+    counters move ahead: workgroups on different counters disagree on the
+    launch, so H partials and the K slices' exchanged products go missing.
+    Every wait reaches its deadline (about 1 ms), the waiting lanes compute
+    their values themselves, every kernel ends normally, Y and H still match
+    the oracle, and the wait counter says the fallback ran.  (Counter layout:
+    eight 64-bit weight counters 128 bytes apart from byte 128, eight
+    LoRA-down counters from byte 1280.)"""
     N, K, r, alpha = 512, 1024, 16, 16.0
     d = synth.make_layer(synth.LayerShape("t", M=M, N=N, K=K, r=r, seed_offset=4500 + M))
     _, wd = oracle_layer(d, alpha, r)
@@ -454,8 +466,9 @@ def test_forward_wait_gives_up_and_stays_correct(M):
     Y, H = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)     # one consistent launch first
     torch.cuda.synchronize()
     assert qa.fwd_wait_count(ws) == 0
-    for s in range(8):
-        ctr = ws[1280 + 128 * s:1280 + 128 * s + 8].view(torch.int64)
+    first, slots = (1280, range(8)) if M <= 4 else (128, range(4))
+    for s in slots:
+        ctr = ws[first + 128 * s:first + 128 * s + 8].view(torch.int64)
         ctr += 5 << 20
     torch.cuda.synchronize()
     say(f"[wait give-up] M={M}: launching with desynchronized counters")
