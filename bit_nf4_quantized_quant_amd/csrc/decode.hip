@@ -70,10 +70,25 @@ __device__ __forceinline__ float* spare(char* lut, int f) {
 __device__ __forceinline__ float* lower(char* lut, int f) {
   return reinterpret_cast<float*>(lut + ((f >> 5) << 8) + ((f & 31) << 2));
 }
-constexpr int kHredOff = 0;       // spare: [8 waves][16 m][16 cols] LoRA-down wave partials
-constexpr int kHpartsOff = 2048;  // spare: [S][M][nj] LoRA-down partials read back (<= 2048)
 constexpr int kYredOff = 0;       // spare: [8 waves][1024] product wave partials (after the LoRA-up)
 constexpr uint32_t kMissing = 0xFFFFFFFFu;   // a partial that never came (a NaN pattern)
+
+// Up to 2 blocks per wave (slice rows of at most 512 bytes) the tile's
+// packed codes are loaded a row at a time (consecutive lanes on consecutive
+// 16-byte pieces: whole cache lines per load) and staged in the pair table's
+// spare halves: byte b of row r in 128-byte piece 4 r + b / 128, its 32-byte
+// quarters rotated by r % 4 so that the rows one MFMA operand read touches
+// spread over the banks.  Longer slices load each MFMA operand straight from
+// memory (16 rows x 8 bytes per load), which keeps the LDS at 72 KiB there
+// too: two workgroups share a compute unit either way.
+template <int kNB>
+struct Stage {
+  static constexpr bool kOn = kNB <= 2;
+  static constexpr int kChunks = kOn ? 8 * kNB * 32 / 16 * kTileRows / kWaves / 64 : 1;   // 16-B loads per lane
+  __device__ static __forceinline__ char* at(char* lut, int row, int b) {
+    return lut + ((4 * row + (b >> 7)) << 8) + 128 + ((b & 127) ^ ((row & 3) << 5));
+  }
+};
 
 // Y[m][row] * kappa computed by one lane from X, the packed weight, A and B,
 // for an exchange whose partial never came; counted on the give-up counter.
@@ -110,8 +125,10 @@ __device__ __attribute__((noinline)) float lane_output(const uint16_t* X, const 
 // kNB: NF4 blocks per wave at most (the launcher's bound for this shape).
 template <int kNB>
 __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams p) {
-  // pair table (64 KiB); its spare halves hold the reductions
+  // pair table (64 KiB); its spare halves hold the staged codes and then the
+  // reductions
   __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];
+  __shared__ float hbuf[2048];   // LoRA-down wave partials, then the H partials read back
   __shared__ float lev[16];
   __shared__ uint32_t tag_lds;
   QLORA_FETCH_ARGS(p);
@@ -176,14 +193,33 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
       a[i][1] = ld128(ra, jrow * (uint32_t)K * 2 + kb + 16);
     }
   }
-  u32x2 cw[kNB][kGroups];
+  // The tile's codes, row by row: wave w loads rows 8 w .. 8 w + 7 of the
+  // slice, consecutive lanes on consecutive 16-byte pieces of a row (whole
+  // cache lines per load), for the LDS stage.  Pieces past the wave's rows
+  // repeat its last piece.
+  const int rowp = 2 * len;                    // 16-byte pieces per row of the slice
+  const int wpieces = 8 * rowp;                // the wave's pieces
+  u32x4 cv[Stage<kNB>::kChunks];
+  uint32_t cdst[Stage<kNB>::kChunks];
+  u32x2 cwd[Stage<kNB>::kOn ? 1 : kNB][kGroups];   // longer slices: the operands themselves
+  if constexpr (Stage<kNB>::kOn) {
 #pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
-    const uint32_t row = (uint32_t)(n0 + 16 * q + nl);
+    for (int u = 0; u < Stage<kNB>::kChunks; ++u) {
+      const int idx = min(u * 64 + lane, wpieces - 1);
+      const int rr = idx / rowp, cc = idx - rr * rowp;
+      const uint32_t row = (uint32_t)(n0 + 8 * wave + rr);
+      cv[u] = ld128(rc, row * (uint32_t)(K / 2) + (uint32_t)sb0 * 32u + (uint32_t)cc * 16u);
+      cdst[u] = (uint32_t)(Stage<kNB>::at(lut, 8 * wave + rr, cc * 16) - lut);
+    }
+  } else {
 #pragma unroll
-    for (int i = 0; i < kNB; ++i)
-      cw[i][q] = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, row * (uint32_t)(K / 2) + (uint32_t)blk[i] * 32u + 8u * g4, 0, 0));
+    for (int q = 0; q < kGroups; ++q) {
+      const uint32_t row = (uint32_t)(n0 + 16 * q + nl);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i)
+        cwd[i][q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  rc, row * (uint32_t)(K / 2) + (uint32_t)blk[i] * 32u + 8u * g4, 0, 0));
+    }
   }
   // Block constants with one lane per tile row (row n0 + lane): the c2 byte
   // of each of the wave's blocks, and c1 of its first and last block (a run
@@ -215,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
     }
     // th[v] = partial H[m = 4 g4 + v][column nl]
 #pragma unroll
-    for (int v = 0; v < 4; ++v) *spare(lut, kHredOff + wave * 256 + (4 * g4 + v) * 16 + nl) = th[v];
+    for (int v = 0; v < 4; ++v) hbuf[wave * 256 + (4 * g4 + v) * 16 + nl] = th[v];
   }
   if (threadIdx.x == 0) {
     asm volatile("" : "+v"(epoch));   // (keeps the use of the counter's value, and its wait, here)
@@ -228,9 +264,15 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
     if (m < M && col < count) {
       float h = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) h += *spare(lut, kHredOff + w * 256 + threadIdx.x);
+      for (int w = 0; w < kWaves; ++w) h += hbuf[w * 256 + threadIdx.x];
       st_tagged(&p.Hpart[((size_t)s * M + m) * r + g * hc + col], tag, h);
     }
+  }
+  // codes into the stage
+  if constexpr (Stage<kNB>::kOn) {
+#pragma unroll
+    for (int u = 0; u < Stage<kNB>::kChunks; ++u) *reinterpret_cast<u32x4*>(lut + cdst[u]) = cv[u];
+    __syncthreads();
   }
 
   // The weight stream: per block and row group, two MFMAs on bf16 levels and
@@ -249,10 +291,16 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
 #pragma unroll
     for (int q = 0; q < kGroups; ++q) {
       const float chat = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * q + nl), __float_as_int(chat_row)));
+      // 8 code bytes of row 16 q + nl: elements 16 g4 .. 16 g4 + 15 of the block
+      u32x2 cw;
+      if constexpr (Stage<kNB>::kOn)
+        cw = *reinterpret_cast<const u32x2*>(Stage<kNB>::at(lut, 16 * q + nl, (blk[i] - sb0) * 32 + 8 * g4));
+      else
+        cw = cwd[i][q];
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint32_t w = cw[i][q][h];
+        const uint32_t w = cw[h];
         u32x4 wv;
         wv[0] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<0>(w, lane4));
         wv[1] = *reinterpret_cast<const uint32_t*>(lut + pair_addr<1>(w, lane4));
@@ -319,7 +367,7 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
         float v;
         if (!poll_tagged(&p.Hpart[((size_t)sp * M + m) * r + jl + jj], hw[u], tag, deadline, &v))
           v = __uint_as_float(kMissing);
-        *spare(lut, kHpartsOff + idx) = v;
+        hbuf[idx] = v;
       }
     }
   }
@@ -334,7 +382,7 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
       float h = 0.f;
       bool missing = false;
       for (int sp = 0; sp < S; ++sp) {
-        const float v = *spare(lut, kHpartsOff + sp * M * nj + idx);
+        const float v = hbuf[sp * M * nj + idx];
         missing = missing || __float_as_uint(v) == kMissing;
         h += v;
       }
