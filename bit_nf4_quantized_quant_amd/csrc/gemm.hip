@@ -13,15 +13,18 @@
 // step.  2 x WN waves each own (BM/2) x (BN/WN) of the tile as 32x32x16 MFMA
 // accumulators: 4 waves for 128 x 128 tiles, 8 waves (two per SIMD, so one
 // wave's dequantization overlaps the other's MFMAs) for 256 x 256 tiles.
-// The forward product keeps its operands in fragment-major tiles (below)
-// with loads two steps ahead; the backward's products stage [rows][64 + 8]
-// bf16 tiles (reduction contiguous, 16-byte pad so that 16-byte fragment
-// reads of eight consecutive rows hit distinct banks).
+// The two products with the weight (forward Y and backward dX) keep their
+// operands in fragment-major tiles (below), or the weight in its own [n][k]
+// layout read by transposing LDS reads, with loads two steps ahead; the
+// skinny LoRA products stage [rows][64 + 8] bf16 tiles (reduction
+// contiguous, 16-byte pad so that 16-byte fragment reads of eight
+// consecutive rows hit distinct banks).
 //
 // Loaders turn every source layout into that LDS form:
-//   RowsBf16  bf16 [rows][red] (X, dY, A, B, and the bf16 H^T, dH^T)
-//   Nf4Rows   NF4 codes [rows][K/2] -> bf16 W_deq, bit-exact with the spec
-//   Nf4Cols   NF4 codes read as [red = n][rows = k]: the transposed weight for dX
+//   XRows     bf16 [rows][red] (X, dY) into fragment-major tiles
+//   WRows     NF4 codes [rows][K/2] -> bf16 W_deq rows (forward), bit-exact
+//   WNat      NF4 codes [n][K/2] -> bf16 W_deq in its own layout (dX)
+//   RowsBf16  bf16 [rows][red] (A, B, and the bf16 H^T, dH^T)
 //   ColsBf16  bf16 [red][rows] (transposed operands of the LoRA gradients)
 // A transposed source is read as 4 x 8 patches (4 rows of 8 contiguous
 // elements) and written to LDS as 8 rows of 4 reduction elements.
@@ -257,7 +260,9 @@ __device__ __forceinline__ int frag_read_slot(int lane, int s) {
 // row's 8-element chunks are 16-byte aligned.  A reduction tail past the row
 // end reads the next row (or zero past the tensor): finite values that the
 // other operand's zeros cancel.  kDepth: steps in flight in registers.
-template <int R, int T, bool kVec, int kDepth = 2>
+// kChecked: the step offset goes in the per-lane offset, which the buffer
+// range check covers, so a tail past the tensor's end reads 0.
+template <int R, int T, bool kVec, int kDepth = 2, bool kChecked = false>
 struct XRows {
   static constexpr int kChunks = R * BK / 8 / T;   // 16-byte chunks per thread: chunk c is
   static_assert(kChunks % 4 == 0, "whole chunks per quarter step");   // row (tid + c T) / 8, part (tid + c T) % 8
@@ -276,15 +281,16 @@ struct XRows {
   }
   template <int S>
   __device__ __forceinline__ void load(int kt) {
-    const int sof = kt * BK * 2;
+    const int sof = kChecked ? 0 : kt * BK * 2;
+    const uint32_t vof = kChecked ? (uint32_t)(kt * BK * 2) : 0u;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       if (kVec) {
-        reg[S][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[c], sof, 0));
+        reg[S][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[c] + vof, sof, 0));
       } else {
         uint32_t e[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, off[c] + 2 * q, sof, 0);
+        for (int q = 0; q < 8; ++q) e[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, off[c] + vof + 2 * q, sof, 0);
         reg[S][c] = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
       }
     }
@@ -399,58 +405,106 @@ struct WRows {
   }
 };
 
-// NF4 weight read transposed: tile row i = weight column k0 + i, reduction =
-// weight row n.  A thread takes patches of 4 rows (n) x 8 columns (k); the 8
-// columns lie in one block of each row, so a patch needs 4 constants.
-template <int R, int T = NT>
-struct Nf4Cols {
-  static constexpr int kPatches = 2 * R;
-  static constexpr int kPer = (kPatches + T - 1) / T;
-  const uint8_t* codes;
-  const uint8_t* c2;
-  const float* c1;
+// NF4 weight as the reduction-side operand of dX = dY W_deq: a step is 64
+// weight rows n (the reduction) by BN columns k (the output), expanded to
+// bf16( fp32(level * c_hat) ) (bit-exact with W_deq) into LDS in the
+// weight's own layout, [64 n][BN k] at a row stride of kRowBytes.  Unit c of
+// row n is 32 consecutive codes (one 16-byte load, one block constant) and
+// 64 bytes of LDS, whose four 16-byte pieces sit in the order P ^ swz(n, c):
+// with rows 64 (mod 256) bytes apart, the 16 lanes of a 16-byte store then
+// meet 16 different bank groups, and a transposing read (4 rows x 64 bytes
+// per half wave) still covers each row's unit whole.  Rows past N get
+// c_hat = 0, so they add nothing; step offsets go in the per-lane offset,
+// which the buffer range check covers, so codes past the tensor read 0.
+template <int BN, int T>
+struct WNat {
+  static_assert(BN == 128 || BN == 256, "tile widths with a conflict-free piece order");
+  static constexpr int kRowBytes = BN * 2 + 64;
+  static constexpr int kUnits = 64 * (BN / 32) / T;
+  static_assert(kUnits >= 1 && 64 * (BN / 32) % T == 0, "whole units per thread");
+  __host__ __device__ static constexpr int swz(int n, int c) {
+    return BN == 256 ? (((c >> 2) & 1) | ((n & 1) << 1)) : (n & 3);
+  }
+  rsrc_t rc, r2, r1;
+  uint32_t coff[kUnits];   // code bytes of the unit at step 0 (tile-relative)
+  uint32_t boff[kUnits];   // its block index at step 0 (tile-relative)
+  uint32_t bglob[kUnits];  // its global block index at step 0
+  uint32_t soff[kUnits];   // its LDS byte offset in a tile
+  int sw[kUnits];          // its piece order
+  uint32_t rstep, bstep;   // code bytes and blocks per 64 rows
+  int64_t N;
   float mean;
-  int64_t N, K;
-  int64_t col0;
   const float* lut;
-  uint32_t word[kPer][4];
-  float chat[kPer][4];
+  u32x4 q[2][kUnits];
+  uint32_t c2v[2][kUnits];
+  float c1v[2][kUnits];
+  int lim[2];              // rows of the step held in each slot that exist
+  float chat[kUnits];
 
-  __device__ __forceinline__ void load(int kt) {
+  __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* c2, const float* c1, float mu,
+                                       int64_t N_, int64_t K, int64_t k0, const float* lut_) {
+    const int64_t nb = K / BK;
+    N = N_;
+    rc = tile_rsrc(codes, k0 / 2, N * (K / 2));
+    r2 = tile_rsrc(c2, k0 / BK, N * nb);
+    r1 = tile_rsrc(c1, 0, ((N * nb + 255) / 256) * 4);
+    rstep = (uint32_t)(64 * (K / 2));
+    bstep = (uint32_t)(64 * nb);
+    mean = mu;
+    lut = lut_;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pid = threadIdx.x + u * T;
-      if (pid >= kPatches) break;
-      const int pr = pid % (BK / 4), pc = pid / (BK / 4);
-      const int64_t k = col0 + pc * 8;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = (int64_t)kt * BK + pr * 4 + q;
-        if (n < N && k < K) {
-          word[u][q] = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + k / 2);
-          const int64_t bi = n * (K / 64) + k / 64;
-          chat[u][q] = dequant_constant(c2[bi], c1[bi >> 8], mean);
-        } else {
-          word[u][q] = 0u;
-          chat[u][q] = 0.f;
-        }
-      }
+    for (int u = 0; u < kUnits; ++u) {
+      const int idx = threadIdx.x + u * T;
+      const int n = idx / (BN / 32), c = idx % (BN / 32);
+      coff[u] = (uint32_t)(n * (K / 2) + c * 16);
+      boff[u] = (uint32_t)(n * nb + c / 2);
+      bglob[u] = (uint32_t)(n * nb + k0 / BK + c / 2);
+      soff[u] = (uint32_t)(n * kRowBytes + c * 64);
+      sw[u] = swz(n, c);
     }
   }
-  __device__ __forceinline__ void store(lds_t* t) const {
+  template <int S>
+  __device__ __forceinline__ void load(int kt) {
+    lim[S] = (int)lmin(64, N - (int64_t)kt * 64);
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pid = threadIdx.x + u * T;
-      if (pid >= kPatches) break;
-      const int pr = pid % (BK / 4), pc = pid / (BK / 4);
-#pragma unroll
-      for (int z = 0; z < 8; ++z) {
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = __fmul_rn(lut[(word[u][q] >> (4 * z)) & 15u], chat[u][q]);
-        st_lds8(t + (pc * 8 + z) * PITCH + pr * 4, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
-      }
+    for (int u = 0; u < kUnits; ++u) {
+      q[S][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff[u] + kt * rstep, 0, 0));
+      c2v[S][u] = __builtin_amdgcn_raw_buffer_load_b8(r2, boff[u] + kt * bstep, 0, 0);
+      c1v[S][u] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(r1, ((bglob[u] + (uint32_t)kt * bstep) >> 8) * 4, 0, 0));
     }
+  }
+  template <int S, int P>
+  __device__ __forceinline__ void store_part(lds_t* t) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int n = (threadIdx.x + u * T) / (BN / 32);
+      if (P == 0) chat[u] = n < lim[S] ? dequant_constant(c2v[S][u], c1v[S][u], mean) : 0.f;
+      const uint32_t word = q[S][u][P];
+      const uint32_t lo4 = (word << 2) & 0x3C3C3C3Cu;   // 4 * low nibble of each byte
+      const uint32_t hi4 = (word >> 2) & 0x3C3C3C3Cu;   // 4 * high nibble of each byte
+      u32x4 o;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t al = byte_of(lo4, b), ah = byte_of(hi4, b);
+        const float lo = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + al), chat[u]);
+        const float hi = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + ah), chat[u]);
+        o[b] = pack_bf16x2(lo, hi);
+      }
+      st_lds16(reinterpret_cast<lds_t*>(reinterpret_cast<char*>(t) + soff[u] + 16 * (P ^ sw[u])), o);
+    }
+  }
+  __device__ __forceinline__ void prologue(int kt0, int last, lds_t* t) {
+    load<0>(kt0);
+    store_part<0, 0>(t);
+    store_part<0, 1>(t);
+    store_part<0, 2>(t);
+    store_part<0, 3>(t);
+    load<1>(min(kt0 + 1, last));
+  }
+  template <int S>
+  __device__ __forceinline__ void ahead(int kt, int last) {
+    load<S>(min(kt + 2, last));
   }
 };
 
@@ -549,6 +603,89 @@ __device__ __forceinline__ void mma_step_store(const lds_t* sa, const lds_t* sb,
   sub(std::integral_constant<int, 1>{});
   sub(std::integral_constant<int, 2>{});
   sub(std::integral_constant<int, 3>{});
+}
+
+// The step of mma_step_store with the B operand in the weight's own layout
+// (WNat): a 32x32x16 B fragment (operand rows = 32 output columns k, 16 of
+// the reduction n) is two gfx950 transposing reads.  In each 16-lane group
+// the transposing read hands lane i element e of source lane 4 e + i / 4's
+// 8 bytes, element i % 4; so with source lane j pointing at row n + j / 4,
+// columns k + 4 (j % 4) .. + 3, lane i receives rows n .. n + 3 of column
+// k + i.  Lanes 16 G .. 16 G + 15 take columns 16 (G % 2) + i of the
+// fragment and reduction elements 8 (G / 2) .. + 7 of the sub-step.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int BNT>
+__device__ __forceinline__ bf16x8 frag_tr(const lds_t* sb, int row0, int ps) {
+  using W = WNat<BNT, 128>;
+  const int lane = threadIdx.x & 63;
+  const int G = (lane >> 4) & 3, i = lane & 15;
+  const int n = 16 * ps + 8 * (G >> 1) + (i >> 2);   // (n + 4 has the same piece order)
+  const int c = row0 >> 5;                            // the unit (row0 is a multiple of 32)
+  const int piece = 2 * (G & 1) + ((i >> 1) & 1);
+  const char* base = reinterpret_cast<const char*>(sb) + n * W::kRowBytes + c * 64 +
+                     16 * (piece ^ W::swz(n, c)) + 8 * (i & 1);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + 4 * W::kRowBytes));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int BM, int BN, int WN, int S, class LA, class LB>
+__device__ __forceinline__ void mma_step_store_tr(const lds_t* sa, const lds_t* sb, Acc<BM, BN, WN>& acc, LA& la,
+                                                  LB& lb, lds_t* da, lds_t* db) {
+  constexpr int TM = Acc<BM, BN, WN>::TM, TN = Acc<BM, BN, WN>::TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto read = [&](int buf, int ps) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[buf][i] = __builtin_bit_cast(
+          bf16x8, ld16(sa + ((ps * (BM / 32) + (wm * (BM / 2) + i * 32) / 32) * 64 + frag_read_slot(lane, ps)) * 8));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[buf][j] = frag_tr<BN>(sb, wn * (BN / WN) + j * 32, ps);
+  };
+  auto sub = [&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (p < 3) read((p + 1) & 1, p + 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[p & 1][j], fa[p & 1][i], acc.c[i][j], 0, 0, 0);
+    la.template store_part<S, p>(da);
+    lb.template store_part<S, p>(db);
+  };
+  read(0, 0);
+  sub(std::integral_constant<int, 0>{});
+  sub(std::integral_constant<int, 1>{});
+  sub(std::integral_constant<int, 2>{});
+  sub(std::integral_constant<int, 3>{});
+}
+
+// run_pipelined with the B operand in the weight's own layout (SB bytes per
+// buffer: 64 rows of WNat<BN>::kRowBytes).
+template <int BM, int BN, int WN, class LA, class LB>
+__device__ __forceinline__ void run_pipelined_tr(LA& la, LB& lb, int kt0, int kt1, lds_t* sa, lds_t* sb,
+                                                 Acc<BM, BN, WN>& acc) {
+  if (kt0 >= kt1) return;
+  constexpr int SA = BM * BK, SB = 64 * WNat<BN, 128>::kRowBytes / 2;
+  const int last = kt1 - 1;
+  la.prologue(kt0, last, sa);
+  lb.prologue(kt0, last, sb);
+  __syncthreads();
+  for (int kt = kt0;; kt += 2) {
+    la.template ahead<0>(kt, last);
+    lb.template ahead<0>(kt, last);
+    mma_step_store_tr<BM, BN, WN, 1>(sa, sb, acc, la, lb, sa + SA, sb + SB);
+    __syncthreads();
+    if (kt + 1 > last) break;
+    la.template ahead<1>(kt + 1, last);
+    lb.template ahead<1>(kt + 1, last);
+    mma_step_store_tr<BM, BN, WN, 0>(sa + SA, sb + SB, acc, la, lb, sa, sb);
+    __syncthreads();
+    if (kt + 2 > last) break;
+  }
 }
 
 // The X/W product over steps [kt0, kt1) on fragment-major tiles (SA, SB bf16
@@ -738,10 +875,6 @@ __device__ __forceinline__ void tile_of(int L, int mtiles, int ntiles, int gm, i
 // dynamic LDS of the pipelined products (fragment-major tiles, two buffers)
 __host__ __device__ constexpr size_t frag_lds_bytes(int bm, int bn) {
   return (size_t)2 * (bm + bn) * BK * sizeof(lds_t);
-}
-
-__host__ __device__ constexpr size_t gemm_lds_bytes(int bm, int bn) {
-  return (size_t)2 * (bm + bn) * PITCH * sizeof(lds_t) + 16 * sizeof(float);
 }
 
 // Forward, M > 16: Y = bf16( X W_deq^T + (s H) B^T ).  Phase 1 streams X and
@@ -945,8 +1078,7 @@ __global__ void __launch_bounds__(256) reduce_hilo_kernel(const float* __restric
   }
 }
 
-// dX = dY W_deq + dH A (bf16 output).  Phase 1 contracts over n with the
-// transposed NF4 weight; phase 2 appends r steps of dH against A^T.
+// dX = dY W_deq + dH A (bf16 output, split-K partials when splits > 1).
 struct DxParams {
   const uint16_t* dY;
   int64_t M, N, K;
@@ -964,13 +1096,20 @@ struct DxParams {
   Nf4Table tab;
 };
 
-template <int BM, int BN, int WN>
-__global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
+// dX = dY W_deq + dH A (bf16 output), one product on the pipelined engine:
+// rows of dY (reduction n contiguous, zero past the tensor) against the
+// weight's codes expanded per step into its own [n][k] layout (WNat), which
+// the matrix cores take through transposing LDS reads; r more reduction
+// steps append dH against A.  No expanded copy of the weight is written:
+// the codes are the only weight bytes read.  kVecY: N % 8 == 0 (16-byte rows
+// of dY).
+template <int BM, int BN, int WN, bool kVecY>
+__global__ void __launch_bounds__(128 * WN) dxr_gemm_kernel(DxParams p) {
   constexpr int T = 128 * WN;
   extern __shared__ __attribute__((aligned(16))) lds_t smem[];
+  __shared__ float lut[16];
   lds_t* sa = smem;
-  lds_t* sb = smem + 2 * BM * PITCH;
-  float* lut = reinterpret_cast<float*>(sb + 2 * BN * PITCH);
+  lds_t* sb = smem + 2 * BM * BK;   // A fragment-major, B in the weight's layout; both double-buffered
   load_lut(lut, p.tab);
   const int tiles = p.mtiles * p.ntiles;
   const int split = uniform((int)blockIdx.x / tiles);
@@ -983,127 +1122,11 @@ __global__ void __launch_bounds__(128 * WN) dx_gemm_kernel(DxParams p) {
   zero(acc);
   __syncthreads();
   {
-    RowsBf16<BM, T> la{p.dY, p.N, (int)lmin(BM, p.M - m0), (int)p.N, m0, (p.N % 8) == 0};
-    Nf4Cols<BN, T> lb{p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut};
-    run_phase<BM, BN, WN>(la, lb, nt0, nt1, sa, sb, acc);
-  }
-  if (split == 0)
-    lora_tail<BM, BN, WN>(
-        acc, p.r,
-        [&](int i, int kk) { return frag_f32_row(p.dH, p.r, m0 + i, p.M, kk, p.r, 1.0f); },
-        [&](int j, int kk) { return frag_bf16_col(p.A, p.K, k0 + j, p.K, kk, p.r); });
-  // (dX is 16-byte aligned and K % 64 == 0: every group of four is aligned)
-  if (p.splits == 1) {
-    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
-      store4_bf16(p.dX, p.K, m0 + i, k0 + j, p.M, p.K, v, true);
-    });
-  } else {
-    float* out = p.part + (int64_t)split * p.M * p.K;
-    for_each_out4(acc, [&](int i, int j, const f32x4& v) {
-      store4_f32(out, p.K, m0 + i, k0 + j, p.M, p.K, v, true);
-    });
-  }
-}
-
-// ---------------------------------------------------------------- dX at large M
-// At large M the backward's dX = dY W_deq is a dense, compute-bound product
-// whose reduction runs over the weight's rows n.  The weight is then expanded
-// once per call into a scratch W_deq^T, bf16 [K][ldt] (ldt = N rounded up to
-// 64, zero past N), and the product runs on the pipelined bf16 engine with
-// both operands stored along the reduction.  The expansion moves 2.5 bytes
-// per weight (codes in, bf16 out), a few percent of the product's time at
-// M >= 512; below that the fused dx_gemm_kernel reads the codes directly.
-constexpr int64_t kDxtMinM = 512;
-constexpr int kDtN = 128, kDtK = 256;   // tile of the transposing expansion (n x k)
-
-// W_deq^T tile: thread t takes rows n0 + 2 (t % 64) + {0, 1} and the 32
-// columns k0 + 32 (t / 64) .. +31 (half a block of each row, so one constant
-// per row): one 16-byte code load per row, 8 threads covering 128
-// contiguous code bytes of a row.  It expands them to bf16 (fp32 level *
-// c_hat, bit-exact with W_deq) and stores (n, n+1) pairs per column into an
-// LDS tile [k][n]; the tile leaves as 256-byte rows of the output.
-__global__ void __launch_bounds__(512) nf4_dequant_t_kernel(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ c2,
-                                                            const float* __restrict__ c1,
-                                                            const float* __restrict__ mean, int64_t N, int64_t K,
-                                                            int64_t ldt, uint16_t* __restrict__ out, Nf4Table tab) {
-  __shared__ float lut[16];
-  __shared__ __attribute__((aligned(16))) uint32_t t[kDtK * kDtN / 2];   // [k][n pair], 64 KiB
-  load_lut(lut, tab);
-  const int64_t ntiles = (ldt + kDtN - 1) / kDtN;
-  const int64_t n0 = (int64_t)(blockIdx.x % ntiles) * kDtN, k0 = (int64_t)(blockIdx.x / ntiles) * kDtK;
-  const int np = threadIdx.x & 63, kg = threadIdx.x >> 6;
-  const int64_t kc = k0 + 32 * kg;
-  const float mu = *mean;
-  u32x4 w[2];
-  float chat[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t n = n0 + 2 * np + h;
-    if (n < N && kc < K) {
-      w[h] = ld16(codes + n * (K / 2) + kc / 2);
-      const int64_t bi = n * (K / 64) + kc / 64;
-      chat[h] = dequant_constant(c2[bi], c1[bi >> 8], mu);
-    } else {   // rows past N (and columns past K) expand to zero
-      w[h] = u32x4{0u, 0u, 0u, 0u};
-      chat[h] = 0.f;
-    }
-  }
-  __syncthreads();   // the level table
-#pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const float lo = __fmul_rn(lut[(w[0][e >> 3] >> (4 * (e & 7))) & 15u], chat[0]);
-    const float hi = __fmul_rn(lut[(w[1][e >> 3] >> (4 * (e & 7))) & 15u], chat[1]);
-    t[(32 * kg + e) * (kDtN / 2) + np] = pack_bf16x2(lo, hi);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kDtK * kDtN / 8 / 512; ++i) {
-    const int c = threadIdx.x + i * 512, kr = c >> 4, j = c & 15;
-    const int64_t k = k0 + kr, n = n0 + 8 * j;
-    if (k < K && n < ldt)
-      *reinterpret_cast<u32x4*>(out + k * ldt + n) = *reinterpret_cast<const u32x4*>(&t[kr * (kDtN / 2) + 4 * j]);
-  }
-}
-
-struct DxtParams {
-  const uint16_t* dY;
-  const uint16_t* wt;   // W_deq^T [K][ldt]
-  int64_t M, N, K, ldt;
-  int r;
-  const float* dH;
-  const uint16_t* A;
-  uint16_t* dX;
-  float* part;          // split-K partials [splits][M][K] (splits > 1)
-  int splits, steps_per_split;
-  int mtiles, ntiles, gm;
-};
-
-// dX = dY W_deq + dH A on the pipelined engine: rows of dY (reduction n
-// contiguous; past N they meet W_deq^T's zero columns) against rows of
-// W_deq^T.  kVecY: N % 8 == 0 (16-byte rows of dY).
-template <int BM, int BN, int WN, bool kVecY>
-__global__ void __launch_bounds__(128 * WN) dxt_gemm_kernel(DxtParams p) {
-  constexpr int T = 128 * WN;
-  extern __shared__ __attribute__((aligned(16))) lds_t smem[];
-  lds_t* sa = smem;
-  lds_t* sb = smem + 2 * BM * BK;   // fragment-major tiles, double-buffered
-  const int tiles = p.mtiles * p.ntiles;
-  const int split = uniform((int)blockIdx.x / tiles);
-  int mi, ki;
-  tile_of((int)blockIdx.x - split * tiles, p.mtiles, p.ntiles, p.gm, mi, ki);
-  const int64_t m0 = (int64_t)mi * BM, k0 = (int64_t)ki * BN;
-  const int nsteps = (int)(p.ldt / BK);
-  const int nt0 = split * p.steps_per_split, nt1 = min(nsteps, nt0 + p.steps_per_split);
-  Acc<BM, BN, WN> acc;
-  zero(acc);
-  __syncthreads();
-  {
-    XRows<BM, T, kVecY, (WN == 4 && kVecY ? 2 : 1)> la;
+    XRows<BM, T, kVecY, (WN == 4 && kVecY ? 2 : 1), true> la;
     la.init(p.dY, p.N, p.M, m0);
-    XRows<BN, T, true, (WN == 4 ? 2 : 1)> lb;
-    lb.init(p.wt, p.ldt, p.K, k0);
-    run_pipelined<BM, BN, WN>(la, lb, nt0, nt1, sa, sb, acc);
+    WNat<BN, T> lb;
+    lb.init(p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut);
+    run_pipelined_tr<BM, BN, WN>(la, lb, nt0, nt1, sa, sb, acc);
   }
   if (split == 0)
     lora_tail<BM, BN, WN>(
@@ -1121,6 +1144,10 @@ __global__ void __launch_bounds__(128 * WN) dxt_gemm_kernel(DxtParams p) {
       store4_f32(out, p.K, m0 + i, k0 + j, p.M, p.K, v, true);
     });
   }
+}
+
+__host__ __device__ constexpr size_t dxr_lds_bytes(int bm, int bn) {
+  return (size_t)2 * bm * BK * sizeof(lds_t) + (size_t)2 * 64 * (bn * 2 + 64);
 }
 
 // Skinny-product loaders with a per-tile origin, built on the loaders above.
@@ -1320,13 +1347,11 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Backward workspace: H (if recomputed), dH, their bf16 transposes, split-K
-// partials and, at large M, the expanded W_deq^T.
+// Backward workspace: H (if recomputed), dH, their bf16 transposes and
+// split-K partials.
 struct BwdPlan {
   int s_dh, s_db, s_da;
-  bool dxt;        // dX through the expanded W_deq^T
-  int64_t ldt;     // its row length (N rounded up to 64)
-  size_t off_H, off_dH, off_Ht, off_dHt, off_part, off_wt, bytes;
+  size_t off_H, off_dH, off_Ht, off_dHt, off_part, bytes;
 };
 
 // Split-K of a 128 x 128 skinny product: as many splits as keep all its
@@ -1351,12 +1376,9 @@ static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   b.off_part = b.off_dHt + al((size_t)M * r * 4);
   size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * 2 * r, (size_t)b.s_da * 2 * r * K}) * 4;
   part = std::max(part, lora_down_scratch_bytes(M, K, r));
-  b.dxt = M >= kDxtMinM && N > 0;
-  b.ldt = (N + 63) / 64 * 64;
-  const GemmPlan g = gemm_plan(M, K, b.dxt ? b.ldt / BK : (N + BK - 1) / BK);
+  const GemmPlan g = gemm_plan(M, K, (N + BK - 1) / BK);
   if (g.splits > 1) part = std::max(part, (size_t)g.splits * M * K * sizeof(float));
-  b.off_wt = b.off_part + al(part);
-  b.bytes = b.off_wt + (b.dxt ? al((size_t)b.ldt * K * 2) : 0);
+  b.bytes = b.off_part + al(part);
   return b;
 }
 
@@ -1416,37 +1438,7 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     }
   }
   // dX = dY W_deq + dH A
-  if (a.dX && a.M > 0 && plan.dxt) {
-    uint16_t* wt = reinterpret_cast<uint16_t*>(ws + plan.off_wt);
-    hipLaunchKernelGGL(nf4_dequant_t_kernel, dim3(cdiv(plan.ldt, kDtN) * cdiv(a.K, kDtK)), dim3(512), 0, s,
-                       a.w.codes, a.w.c2, a.w.c1, a.w.mean, a.N, a.K, plan.ldt, wt, code_table(a.w.table));
-    DxtParams p;
-    p.dY = a.dY;
-    p.wt = wt;
-    p.M = a.M;
-    p.N = a.N;
-    p.K = a.K;
-    p.ldt = plan.ldt;
-    p.r = (int)a.r;
-    p.dH = dH;
-    p.A = a.A;
-    p.dX = a.dX;
-    const GemmPlan g = gemm_plan(a.M, a.K, plan.ldt / BK);
-    p.part = part;
-    p.splits = g.splits;
-    p.steps_per_split = g.steps_per_split;
-    const bool vy = (a.N % 8) == 0;
-    if (g.tile == 256)
-      e = launch_tiled(vy ? dxt_gemm_kernel<256, 256, 4, true> : dxt_gemm_kernel<256, 256, 4, false>, 512,
-                       frag_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits, p, s);
-    else
-      e = launch_tiled(vy ? dxt_gemm_kernel<128, 128, 2, true> : dxt_gemm_kernel<128, 128, 2, false>, 256,
-                       frag_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits, p, s);
-    if (e != hipSuccess) return e;
-    if (g.splits > 1)
-      hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.K, 256), 4096)),
-                         dim3(256), 0, s, part, g.splits, (int64_t)(a.M * a.K), 1.0f, a.dX, (float*)nullptr);
-  } else if (a.dX && a.M > 0) {
+  if (a.dX && a.M > 0) {
     DxParams p;
     p.dY = a.dY;
     p.M = a.M;
@@ -1465,12 +1457,13 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     p.splits = g.splits;
     p.steps_per_split = g.steps_per_split;
     p.tab = code_table(a.w.table);
+    const bool vy = (a.N % 8) == 0;
     if (g.tile == 256)
-      e = launch_tiled(dx_gemm_kernel<256, 256, 4>, 512, gemm_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits,
-                       p, s);
+      e = launch_tiled(vy ? dxr_gemm_kernel<256, 256, 4, true> : dxr_gemm_kernel<256, 256, 4, false>, 512,
+                       dxr_lds_bytes(256, 256), g.mtiles, g.ntiles, g.splits, p, s);
     else
-      e = launch_tiled(dx_gemm_kernel<128, 128, 2>, 256, gemm_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits,
-                       p, s);
+      e = launch_tiled(vy ? dxr_gemm_kernel<128, 128, 2, true> : dxr_gemm_kernel<128, 128, 2, false>, 256,
+                       dxr_lds_bytes(128, 128), g.mtiles, g.ntiles, g.splits, p, s);
     if (e != hipSuccess) return e;
     if (g.splits > 1)
       hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.K, 256), 4096)),

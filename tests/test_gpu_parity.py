@@ -499,7 +499,8 @@ def test_forward_decode_layer_full_size(shape):
 
 # ------------------------------------------------------------------ backward
 
-# M >= 512 takes the expanded-W_deq^T product for dX (the last two: N % 8 == 0 and not)
+# dX runs on 128 x 128 tiles with split-K here (the last two with M >= 512: N % 8 == 0 and
+# not, so 16-byte and element-wise dY loads); the 65B-scale test below takes 256 x 256 tiles
 BWD_CASES = [(16, 256, 256, 8), (3, 100, 320, 5), (70, 130, 192, 16), (257, 300, 448, 72), (1, 64, 64, 1),
              (520, 600, 1280, 32), (512, 130, 320, 8)]
 
