@@ -295,6 +295,8 @@ struct XRows {
       }
     }
   }
+  template <int S, int P>
+  __device__ __forceinline__ void prep() {}
   // quarter P of the next step (register slot S when two steps are in flight)
   template <int S, int P>
   __device__ __forceinline__ void store_part(lds_t* t) const {
@@ -321,6 +323,31 @@ struct XRows {
   }
 };
 
+// Eight codes (one dword of packed nibbles) to eight bf16 weights,
+// bf16( fp32(level * c_hat) ), bit-exact with W_deq, in two halves: fetch8
+// issues one pair-table read per code byte (the table's byte address is the
+// whole LDS address), finish8 scales and rounds.  A product step issues the
+// reads of a sub-step before its matrix-core instructions and the rest after
+// them (the compiler schedules within that).
+struct Levels8 {
+  float2 v[4];
+};
+__device__ __forceinline__ Levels8 fetch8(uint32_t word, const float2* lut2) {
+  Levels8 l;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t off = ((word >> (8 * b)) & 0xFFu) * 8u;
+    l.v[b] = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(lut2) + off);
+  }
+  return l;
+}
+__device__ __forceinline__ u32x4 finish8(const Levels8& l, float chat) {
+  u32x4 o;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) o[b] = pack_bf16x2(__fmul_rn(l.v[b].x, chat), __fmul_rn(l.v[b].y, chat));
+  return o;
+}
+
 // NF4 weight rows [n][k] (forward): unit u of a thread is half a block (32
 // codes, one constant) of row (tid + u T) / 2, expanded to
 // bf16( fp32(level * c_hat) ), bit-exact with W_deq.
@@ -332,21 +359,22 @@ struct WRows {
   uint32_t boff[kUnits];   // its block index at kt = 0 (tile-relative)
   uint32_t bglob[kUnits];  // its global block index at kt = 0
   float mean;
-  const float* lut;
+  const float2* lut2;
   u32x4 q[2][kUnits];      // two steps in flight
   uint32_t c2v[2][kUnits];
   float c1v[2][kUnits];
   float chat[kUnits];      // constants of the step being stored
+  Levels8 lv[kUnits];      // levels of the chunk being stored
 
   __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* c2, const float* c1, float mu,
-                                       int64_t N, int64_t K, int64_t row0, const float* lut_) {
+                                       int64_t N, int64_t K, int64_t row0, const float2* lut2_) {
     const int rows = (int)lmin(R, N - row0);
     const int64_t nb = K / BK;
     rc = tile_rsrc(codes, row0 * (K / 2), N * (K / 2));
     r2 = tile_rsrc(c2, row0 * nb, N * nb);
     r1 = tile_rsrc(c1, 0, ((N * nb + 255) / 256) * 4);
     mean = mu;
-    lut = lut_;
+    lut2 = lut2_;
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       const int idx = threadIdx.x + u * T;
@@ -365,37 +393,33 @@ struct WRows {
       c1v[S][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ((bglob[u] + kt) >> 8) * 4, 0, 0));
     }
   }
-  // chunk P (8 codes) of every unit of the step held in slot S; the level
-  // table lives in static LDS, so a code's byte address (code * 4) is its
-  // whole ds_read address
+  // chunk P (8 codes) of every unit of the step held in slot S
   template <int S, int P>
   __device__ __forceinline__ void store_part(lds_t* t) {
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) store_unit<S, P>(t, u);
   }
   template <int S, int P>
+  __device__ __forceinline__ void prep() {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) lv[u] = fetch8(q[S][u][P], lut2);
+  }
+  template <int S, int P>
   __device__ __forceinline__ void store_unit(lds_t* t, int u) {
     if (P == 0) chat[u] = dequant_constant(c2v[S][u], c1v[S][u], mean);
     const int idx = threadIdx.x + u * T;
     const int row = idx >> 1, h = idx & 1;
-    const uint32_t word = q[S][u][P];
-    const uint32_t lo4 = (word << 2) & 0x3C3C3C3Cu;   // 4 * low nibble of each byte
-    const uint32_t hi4 = (word >> 2) & 0x3C3C3C3Cu;   // 4 * high nibble of each byte
-    u32x4 o;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t al = byte_of(lo4, b), ah = byte_of(hi4, b);
-      const float lo = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + al), chat[u]);
-      const float hi = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + ah), chat[u]);
-      o[b] = pack_bf16x2(lo, hi);
-    }
-    st_lds16(t + frag_slot<R>(row, 4 * h + P), o);
+    st_lds16(t + frag_slot<R>(row, 4 * h + P), finish8(lv[u], chat[u]));
   }
   __device__ __forceinline__ void prologue(int kt0, int last, lds_t* t) {
     load<0>(kt0);
+    prep<0, 0>();
     store_part<0, 0>(t);
+    prep<0, 1>();
     store_part<0, 1>(t);
+    prep<0, 2>();
     store_part<0, 2>(t);
+    prep<0, 3>();
     store_part<0, 3>(t);
     load<1>(min(kt0 + 1, last));
   }
@@ -410,9 +434,10 @@ struct WRows {
 // bf16( fp32(level * c_hat) ) (bit-exact with W_deq) into LDS in the
 // weight's own layout, [64 n][BN k] at a row stride of kRowBytes.  Unit c of
 // row n is 32 consecutive codes (one 16-byte load, one block constant) and
-// 64 bytes of LDS, whose four 16-byte pieces sit in the order P ^ swz(n, c):
-// with rows 64 (mod 256) bytes apart, the 16 lanes of a 16-byte store then
-// meet 16 different bank groups, and a transposing read (4 rows x 64 bytes
+// 64 bytes of LDS, whose four 16-byte pieces sit in the order P ^ swz(n, c).
+// A 16-byte store is served 8 lanes (128 bytes) at a time: with rows 64
+// (mod 128) bytes apart, the piece order puts each such group of lanes on 8
+// different 16-byte bank groups, and a transposing read (4 rows x 64 bytes
 // per half wave) still covers each row's unit whole.  Rows past N get
 // c_hat = 0, so they add nothing; step offsets go in the per-lane offset,
 // which the buffer range check covers, so codes past the tensor read 0.
@@ -423,7 +448,7 @@ struct WNat {
   static constexpr int kUnits = 64 * (BN / 32) / T;
   static_assert(kUnits >= 1 && 64 * (BN / 32) % T == 0, "whole units per thread");
   __host__ __device__ static constexpr int swz(int n, int c) {
-    return BN == 256 ? (((c >> 2) & 1) | ((n & 1) << 1)) : (n & 3);
+    return BN == 256 ? ((c >> 1) & 3) : (((c >> 1) & 1) | ((n & 1) << 1));
   }
   rsrc_t rc, r2, r1;
   uint32_t coff[kUnits];   // code bytes of the unit at step 0 (tile-relative)
@@ -434,15 +459,16 @@ struct WNat {
   uint32_t rstep, bstep;   // code bytes and blocks per 64 rows
   int64_t N;
   float mean;
-  const float* lut;
+  const float2* lut2;
   u32x4 q[2][kUnits];
   uint32_t c2v[2][kUnits];
   float c1v[2][kUnits];
   int lim[2];              // rows of the step held in each slot that exist
   float chat[kUnits];
+  Levels8 lv[kUnits];      // levels of the chunk being stored
 
   __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* c2, const float* c1, float mu,
-                                       int64_t N_, int64_t K, int64_t k0, const float* lut_) {
+                                       int64_t N_, int64_t K, int64_t k0, const float2* lut2_) {
     const int64_t nb = K / BK;
     N = N_;
     rc = tile_rsrc(codes, k0 / 2, N * (K / 2));
@@ -451,7 +477,7 @@ struct WNat {
     rstep = (uint32_t)(64 * (K / 2));
     bstep = (uint32_t)(64 * nb);
     mean = mu;
-    lut = lut_;
+    lut2 = lut2_;
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       const int idx = threadIdx.x + u * T;
@@ -475,30 +501,29 @@ struct WNat {
     }
   }
   template <int S, int P>
+  __device__ __forceinline__ void prep() {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) lv[u] = fetch8(q[S][u][P], lut2);
+  }
+  template <int S, int P>
   __device__ __forceinline__ void store_part(lds_t* t) {
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       const int n = (threadIdx.x + u * T) / (BN / 32);
       if (P == 0) chat[u] = n < lim[S] ? dequant_constant(c2v[S][u], c1v[S][u], mean) : 0.f;
-      const uint32_t word = q[S][u][P];
-      const uint32_t lo4 = (word << 2) & 0x3C3C3C3Cu;   // 4 * low nibble of each byte
-      const uint32_t hi4 = (word >> 2) & 0x3C3C3C3Cu;   // 4 * high nibble of each byte
-      u32x4 o;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t al = byte_of(lo4, b), ah = byte_of(hi4, b);
-        const float lo = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + al), chat[u]);
-        const float hi = __fmul_rn(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut) + ah), chat[u]);
-        o[b] = pack_bf16x2(lo, hi);
-      }
-      st_lds16(reinterpret_cast<lds_t*>(reinterpret_cast<char*>(t) + soff[u] + 16 * (P ^ sw[u])), o);
+      st_lds16(reinterpret_cast<lds_t*>(reinterpret_cast<char*>(t) + soff[u] + 16 * (P ^ sw[u])),
+               finish8(lv[u], chat[u]));
     }
   }
   __device__ __forceinline__ void prologue(int kt0, int last, lds_t* t) {
     load<0>(kt0);
+    prep<0, 0>();
     store_part<0, 0>(t);
+    prep<0, 1>();
     store_part<0, 1>(t);
+    prep<0, 2>();
     store_part<0, 2>(t);
+    prep<0, 3>();
     store_part<0, 3>(t);
     load<1>(min(kt0 + 1, last));
   }
@@ -566,6 +591,7 @@ __device__ __forceinline__ void run_phase(LA& la, LB& lb, int kt0, int kt1, lds_
   mma_tile<BM, BN, WN>(sa + cur * SA, sb + cur * SB, acc);
 }
 
+
 // One 64-deep step on LDS buffers (sa, sb), with the expansion of the next
 // step (register slot S -> LDS buffers da, db) spread over its four 16-deep
 // sub-steps, so that the dequantization VALU work issues between MFMAs.
@@ -590,6 +616,8 @@ __device__ __forceinline__ void mma_step_store(const lds_t* sa, const lds_t* sb,
   auto sub = [&](auto P) {
     constexpr int p = decltype(P)::value;
     if (p < 3) read((p + 1) & 1, p + 1);
+    la.template prep<S, p>();
+    lb.template prep<S, p>();
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -648,6 +676,8 @@ __device__ __forceinline__ void mma_step_store_tr(const lds_t* sa, const lds_t* 
   auto sub = [&](auto P) {
     constexpr int p = decltype(P)::value;
     if (p < 3) read((p + 1) & 1, p + 1);
+    la.template prep<S, p>();
+    lb.template prep<S, p>();
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -784,6 +814,15 @@ __device__ __forceinline__ void load_lut(float* lut, const Nf4Table& tab) {
   if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
 }
 
+// The pair table of the weight loaders: entry b = (level[b & 15], level[b >> 4]),
+// the two levels of code byte b (element 2i in the low nibble), so one 8-byte
+// LDS read serves two codes.  Built from the 16-entry table after a barrier.
+__device__ __forceinline__ void load_lut2(float2* lut2, float* lut, const Nf4Table& tab) {
+  load_lut(lut, tab);
+  __syncthreads();
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) lut2[b] = make_float2(lut[b & 15], lut[b >> 4]);
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xFFFFu); }
 
 // LoRA term appended to a tile's accumulators straight from global memory:
@@ -906,9 +945,10 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
   constexpr int T = 128 * WN;
   extern __shared__ __attribute__((aligned(16))) lds_t smem[];
   __shared__ float lut[16];
+  __shared__ float2 lut2[256];
   lds_t* sa = smem;
   lds_t* sb = smem + 2 * BM * BK;   // fragment-major tiles, double-buffered
-  load_lut(lut, p.tab);
+  load_lut2(lut2, lut, p.tab);
   const int tiles = p.mtiles * p.ntiles;
   const int split = uniform((int)blockIdx.x / tiles);
   int mi, ni;
@@ -923,7 +963,7 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
     XRows<BM, T, true, (WN == 4 ? 2 : 1)> la;
     la.init(p.X, p.K, p.M, m0);
     WRows<BN, T> lb;
-    lb.init(p.codes, p.c2, p.c1, *p.mean, p.N, p.K, n0, lut);
+    lb.init(p.codes, p.c2, p.c1, *p.mean, p.N, p.K, n0, lut2);
     run_pipelined<BM, BN, WN>(la, lb, kt0, kt1, sa, sb, acc);
   }
   if (split == 0)
@@ -1108,9 +1148,10 @@ __global__ void __launch_bounds__(128 * WN) dxr_gemm_kernel(DxParams p) {
   constexpr int T = 128 * WN;
   extern __shared__ __attribute__((aligned(16))) lds_t smem[];
   __shared__ float lut[16];
+  __shared__ float2 lut2[256];
   lds_t* sa = smem;
   lds_t* sb = smem + 2 * BM * BK;   // A fragment-major, B in the weight's layout; both double-buffered
-  load_lut(lut, p.tab);
+  load_lut2(lut2, lut, p.tab);
   const int tiles = p.mtiles * p.ntiles;
   const int split = uniform((int)blockIdx.x / tiles);
   int mi, ki;
@@ -1125,7 +1166,7 @@ __global__ void __launch_bounds__(128 * WN) dxr_gemm_kernel(DxParams p) {
     XRows<BM, T, kVecY, (WN == 4 && kVecY ? 2 : 1), true> la;
     la.init(p.dY, p.N, p.M, m0);
     WNat<BN, T> lb;
-    lb.init(p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut);
+    lb.init(p.codes, p.c2, p.c1, *p.mean, p.N, p.K, k0, lut2);
     run_pipelined_tr<BM, BN, WN>(la, lb, nt0, nt1, sa, sb, acc);
   }
   if (split == 0)
