@@ -1222,14 +1222,17 @@ hipError_t launch_skinny(const LA& la, const LB& lb, int64_t rows, int64_t cols,
 }
 
 // Split-K of a skinny product: double the splits while the workgroups number
-// under 512 and every split keeps at least 8 of the 64-deep steps (a split of
-// one or two steps spends its time on the prologue, and its partial costs
-// the reduction a round trip), at most 64.
-int pick_splits(int64_t tiles, int64_t ksteps) {
+// under 512 and every split keeps at least min_steps of the 64-deep steps, at
+// most 64.  The LoRA-down H = X A^T and dH = s dY B (r <= 128 columns, few
+// tiles) go down to 2 steps per split: their partials are small, and more
+// workgroups beat the prologue each one pays (3-5 us less at M = 64..512 on
+// the Llama MLP shapes than with 8 steps).
+int pick_splits(int64_t tiles, int64_t ksteps, int64_t min_steps) {
   int s = 1;
-  while (tiles * s < 512 && s * 2 * 8 <= ksteps && s < 64) s *= 2;
+  while (tiles * s < 512 && s * 2 * min_steps <= ksteps && s < 64) s *= 2;
   return s;
 }
+constexpr int64_t kLoraMinSteps = 2;
 
 }  // namespace
 
@@ -1243,7 +1246,7 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
   SRowsBf16<64> lb;
   lb.src = A; lb.ld = K; lb.red = (int)K; lb.vec = true;
   const int64_t ksteps = K / BK;
-  const int splits = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), ksteps);
+  const int splits = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), ksteps, kLoraMinSteps);
   float* out = splits == 1 ? H : scratch;
   hipError_t e = launch_skinny<128, 64>(la, lb, M, r, K, splits, out, s);
   if (e != hipSuccess || splits == 1) return e;
@@ -1253,7 +1256,7 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
 }
 
 size_t lora_down_scratch_bytes(int64_t M, int64_t K, int64_t r) {
-  const int splits = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), K / BK);
+  const int splits = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), K / BK, kLoraMinSteps);
   return splits == 1 ? 0 : (size_t)splits * M * r * sizeof(float);
 }
 
@@ -1406,7 +1409,7 @@ static int one_round_splits(int64_t tiles, int64_t ksteps) {
 
 static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   BwdPlan b;
-  b.s_dh = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), (N + BK - 1) / BK);
+  b.s_dh = pick_splits((int64_t)cdiv(M, 128) * cdiv(r, 64), (N + BK - 1) / BK, kLoraMinSteps);
   b.s_db = one_round_splits((int64_t)cdiv(N, 128) * cdiv(2 * r, 128), (M + BK - 1) / BK);
   b.s_da = one_round_splits((int64_t)cdiv(2 * r, 128) * cdiv(K, 128), (M + BK - 1) / BK);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
