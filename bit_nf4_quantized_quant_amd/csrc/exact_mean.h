@@ -88,12 +88,9 @@ QLORA_HD inline void shift_big(const uint32_t* x, int s, uint32_t* y) {
 
 // bucket[b] = sum of integer mantissas of the values whose max(exponent,1) is b.
 // Returns the fp32 bit pattern of the correctly rounded mean of n values.
-QLORA_HD inline uint32_t mean_from_buckets(const unsigned long long* bucket, uint64_t n) {
+// The rounded mean of S * 2^-149 over n values (S: kLimbs-limb integer).
+QLORA_HD inline uint32_t mean_from_sum(const uint32_t* S, uint64_t n) {
   using namespace detail;
-  uint32_t S[kLimbs];
-  for (int i = 0; i < kLimbs; ++i) S[i] = 0;
-  for (int b = 1; b < 255; ++b)
-    if (bucket[b]) add_shifted(S, bucket[b], b - 1);
   const int ls = bitlen_big(S);
   if (ls == 0 || n == 0) return 0u;
   const int ln = bitlen64(n);
@@ -101,9 +98,10 @@ QLORA_HD inline uint32_t mean_from_buckets(const unsigned long long* bucket, uin
   uint32_t T[kLimbs];
   shift_big(S, sh, T);
   bool sticky = sh < 0 ? !low_bits_zero(S, -sh) : false;
-  // long division of T by n in 16-bit digits (remainder < n < 2^48)
+  // long division of T by n in 16-bit digits (remainder < n < 2^48), from
+  // T's highest nonzero limb (the leading zero digits add nothing)
   uint64_t rem = 0, Q = 0;
-  for (int i = kLimbs - 1; i >= 0; --i) {
+  for (int i = (bitlen_big(T) + 31) / 32 - 1; i >= 0; --i) {
     for (int h = 1; h >= 0; --h) {
       const uint64_t cur = (rem << 16) | ((T[i] >> (16 * h)) & 0xFFFFu);
       const uint64_t q = cur / n;
@@ -127,6 +125,16 @@ QLORA_HD inline uint32_t mean_from_buckets(const unsigned long long* bucket, uin
     E += 1;
   }
   return ((uint32_t)(E + 127) << 23) | ((uint32_t)keep & 0x7FFFFFu);
+}
+
+// The rounded mean of n values from their exponent buckets (see above).
+QLORA_HD inline uint32_t mean_from_buckets(const unsigned long long* bucket, uint64_t n) {
+  using namespace detail;
+  uint32_t S[kLimbs];
+  for (int i = 0; i < kLimbs; ++i) S[i] = 0;
+  for (int b = 1; b < 255; ++b)
+    if (bucket[b]) add_shifted(S, bucket[b], b - 1);
+  return mean_from_sum(S, n);
 }
 
 }  // namespace qlora
