@@ -646,6 +646,43 @@ def test_forward_mlp_layer_full_size_sampled(name, N, K):
         check_fwd_sampled(d, ref, rows, Y, H, sh.alpha, sh.r, sh.name)
 
 
+def test_forward_256_tiles_every_output():
+    """A forward that runs on 256 x 256 tiles (M = 1000, N = 16320: 4 x 64
+    tiles, one per CU, the last row and column tiles ragged), every output
+    of Y and H against the oracle."""
+    M, N, K, r, alpha = 1000, 16320, 1024, 64, 16.0
+    say(f"[fwd 256 tiles] M={M} N={N} K={K} r={r}")
+    shape = synth.LayerShape("t256", M=M, N=N, K=K, r=r, seed_offset=9001)
+    d = synth.make_layer(shape)
+    _, wd = oracle_layer(d, alpha, r)
+    q = gpu_quantize(d["W"])
+    Y, H = qa.linear_fwd(dev_bf16(d["X"]), q, dev_bf16(d["A"]), dev_bf16(d["B"]), alpha)
+    torch.cuda.synchronize()
+    Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (256 x 256 tiles)")
+    check_close(host(H), Hr, "H (256 x 256 tiles)")
+
+
+def test_backward_256_tiles_every_output():
+    """A backward whose dX runs on 256 x 256 tiles (M = 1000, K = 16384: 4 x 64
+    tiles) with a ragged reduction (N = 1004: 15 full steps and 44 rows, dY
+    read element-wise since N % 8 != 0), every output of dX, dA and dB
+    against the oracle."""
+    M, N, K, r, alpha = 1000, 1004, 16384, 16, 16.0
+    say(f"[bwd 256 tiles] M={M} N={N} K={K} r={r}")
+    shape = synth.LayerShape("t256b", M=M, N=N, K=K, r=r, seed_offset=9002)
+    d = synth.make_layer(shape, with_dy=True)
+    _, wd = oracle_layer(d, alpha, r)
+    q = gpu_quantize(d["W"])
+    X, A, B, dY = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"]), dev_bf16(d["dY"])
+    dX, dA, dB = qa.linear_bwd(dY, X, q, A, B, alpha)
+    torch.cuda.synchronize()
+    g = oracle.linear_bwd(d["dY"], d["X"], wd, d["A"], d["B"], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(dX)), g["dX"], "dX (256 x 256 tiles)")
+    check_close(bf16_f64(host_bf16_bits(dA)), g["dA"], "dA")
+    check_close(bf16_f64(host_bf16_bits(dB)), g["dB"], "dB")
+
+
 def test_train65b_layer_full_size_sampled():
     """The 65B-scale training layer (W 22016 x 8192, M = 4096, r = 64) forward
     and backward: all constants, sampled rows of W_deq, sampled outputs of Y,
