@@ -17,7 +17,9 @@ namespace dec {
 namespace {
 
 // 16 output rows per workgroup.  Wave w takes rows 4 (w % 4) .. +3 of the
-// tile over one half of K (w / 4).  Per row, lane l reads 16 bytes of codes
+// tile over one half of K (w / 4).  (Layers that would need three or more
+// rounds of workgroups take 32-row tiles instead: wave w, rows 4 w .. +3
+// over all of K.)  Per row, lane l reads 16 bytes of codes
 // (32 codes inside one NF4 block), so a load instruction covers 1 KB of one
 // row.  Each wave loads the X values of its own pieces into registers, so no
 // wave waits for another before its dot products: they run while the rest
@@ -168,11 +170,15 @@ __device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_
 // kNPL: 16-byte pieces per lane and row (the launcher's exact count), or 0
 // for any count (the launcher takes 0 whenever the rows of c2 are not dword
 // aligned).
-template <int M, int kNPL>
+template <int M, int kNPL, bool kFull>
 __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red, uint32_t* tag_lds) {
   constexpr bool kDw = kNPL > 0;
+  constexpr int kTileRows = kFull ? 2 * kRows : kRows;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = wave & 3, half = wave >> 2;
+  // 16-row tiles: wave w takes rows 4 (w % 4) .. +3 over half w / 4 of K;
+  // 32-row tiles (kFull): rows 4 w .. +3 over all of K
+  const int grp = kFull ? wave : (wave & 3), half = kFull ? 0 : (wave >> 2);
+  const bool finisher = kFull || half == 1;   // adds the LoRA term and stores
   const float mu = load_mean(p);
   // this launch's epoch: thread 0's counter update goes out first, and its
   // reply, which comes back ahead of every later load, is used only at the
@@ -183,13 +189,13 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   uint32_t row[kGvRowsPerWave];
 #pragma unroll
   for (int rr = 0; rr < kGvRowsPerWave; ++rr)
-    row[rr] = (uint32_t)(tile * kRows + kGvRowsPerWave * grp + rr);
+    row[rr] = (uint32_t)(tile * kTileRows + kGvRowsPerWave * grp + rr);
   const uint32_t n_c2 = (uint32_t)p.N * (uint32_t)(p.K / 64);
   const rsrc_t rc = make_rsrc(p.codes, n_c2 * 32u);   // rows >= N read as zero codes
   const rsrc_t r2 = make_rsrc(p.c2, n_c2);
   const rsrc_t r1 = make_rsrc(p.c1, ((n_c2 + 255u) / 256u) * 4u);
   const rsrc_t rx = make_rsrc(p.X, (uint32_t)M * p.K * 2);
-  const int hp = p.K / 64;                 // pieces per row in each half of K
+  const int hp = kFull ? p.K / 32 : p.K / 64;   // pieces per row in the wave's range of K
   const int npl = (hp + 63) / 64;          // pieces per lane
   const uint32_t c0 = (uint32_t)(half * hp + lane);
   const uint32_t lane4 = (uint32_t)(lane & 31) * 4u;
@@ -206,7 +212,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   uint32_t bv[kGvRowsPerWave][2];
   uint64_t hv[M][2];
   auto read_lora = [&]() {
-    if (half == 1 && lora) {
+    if (finisher && lora) {
       const uint32_t last = (uint32_t)p.N - 1u;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -272,7 +278,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   // half add s H B^T (H from this launch's tagged partials, tag = epoch + 1,
   // polled until present), their own sums and the first half's, and store.
   const int rt = lane >> 4;   // this lane's row in the wave's group, if lane % 16 == 0
-  if (half == 0) {
+  if (!finisher) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float v[kGvRowsPerWave];
@@ -281,14 +287,14 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
       const float t = wave_sum4(v);
       if ((lane & 15) == 0) red[(grp * kGvRowsPerWave + rt) * M + m] = t;
     }
-    if (threadIdx.x == 0) {
-      // (the empty asm keeps the use of the reply here, at the end)
-      asm volatile("" : "+v"(ticket));
-      *tag_lds = (uint32_t)(ticket >> 20) + 1u;
-    }
+  }
+  if (threadIdx.x == 0) {
+    // (the empty asm keeps the use of the reply here, at the end)
+    asm volatile("" : "+v"(ticket));
+    *tag_lds = (uint32_t)(ticket >> 20) + 1u;
   }
   __syncthreads();
-  if (half == 0) return;
+  if (!finisher) return;
 
   if (lora) {
     const uint32_t tag = *tag_lds;
@@ -320,7 +326,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
     for (int rr = 0; rr < kGvRowsPerWave; ++rr) v[rr] = acc[rr][m];
     const float t = wave_sum4(v);
     if ((lane & 15) == 0 && row[0] + rt < (uint32_t)p.N) {
-      const float y = (t + red[(grp * kGvRowsPerWave + rt) * M + m]) * p.inv_kappa;
+      const float y = (kFull ? t : t + red[(grp * kGvRowsPerWave + rt) * M + m]) * p.inv_kappa;
       p.Y[(size_t)m * p.N + row[0] + rt] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFFu);
     }
   }
@@ -328,7 +334,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
 
 // Two workgroups per CU (4 waves per SIMD) up to M = 3; at M = 4 the X
 // registers need more, and one workgroup per CU runs faster than spilling.
-template <int M, int kNPL>
+template <int M, int kNPL, bool kFull>
 __global__ void __launch_bounds__(kThreads, M <= 3 ? 4 : 2) qlora_gemv_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];   // 64 KiB
   __shared__ float red[kRows * M];
@@ -341,18 +347,26 @@ __global__ void __launch_bounds__(kThreads, M <= 3 ? 4 : 2) qlora_gemv_kernel(De
     gemv_down_tile<M>(p, tile, red, &tag, hticket);
     return;
   }
-  gemv_tile<M, kNPL>(p, tile - p.n_htiles, lut, red, &tag);
+  gemv_tile<M, kNPL, kFull>(p, tile - p.n_htiles, lut, red, &tag);
 }
 
 typedef void (*GemvKernel)(DecodeParams);
 template <int M>
-GemvKernel gemv_kernel(int npl) {
+GemvKernel gemv_kernel(int npl, bool full) {
+  if (full) {   // 32-row tiles: whole pieces per lane over all of K (the launcher's condition)
+    switch (npl) {
+      case 1: return qlora_gemv_kernel<M, 1, true>;
+      case 2: return qlora_gemv_kernel<M, 2, true>;
+      case 3: return qlora_gemv_kernel<M, 3, true>;
+      default: return qlora_gemv_kernel<M, 4, true>;
+    }
+  }
   switch (npl) {
-    case 1: return qlora_gemv_kernel<M, 1>;
-    case 2: return qlora_gemv_kernel<M, 2>;
-    case 3: return qlora_gemv_kernel<M, 3>;
-    case 4: return qlora_gemv_kernel<M, 4>;
-    default: return qlora_gemv_kernel<M, 0>;
+    case 1: return qlora_gemv_kernel<M, 1, false>;
+    case 2: return qlora_gemv_kernel<M, 2, false>;
+    case 3: return qlora_gemv_kernel<M, 3, false>;
+    case 4: return qlora_gemv_kernel<M, 4, false>;
+    default: return qlora_gemv_kernel<M, 0, false>;
   }
 }
 
@@ -361,11 +375,23 @@ GemvKernel gemv_kernel(int npl) {
 hipError_t launch_gemv_fwd(const DecodeParams& p0, hipStream_t s) {
   DecodeParams p = p0;
   p.n_htiles = p.r;   // one LoRA-down workgroup per row of A
-  const int hp = p.K / 64, npl = p.c2_vec ? (hp + 63) / 64 : 0;
-  const GemvKernel k = p.M == 1 ? gemv_kernel<1>(npl)
-                      : p.M == 2 ? gemv_kernel<2>(npl)
-                      : p.M == 3 ? gemv_kernel<3>(npl)
-                                 : gemv_kernel<4>(npl);
+  // 32-row tiles where 16-row tiles need three or more rounds of resident
+  // workgroups (two per CU, one at M = 4) and 32-row tiles fewer, and every
+  // lane takes whole pieces of all of K (K a multiple of 2048, at most 4
+  // pieces, c2 rows dword-aligned).  The time steps with each round and
+  // grows little with a workgroup's bytes: 22016 x 4096, M = 1, r = 64
+  // 15.7 -> 13.8 us, 11008 x 4096 at M = 4 17.3 -> 16.3 us; from two rounds
+  // to one it was a toss-up (4096^2 at M = 4 slower by 10 %).
+  const int64_t slots = (p.M == 4 ? 1 : 2) * (int64_t)cu_count();
+  const int64_t t16 = (p.N + kRows - 1) / kRows, t32 = (p.N + 2 * kRows - 1) / (2 * kRows);
+  const int64_t rounds16 = (t16 + p.r + slots - 1) / slots, rounds32 = (t32 + p.r + slots - 1) / slots;
+  const bool full = p.c2_vec && p.K % 2048 == 0 && p.K / 2048 <= 4 && rounds16 >= 3 && rounds32 < rounds16;
+  if (full) p.n_wtiles = (int)t32;
+  const int hp = full ? p.K / 32 : p.K / 64, npl = p.c2_vec ? (hp + 63) / 64 : 0;
+  const GemvKernel k = p.M == 1 ? gemv_kernel<1>(npl, full)
+                      : p.M == 2 ? gemv_kernel<2>(npl, full)
+                      : p.M == 3 ? gemv_kernel<3>(npl, full)
+                                 : gemv_kernel<4>(npl, full);
   const dim3 grid(p.n_htiles + p.n_wtiles);
   hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();

@@ -646,6 +646,26 @@ def test_forward_mlp_layer_full_size_sampled(name, N, K):
         check_fwd_sampled(d, ref, rows, Y, H, sh.alpha, sh.r, sh.name)
 
 
+@pytest.mark.parametrize("M,N", [(1, 16400), (4, 9000)])
+def test_forward_gemv_32_row_tiles_every_output(M, N):
+    """The GEMV on 32-row tiles, which it takes when 16-row tiles would need
+    three or more rounds of resident workgroups and 32-row tiles fewer (M = 1,
+    N = 16400: 1089 workgroups become 577, the last tile 16 rows; M = 4, one
+    workgroup per CU, N = 9000: 627 become 346, the last tile 8 rows; K =
+    2048: one piece per lane over all of K), every output of Y and H against
+    the oracle."""
+    K, r, alpha = 2048, 64, 16.0
+    say(f"[gemv 32-row tiles] M={M} N={N} K={K} r={r}")
+    shape = synth.LayerShape("t32r", M=M, N=N, K=K, r=r, seed_offset=9100 + M)
+    d = synth.make_layer(shape)
+    _, wd = oracle_layer(d, alpha, r)
+    q = gpu_quantize(d["W"])
+    Y, H = run_fwd(d, q, alpha, r)
+    Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (32-row GEMV tiles)")
+    check_close(host(H), Hr, "H (32-row GEMV tiles)")
+
+
 def test_forward_256_tiles_every_output():
     """A forward that runs on 256 x 256 tiles (M = 1000, N = 16320: 4 x 64
     tiles, one per CU, the last row and column tiles ragged), every output
