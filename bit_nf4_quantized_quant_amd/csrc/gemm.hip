@@ -1118,6 +1118,257 @@ __global__ void __launch_bounds__(256) reduce_hilo_kernel(const float* __restric
   }
 }
 
+// ---------------------------------------------------------------- LoRA gradients in one pass over dY
+
+// itwiki "QLoRA", section on the computation: the output gradient dY reaches
+// the adapter through dH = s dY B (then dA = dH^T X) and dB = s dY^T H.  One
+// launch reads every element of dY once and forms both products from the same
+// LDS tile: workgroup (gm, gn) owns a run of 64-row tiles of dY and the C
+// 128-column chunks [n0, n0 + 128 C).  Per (tile, chunk) step the 8 waves
+//   - waves 0-3: dH[64 rows x 64 j] += dY tile . B chunk (rows read as they
+//     lie), a partial over this workgroup's columns, stored after the tile's
+//     last chunk into part_h[gn];
+//   - all waves: dB[128 n x 64 j] += dY^T . H for the tile (gfx950
+//     transposing LDS reads; H as bf16 hi and lo halves, both accumulated,
+//     fp32-like), kept in registers across the workgroup's tiles and stored
+//     at the end into part_b[gm].
+// Two small reductions (over gn and gm, in fixed order) finish dH and dB.
+// The B chunk, transposed to [j][n], stays in LDS for the whole workgroup.
+// Ranks up to 64 (multiples of 8) are padded to 64 with zeros.
+struct LgParams {
+  const uint16_t* dY;   // [M][N]
+  const uint16_t* B;    // [N][r]
+  const uint16_t* Ht;   // bf16 hi of H^T [r][M]; lo at Ht + r M
+  int64_t M, N;
+  int r;
+  int gm;               // workgroups along M
+  int mtiles;           // 64-row tiles of M
+  float* part_h;        // [gn][M][r]
+  float* part_b;        // [gm][N][r]
+};
+
+// A [64][128] bf16 tile in 256-byte rows of 16 pieces (8 elements each).
+// Piece p of row m sits at slot p ^ f(m), f mixing the row's low four bits,
+// so that the 16 rows of one piece (a row-wise fragment read) and 4 adjacent
+// rows of 4 adjacent pieces (a transposing read) each cover all 16 slots.
+__device__ __forceinline__ int dy_slot(int m, int piece) {
+  const int i = m & 15;
+  return piece ^ (((i & 3) << 2) | ((i >> 2) & 3));
+}
+// Rows m0 .. m0 + 31 of the tile, columns 16 ps + 8 (lane / 32) .. + 7:
+// the operand of a product that reduces over the tile's columns.
+__device__ __forceinline__ bf16x8 dy_frag_rows(const char* t, int m0, int ps) {
+  const int lane = threadIdx.x & 63;
+  const int m = m0 + (lane & 31);
+  return __builtin_bit_cast(bf16x8, ld16(t + m * 256 + 16 * dy_slot(m, 2 * ps + (lane >> 5))));
+}
+// Columns n0 .. n0 + 31 of the tile, rows 16 ps + 8 (lane / 32) .. + 7: the
+// operand of a product that reduces over the tile's rows, two transposing
+// reads (lane i of each 16-lane group receives 4 rows of column i; see
+// frag_tr).
+__device__ __forceinline__ bf16x8 dy_frag_cols(const char* t, int n0, int ps) {
+  const int lane = threadIdx.x & 63;
+  const int G = (lane >> 4) & 3, i = lane & 15;
+  const int m = 16 * ps + 8 * (G >> 1) + (i >> 2);
+  const int pc = (n0 >> 3) + 2 * (G & 1) + ((i >> 1) & 1);
+  const char* a0 = t + m * 256 + 16 * dy_slot(m, pc) + 8 * (i & 1);
+  const char* a1 = t + (m + 4) * 256 + 16 * dy_slot(m + 4, pc) + 8 * (i & 1);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// B chunk in LDS as [64 j][128 C n]; piece p of row j at slot p ^ (j & 15).
+template <int C>
+__device__ __forceinline__ int bt_off(int j, int piece) {
+  return j * (256 * C) + 16 * (piece ^ (j & 15));
+}
+// H^T tile in LDS as [hi, lo][64 j][64 m]; piece p of row j at p ^ ((j / 2) & 7).
+__device__ __forceinline__ int ht_off(int hl, int j, int piece) {
+  return hl * 8192 + j * 128 + 16 * (piece ^ ((j >> 1) & 7));
+}
+
+__host__ __device__ constexpr size_t lg_lds_bytes(int C) { return (size_t)2 * 16384 + 2 * 16384 + (size_t)16384 * C; }
+
+template <int C>
+__global__ void __launch_bounds__(512) lora_grads_kernel(LgParams p) {
+  static_assert(C == 2 || C == 4, "an even number of chunks keeps the register slot of a step a constant");
+  extern __shared__ __attribute__((aligned(16))) char lg_smem[];
+  char* sdy = lg_smem;            // 2 x 16 KB: dY tiles
+  char* sht = lg_smem + 32768;    // 2 x 16 KB: H^T hi/lo tiles
+  char* sbt = lg_smem + 65536;    // 16 C KB: the B chunk, transposed
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gm = uniform((int)blockIdx.x % p.gm), gn = uniform((int)blockIdx.x / p.gm);
+  const int t0 = (int)((int64_t)gm * p.mtiles / p.gm), t1 = (int)((int64_t)(gm + 1) * p.mtiles / p.gm);
+  const int ntiles = t1 - t0;
+  const int64_t m0 = (int64_t)t0 * 64, n0 = (int64_t)gn * 128 * C;
+  const int r = p.r;
+
+  // The B chunk, transposed: 4 rows n x 8 columns j per patch, written as
+  // 8 rows j of 4 columns n.  Rows past N read 0 (resource end); columns
+  // past r are 0.
+  {
+    const rsrc_t rb = make_rsrc(p.B, (uint32_t)(p.N * r * 2));
+#pragma unroll
+    for (int u = 0; u < C / 2; ++u) {
+      const int q = tid + 512 * u;
+      const int j0 = 8 * (q & 7), nl = 4 * (q >> 3);
+      u32x4 v[4];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        const int64_t n = n0 + nl + z;
+        v[z] = j0 < r && n < p.N
+                   ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(n * r + j0) * 2, 0, 0))
+                   : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x2 a = {lo16(v[0][w], v[1][w]), lo16(v[2][w], v[3][w])};
+        const u32x2 b = {hi16(v[0][w], v[1][w]), hi16(v[2][w], v[3][w])};
+        *reinterpret_cast<u32x2*>(sbt + bt_off<C>(j0 + 2 * w, nl >> 3) + 2 * (nl & 7)) = a;
+        *reinterpret_cast<u32x2*>(sbt + bt_off<C>(j0 + 2 * w + 1, nl >> 3) + 2 * (nl & 7)) = b;
+      }
+    }
+  }
+
+  // dY tile pieces (row q / 16, piece q % 16 of q = tid + 512 u) through a
+  // resource based at the workgroup's first row: rows past M read 0.  A
+  // chunk's columns past N read the next row, finite values that the zero
+  // columns of the B chunk cancel; their dB rows are not stored.
+  const rsrc_t rdy = tile_rsrc(p.dY, m0 * p.N * 2, p.M * p.N * 2);
+  uint32_t dyo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = tid + 512 * u;
+    dyo[u] = (uint32_t)(((q >> 4) * p.N + n0 + 8 * (q & 15)) * 2);
+  }
+  // H^T tile pieces: half u, row j = tid / 8, piece tid % 8; rows j >= r are 0.
+  const rsrc_t rht = make_rsrc(p.Ht, (uint32_t)(2 * (int64_t)r * p.M * 2));
+  const int hj = tid >> 3, hp = tid & 7;
+  const bool h_ok = hj < r;
+  uint32_t hto[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) hto[u] = (uint32_t)(((int64_t)u * r * p.M + (int64_t)hj * p.M + m0 + 8 * hp) * 2);
+
+  // C steps in flight: step (t, c) sits in register slot c.  Steps past the
+  // last tile load through an offset past every resource's end (zeros, no
+  // memory traffic) and store into the idle LDS buffer, so the loop carries
+  // no branches around its loads.
+  u32x4 ydr[C][2], htr[2];
+  auto load = [&](auto CC, int t) {
+    constexpr int c = decltype(CC)::value;
+    const bool live = t < ntiles;
+    const uint32_t so = (uint32_t)((64 * (int64_t)t * p.N + 128 * c) * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      ydr[c][u] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdy, live ? dyo[u] + so : 0xFFFFFFF0u, 0, 0));
+    if (c == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        htr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rht, live && h_ok ? hto[u] + (uint32_t)(t * 128) : 0xFFFFFFF0u, 0, 0));
+    }
+  };
+  auto store = [&](auto CC, int t) {
+    constexpr int c = decltype(CC)::value;
+    char* ty = sdy + (c & 1) * 16384;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 512 * u;
+      st_lds16(reinterpret_cast<lds_t*>(ty + (q >> 4) * 256 + 16 * dy_slot(q >> 4, q & 15)), ydr[c][u]);
+    }
+    if (c == 0) {
+      char* th = sht + (t & 1) * 16384;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) st_lds16(reinterpret_cast<lds_t*>(th + ht_off(u, hj, hp)), htr[u]);
+    }
+  };
+
+  f32x16 acc_h = {};
+  f32x16 acc_b[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc_b[c] = f32x16{};
+  bf16x8 hf[4], lf[4];
+  const int mh = wave & 1, jt = wave >> 1;    // dH: rows 32 mh.., columns 32 jt.. (waves 0-3)
+  const int nt = wave >> 1, jb = wave & 1;    // dB: chunk columns 32 nt.., columns 32 jb..
+
+  load(std::integral_constant<int, 0>{}, 0);
+  load(std::integral_constant<int, 1>{}, 0);
+  if constexpr (C == 4) {
+    load(std::integral_constant<int, 2>{}, 0);
+    load(std::integral_constant<int, 3>{}, 0);
+  }
+  store(std::integral_constant<int, 0>{}, 0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    auto step = [&](auto CC) {
+      constexpr int c = decltype(CC)::value;
+      const char* ty = sdy + (c & 1) * 16384;
+      load(std::integral_constant<int, c>{}, t + 1);
+      if (c == 0) {
+        const char* th = sht + (t & 1) * 16384;
+        const int j = 32 * jb + (lane & 31);
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) {
+          hf[ps] = __builtin_bit_cast(bf16x8, ld16(th + ht_off(0, j, 2 * ps + (lane >> 5))));
+          lf[ps] = __builtin_bit_cast(bf16x8, ld16(th + ht_off(1, j, 2 * ps + (lane >> 5))));
+        }
+      }
+      if (wave < 4) {
+        const int j = 32 * jt + (lane & 31);
+#pragma unroll
+        for (int ps = 0; ps < 8; ++ps) {
+          const bf16x8 a = dy_frag_rows(ty, 32 * mh, ps);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, ld16(sbt + bt_off<C>(j, 16 * c + 2 * ps + (lane >> 5))));
+          acc_h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc_h, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int ps = 0; ps < 4; ++ps) {
+        const bf16x8 a = dy_frag_cols(ty, 32 * nt, ps);
+        acc_b[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf[ps], a, acc_b[c], 0, 0, 0);
+        acc_b[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[ps], a, acc_b[c], 0, 0, 0);
+      }
+      if (c == C - 1 && wave < 4) {
+        // this tile's dH over the workgroup's columns
+        float* out = p.part_h + (int64_t)gn * p.M * r;
+        const int64_t m = m0 + 64 * (int64_t)t + 32 * mh + (lane & 31);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j = 32 * jt + 8 * g + 4 * (lane >> 5);
+          if (m < p.M && j < r)
+            *reinterpret_cast<f32x4*>(out + m * r + j) =
+                f32x4{acc_h[4 * g], acc_h[4 * g + 1], acc_h[4 * g + 2], acc_h[4 * g + 3]};
+        }
+        acc_h = f32x16{};
+      }
+      store(std::integral_constant<int, (c + 1) % C>{}, c + 1 < C ? t : t + 1);
+      __syncthreads();
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    if constexpr (C == 4) {
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+    }
+  }
+
+  // dB over this workgroup's rows
+  float* out = p.part_b + (int64_t)gm * p.N * r;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int64_t n = n0 + 128 * c + 32 * nt + (lane & 31);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j = 32 * jb + 8 * g + 4 * (lane >> 5);
+      if (n < p.N && j < r)
+        *reinterpret_cast<f32x4*>(out + n * r + j) =
+            f32x4{acc_b[c][4 * g], acc_b[c][4 * g + 1], acc_b[c][4 * g + 2], acc_b[c][4 * g + 3]};
+    }
+  }
+}
+
 // dX = dY W_deq + dH A (bf16 output, split-K partials when splits > 1).
 struct DxParams {
   const uint16_t* dY;
@@ -1391,8 +1642,34 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The single-pass LoRA-gradient launch: C chunks of 128 columns per
+// workgroup (4, or 2 for N <= 256), gn workgroups along N and as many along M
+// as keep the launch within one workgroup per CU (at least one 64-row tile
+// each).  It takes ranks that are multiples of 8 up to 64 and M, N multiples
+// of 8 (16-byte rows of H^T, dY and B); other layers use the three products.
+struct LgPlan {
+  bool ok;
+  int C, gn, gm, mtiles;
+  size_t part_h, part_b;   // partial bytes
+};
+static LgPlan lg_plan(int64_t M, int64_t N, int64_t r) {
+  LgPlan g{};
+  g.ok = M > 0 && N > 0 && r > 0 && r <= 64 && r % 8 == 0 && M % 8 == 0 && N % 8 == 0;
+  if (!g.ok) return g;
+  g.C = N > 256 ? 4 : 2;
+  g.gn = (int)cdiv(N, 128 * g.C);
+  g.mtiles = (int)cdiv(M, 64);
+  g.gm = (int)std::max<int64_t>(1, std::min<int64_t>(g.mtiles, cu_count() / g.gn));
+  // 32-bit buffer offsets: a workgroup's rows of dY, B and H^T
+  const int64_t rows = 64 * cdiv(g.mtiles, g.gm);
+  g.ok = rows * N * 2 < (1ll << 31) && N * r * 2 < (1ll << 31) && 2 * r * M * 2 < (1ll << 31);
+  g.part_h = (size_t)g.gn * M * r * sizeof(float);
+  g.part_b = (size_t)g.gm * N * r * sizeof(float);
+  return g;
+}
+
 // Backward workspace: H (if recomputed), dH, their bf16 transposes and
-// split-K partials.
+// split-K partials (or the single-pass launch's partials of dH and dB).
 struct BwdPlan {
   int s_dh, s_db, s_da;
   size_t off_H, off_dH, off_Ht, off_dHt, off_part, bytes;
@@ -1420,6 +1697,8 @@ static BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
   b.off_part = b.off_dHt + al((size_t)M * r * 4);
   size_t part = std::max({(size_t)b.s_dh * M * r, (size_t)b.s_db * N * 2 * r, (size_t)b.s_da * 2 * r * K}) * 4;
   part = std::max(part, lora_down_scratch_bytes(M, K, r));
+  const LgPlan lg = lg_plan(M, N, r);
+  if (lg.ok) part = std::max(part, al(lg.part_h) + lg.part_b);
   const GemmPlan g = gemm_plan(M, K, (N + BK - 1) / BK);
   if (g.splits > 1) part = std::max(part, (size_t)g.splits * M * K * sizeof(float));
   b.bytes = b.off_part + al(part);
@@ -1449,8 +1728,33 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     uint16_t* dHt = reinterpret_cast<uint16_t*>(ws + plan.off_dHt);
     const dim3 tgrid(cdiv(a.M, 16), cdiv(a.r, 64));
     if (a.M > 0) hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, H, a.M, a.r, Ht, Ht + a.r * a.M);
+    const LgPlan lg = lg_plan(a.M, a.N, a.r);
+    const bool one_pass = lg.ok && (reinterpret_cast<uintptr_t>(a.dY) % 16) == 0 &&
+                          (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
+    if (one_pass) {
+      // dH and dB from one read of dY, then their reductions
+      LgParams q;
+      q.dY = a.dY;
+      q.B = a.B;
+      q.Ht = Ht;
+      q.M = a.M;
+      q.N = a.N;
+      q.r = (int)a.r;
+      q.gm = lg.gm;
+      q.mtiles = lg.mtiles;
+      q.part_h = part;
+      q.part_b = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + ((lg.part_h + 255) & ~(size_t)255));
+      const auto kern = lg.C == 4 ? lora_grads_kernel<4> : lora_grads_kernel<2>;
+      if ((e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lg_lds_bytes(lg.C))) != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)(lg.gm * lg.gn)), dim3(512), lg_lds_bytes(lg.C), s, q);
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.M * a.r, 256)), dim3(256), 0, s, q.part_h, lg.gn,
+                         (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
+      hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, dH, a.M, a.r, dHt, dHt + a.r * a.M);
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, q.part_b, lg.gm,
+                         (int64_t)(a.N * a.r), a.scale, a.dB, (float*)nullptr);
+    }
     // dH = s dY B : rows m, cols j, reduction n
-    if (a.M > 0) {
+    if (a.M > 0 && !one_pass) {
       SRowsBf16<128> la;
       la.src = a.dY; la.ld = a.N; la.red = (int)a.N; la.vec = n_vec;
       SColsBf16<64> lb;
@@ -1461,7 +1765,7 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, dH, a.M, a.r, dHt, dHt + a.r * a.M);
     }
     // dB = s dY^T H : rows n, cols j, reduction m; H as [hi; lo] (2r columns)
-    if (a.N > 0) {
+    if (a.N > 0 && !one_pass) {
       SColsBf16<128> la;
       la.src = a.dY; la.ld = a.N; la.red = (int)a.M; la.vec = n_vec;
       SRowsBf16<128> lb;

@@ -258,11 +258,14 @@ size_t qlora_linear_fwd_wait_counter_offset(void);
 
 /*
  * Workspace bytes needed by qlora_linear_bwd: H (when recomputed), dH and
- * their bf16 transposes (16 M r bytes) and fp32 split-K partials of the LoRA
+ * their bf16 transposes (16 M r bytes) and fp32 partials of the LoRA
  * gradients and of dX, which grow with M r, N r and r K (and with M K only
- * when dX splits its reduction, at small M).  Nothing of the weight's size:
- * dX expands the codes on chip.  E.g. 36 MiB for N = 22016, K = 8192 at
- * M = 4096, r = 64; 2 MiB for N = K = 4096 at M = 1.
+ * when dX splits its reduction, at small M).  Where dH and dB come from one
+ * pass over dY (M, N and r multiples of 8, r <= 64), their partials take
+ * 4 r (gn M + gm N) bytes, gn = N / 512 column blocks and gm = CUs / gn row
+ * blocks.  Nothing of the weight's size: dX expands the codes on chip.  E.g.
+ * 74 MiB for N = 22016, K = 8192 at M = 4096, r = 64; 2 MiB for
+ * N = K = 4096 at M = 1.
  */
 size_t qlora_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
 
