@@ -504,11 +504,12 @@ def test_forward_decode_layer_full_size(shape):
 # tiles.  dH and dB come from the single pass over dY where M, N and r are multiples of 8 and
 # r <= 64: 16 x 256 (two 128-column chunks per workgroup), 520 x 600 (four chunks, ragged last
 # row tile and column block), 200 x 1032 (r = 24: ragged rows, columns and rank), 64 x 136
-# (a chunk of 8 columns), 640 x 22016 (two row tiles per workgroup) and 2112 x 4096 (33 row
-# tiles over 32 workgroups along M); the others take the three separate products.
+# (a chunk of 8 columns), 640 x 22016 (two row tiles per workgroup), 2112 x 4096 (33 row
+# tiles over 32 workgroups along M) and 136 x 1000 (r = 56: the second 32-wide rank tile
+# partly used); the others take the three separate products.
 BWD_CASES = [(16, 256, 256, 8), (3, 100, 320, 5), (70, 130, 192, 16), (257, 300, 448, 72), (1, 64, 64, 1),
              (520, 600, 1280, 32), (512, 130, 320, 8), (200, 1032, 192, 24), (64, 136, 128, 64),
-             (640, 22016, 64, 64), (2112, 4096, 64, 16)]
+             (640, 22016, 64, 64), (2112, 4096, 64, 16), (136, 1000, 128, 56)]
 
 
 @pytest.mark.parametrize("M,N,K,r", BWD_CASES)
