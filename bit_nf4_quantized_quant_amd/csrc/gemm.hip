@@ -1054,6 +1054,37 @@ __global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restr
   }
 }
 
+// Split-K partials of a column range of the output: out[i][j] (row stride
+// ld) = bf16(sum_s part[s][i][j]) for part [splits][rows][cols], the split
+// order fixed.  Four columns per thread when cols % 4 == 0 and the output
+// rows allow 8-byte stores.
+__global__ void __launch_bounds__(256) reduce_splits_cols_kernel(const float* __restrict__ part, int splits,
+                                                                 int64_t rows, int64_t cols,
+                                                                 uint16_t* __restrict__ out, int64_t ld) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t count = rows * cols;
+  const bool vec = (cols & 3) == 0 && (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0;
+  if (vec) {
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < count / 4; q += stride) {
+      const int64_t i = (4 * q) / cols, j = 4 * q - i * cols;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < splits; ++k) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)k * count + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += v[e];
+      }
+      *reinterpret_cast<u32x2*>(out + i * ld + j) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    }
+    return;
+  }
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < count; o += stride) {
+    float acc = 0.f;
+    for (int k = 0; k < splits; ++k) acc += part[(int64_t)k * count + o];
+    const int64_t i = o / cols;
+    out[i * ld + (o - i * cols)] = to_bf16(acc);
+  }
+}
+
 // out[c][r] = bf16(src[r][c]) for an fp32 src [rows][cols] (out row length
 // rows), and, with lo_out, lo_out[c][r] = bf16(src[r][c] - out[c][r]): the
 // pair carries each value to about 2^-17 relative, so the LoRA factors'
@@ -1548,9 +1579,37 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t steps) {
   return g;
 }
 
+// Large layers run on 256 x 256 tiles, one workgroup per CU.  When their
+// count leaves the last round of workgroups partly empty, the columns of
+// whole rounds stay on one launch and the remaining columns (at least a whole
+// 256 block of them) run as a second launch: 256 x 256 tiles split in two
+// along the reduction when twice their count fits one round (a split step
+// costs what a 256 step costs, against a 128 x 128 step at about 60 % of it
+// for a quarter of the work), else 128 x 128 tiles, two per CU.
+struct FwdTail {
+  int64_t n_main = 0;   // columns of the main launch; 0: no separate tail
+  bool split256 = false;
+  size_t scratch = 0;   // fp32 partials of the split tail
+};
+static FwdTail fwd_tail(const GemmPlan& g, int64_t M, int64_t N, int64_t ksteps) {
+  FwdTail t;
+  if (g.tile != 256 || g.splits != 1) return t;
+  const int64_t cus = cu_count();
+  const int64_t tiles = (int64_t)g.mtiles * g.ntiles, rounds = tiles / cus;
+  const int64_t n_main = rounds * cus / g.mtiles * 256;   // 256-wide column tiles of whole rounds
+  if (tiles % cus == 0 || rounds < 1 || n_main <= 0 || n_main >= N) return t;
+  const int64_t nn = N - n_main;
+  if (cdiv(M, 128) * cdiv(nn, 128) > 2 * cus) return t;
+  t.n_main = n_main;
+  t.split256 = ksteps >= 2 && 2 * (int64_t)g.mtiles * cdiv(nn, 256) <= cus;
+  t.scratch = t.split256 ? (size_t)2 * M * nn * sizeof(float) : 0;
+  return t;
+}
+
 size_t gemm_fwd_scratch_bytes(int64_t M, int64_t N, int64_t K) {
   const GemmPlan g = gemm_plan(M, N, K / BK);
-  return g.splits > 1 ? (size_t)g.splits * M * N * sizeof(float) : 0;
+  const size_t split = g.splits > 1 ? (size_t)g.splits * M * N * sizeof(float) : 0;
+  return std::max(split, fwd_tail(g, M, N, K / BK).scratch);
 }
 
 // Compute units of the current device (cached per device; thread-safe).
@@ -1616,24 +1675,21 @@ hipError_t launch_fwd_cols(const FwdArgs& a, int64_t n0, int64_t nn, int tile, i
   return launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, frag_lds_bytes(128, 128), mtiles, ntiles, splits, p, s);
 }
 
-// Large layers run on 256 x 256 tiles, one workgroup per CU.  When their
-// count leaves the last round of workgroups partly empty, the columns of
-// whole rounds stay on 256 x 256 tiles and the remaining columns (at least
-// a whole 256 block of them) run as a second launch on 128 x 128 tiles, two
-// per CU, whose single round takes a fraction of a 256 round.
 hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
   const GemmPlan g = gemm_plan(a.M, a.N, a.K / BK);
   hipError_t e;
-  if (g.tile == 256 && g.splits == 1) {
-    const int64_t cus = cu_count();
-    const int64_t tiles = (int64_t)g.mtiles * g.ntiles, rounds = tiles / cus;
-    const int64_t nt_main = rounds * cus / g.mtiles;         // 256-wide column tiles of whole rounds
-    const int64_t n_main = nt_main * 256;
-    const int64_t tail_tiles = cdiv(a.M, 128) * cdiv(a.N - n_main, 128);
-    if (tiles % cus != 0 && rounds >= 1 && n_main > 0 && n_main < a.N && tail_tiles <= 2 * cus) {
-      if ((e = launch_fwd_cols(a, 0, n_main, 256, 1, g.steps_per_split, scratch, s)) != hipSuccess) return e;
-      return launch_fwd_cols(a, n_main, a.N - n_main, 128, 1, (int)(a.K / BK), scratch, s);
-    }
+  const FwdTail t = fwd_tail(g, a.M, a.N, a.K / BK);
+  if (t.n_main > 0) {
+    if ((e = launch_fwd_cols(a, 0, t.n_main, 256, 1, g.steps_per_split, scratch, s)) != hipSuccess) return e;
+    const int64_t nn = a.N - t.n_main;
+    const int ksteps = (int)(a.K / BK);
+    if (!t.split256) return launch_fwd_cols(a, t.n_main, nn, 128, 1, ksteps, scratch, s);
+    const int half = (ksteps + 1) / 2;
+    if ((e = launch_fwd_cols(a, t.n_main, nn, 256, (int)cdiv(ksteps, half), half, scratch, s)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(reduce_splits_cols_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * nn, 1024), 4096)),
+                       dim3(256), 0, s, scratch, (int)cdiv(ksteps, half), a.M, nn, a.Y + t.n_main, a.N);
+    return hipGetLastError();
   }
   if ((e = launch_fwd_cols(a, 0, a.N, g.tile, g.splits, g.steps_per_split, scratch, s)) != hipSuccess) return e;
   if (g.splits == 1) return e;

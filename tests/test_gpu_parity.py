@@ -292,9 +292,10 @@ FWD_CASES = [
     # larger M: 128 x 128 tiles with split-K, a ragged M and r, one whole
     # round of 256 x 256 tiles
     (1024, 300, 448, 72), (1100, 600, 1280, 33), (2048, 8192, 256, 8),
-    # 16 x 18 tiles of 256: one whole round on 256 x 256 tiles, a ragged
-    # tail of 296 columns on 128 x 128 tiles
-    (4096, 4392, 128, 16),
+    # 16 x 18 tiles of 256: one whole round on 256 x 256 tiles and a ragged
+    # tail of 296 columns, on 256 x 256 tiles split in two along K (K = 128),
+    # or on 128 x 128 tiles where K = 64 leaves a single step
+    (4096, 4392, 128, 16), (4096, 4392, 64, 16),
 ]
 
 
@@ -688,6 +689,27 @@ def test_forward_256_tiles_every_output():
     Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], alpha, r)
     check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (256 x 256 tiles)")
     check_close(host(H), Hr, "H (256 x 256 tiles)")
+
+
+def test_forward_256_tiles_split_tail_every_output():
+    """A forward whose 256 x 256 tiles leave a partial last round (M = 512,
+    N = 33040: 2 x 130 tiles on 256 CUs): the columns of the whole round run
+    in one launch and the 272-column tail on 256 x 256 tiles split in two
+    along the reduction (K = 576: 5 and 4 steps; the last tile 16 columns
+    wide), reduced into Y's tail columns.  Every output of Y and H against
+    the oracle."""
+    M, N, K, r, alpha = 512, 33040, 576, 64, 16.0
+    say(f"[fwd split tail] M={M} N={N} K={K} r={r}")
+    shape = synth.LayerShape("t256t", M=M, N=N, K=K, r=r, seed_offset=9003)
+    d = synth.make_layer(shape)
+    _, wd = oracle_layer(d, alpha, r)
+    q = gpu_quantize(d["W"])
+    Y, H = qa.linear_fwd(dev_bf16(d["X"]), q, dev_bf16(d["A"]), dev_bf16(d["B"]), alpha)
+    torch.cuda.synchronize()
+    Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (split tail)")
+    check_close(bf16_f64(host_bf16_bits(Y))[:, 32768:], Yr[:, 32768:], "Y (tail columns)")
+    check_close(host(H), Hr, "H (split tail)")
 
 
 def test_backward_256_tiles_every_output():
