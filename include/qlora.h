@@ -184,7 +184,14 @@ int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const 
                 int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r, float alpha, uint16_t* W_out,
                 void* stream);
 
-/* Workspace bytes needed by qlora_linear_fwd. */
+/*
+ * Workspace bytes needed by qlora_linear_fwd: at M <= 16 the decode kernels'
+ * launch counters and tagged partials (under 70 KiB at M <= 4, about
+ * 8 S N M bytes for S slices of K above); at larger M, H (4 M r bytes) and
+ * fp32 partials of the LoRA-down and of the main product where it splits
+ * its reduction (at mid-size M, and the 256-tile tail of a large layer:
+ * 8 M x tail columns, e.g. 50 MB for N = 22016, K = 8192 at M = 4096).
+ */
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
 
 /*
