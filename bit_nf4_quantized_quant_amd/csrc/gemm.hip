@@ -1702,7 +1702,8 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
 // workgroup (4, or 2 for N <= 256), gn workgroups along N and as many along M
 // as keep the launch within one workgroup per CU (at least one 64-row tile
 // each).  It takes ranks that are multiples of 8 up to 64 and M, N multiples
-// of 8 (16-byte rows of H^T, dY and B); other layers use the three products.
+// of 8 (16-byte rows of H^T, dY and B); other layers form dH and dB as two
+// separate products, each reading dY.
 struct LgPlan {
   bool ok;
   int C, gn, gm, mtiles;
