@@ -495,6 +495,10 @@ def main():
     ap.add_argument("--train65b-only", action="store_true",
                     help="only the 65B-scale layer's forward and backward, --steps calls each, no JSON line "
                          "(for matrix-core counter runs)")
+    ap.add_argument("--decode-sizes-only", action="store_true",
+                    help="only the 4096x4096 forward at (M, r) = (1, 64), (8, 0), (8, 64), (16, 0), (16, 64), "
+                         "launched one by one, 2 warmup and --steps calls each, no JSON line "
+                         "(for per-dispatch counter runs of the decode kernels)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -516,6 +520,13 @@ def main():
         b = bench_bwd(torch, qa, sh.M, sh.N, sh.K, sh.r, args.steps, 1)
         log(f"[bench] {sh.name}: fwd {f['ms']:.3f} ms ({f['TFLOPs']:.0f} TFLOP/s), "
             f"bwd {b['ms']:.3f} ms ({b['TFLOPs']:.0f} TFLOP/s)")
+        return
+
+    if args.decode_sizes_only:
+        for M, rr in ((1, 64), (8, 0), (8, 64), (16, 0), (16, 64)):
+            cp = max(2, int(2 * MALL_BYTES / fwd_bytes(M, 4096, 4096, rr)) + 1)
+            res = bench_fwd(torch, qa, M, 4096, 4096, rr, args.steps, 2, cp, graph=False)
+            log(f"[bench] 4096x4096 M={M} r={rr}: {res['ms'] * 1e3:.2f} us/call")
         return
 
     N, K, r = 4096, 4096, 64
