@@ -1128,6 +1128,69 @@ __global__ void __launch_bounds__(256) f32_to_bf16_t_kernel(const float* __restr
   }
 }
 
+// The single pass's partials to the gradients in one launch: the first
+// hb = ceil(M/16) ceil(r/64) workgroups form dH = s sum_g part_h[g] on 16 x 64
+// tiles (four consecutive values per thread, 16-byte loads), store it (fp32
+// [M][r], for the dX product) and its bf16 hi and lo transposes [r][M] (the
+// dA product's operand, as f32_to_bf16_t_kernel writes them); the rest form
+// dB = bf16(s sum_g part_b[g]), four values per thread.  The sums run over
+// the partials in index order, as reduce_splits_kernel's do, so the results
+// are those of the three launches this replaces.  r % 8 == 0.
+__global__ void __launch_bounds__(256) lora_finish_kernel(const float* __restrict__ part_h, int gn,
+                                                          const float* __restrict__ part_b, int gm, int64_t M,
+                                                          int64_t N, int r, float scale, float* __restrict__ dH,
+                                                          uint16_t* __restrict__ dHt, uint16_t* __restrict__ dB) {
+  const int64_t cb = (r + 63) / 64, hb = ((M + 15) / 16) * cb;
+  const int64_t bid = blockIdx.x;
+  if (bid < hb) {
+    __shared__ float t[16][65];
+    const int64_t r0 = (bid / cb) * 16, c0 = (bid % cb) * 64;
+    const int tr = threadIdx.x >> 4, tc = 4 * (threadIdx.x & 15);   // row, first of four columns
+    const int64_t row = r0 + tr, col = c0 + tc;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (row < M && col < r) {
+      const float* q = part_h + row * r + col;
+#pragma unroll 4
+      for (int g = 0; g < gn; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(q + (int64_t)g * M * r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += v[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] *= scale;
+      *reinterpret_cast<f32x4*>(dH + row * r + col) = acc;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[tr][tc + e] = acc[e];
+    __syncthreads();
+    const int pr = threadIdx.x & 7, pc = threadIdx.x >> 3;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cc = pc + 32 * i;
+      const int64_t c = c0 + cc, rr = r0 + 2 * pr;
+      if (c >= r || rr >= M) continue;
+      const float x0 = t[2 * pr][cc], x1 = t[2 * pr + 1][cc];
+      const uint32_t v = pack_bf16x2(x0, x1);
+      store_pair_t(dHt, M, rr, c, v);
+      store_pair_t(dHt + (int64_t)r * M, M, rr, c, pack_bf16x2(x0 - bf16_lo(v), x1 - bf16_hi(v)));
+    }
+    return;
+  }
+  const int64_t count = N * r;
+  const int64_t q = (bid - hb) * 256 + threadIdx.x;
+  if (4 * q >= count) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int g = 0; g < gm; ++g) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part_b + (int64_t)g * count + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] *= scale;
+  *reinterpret_cast<u32x2*>(dB + 4 * q) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+}
+
 // Gradient of a LoRA factor from a product whose small operand came as hi
 // and lo bf16 halves: part[s] holds the product against [hi; lo], so
 // out[i][j] = bf16(scale * sum_s (part[s][i*pitch + j] + part[s][i*pitch + j + lo_off])).
@@ -1804,11 +1867,9 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
       const auto kern = lg.C == 4 ? lora_grads_kernel<4> : lora_grads_kernel<2>;
       if ((e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lg_lds_bytes(lg.C))) != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3((unsigned)(lg.gm * lg.gn)), dim3(512), lg_lds_bytes(lg.C), s, q);
-      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.M * a.r, 256)), dim3(256), 0, s, q.part_h, lg.gn,
-                         (int64_t)(a.M * a.r), a.scale, (uint16_t*)nullptr, dH);
-      hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, dH, a.M, a.r, dHt, dHt + a.r * a.M);
-      hipLaunchKernelGGL(reduce_splits_kernel, dim3(cdiv(a.N * a.r, 256)), dim3(256), 0, s, q.part_b, lg.gm,
-                         (int64_t)(a.N * a.r), a.scale, a.dB, (float*)nullptr);
+      const int64_t hb = (int64_t)cdiv(a.M, 16) * cdiv(a.r, 64), bb = cdiv(a.N * a.r, 1024);
+      hipLaunchKernelGGL(lora_finish_kernel, dim3((unsigned)(hb + bb)), dim3(256), 0, s, q.part_h, lg.gn, q.part_b,
+                         lg.gm, a.M, a.N, (int)a.r, a.scale, dH, dHt, a.dB);
     }
     // dH = s dY B : rows m, cols j, reduction n
     if (a.M > 0 && !one_pass) {
