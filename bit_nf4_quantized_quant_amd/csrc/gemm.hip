@@ -1227,12 +1227,13 @@ __global__ void __launch_bounds__(256) reduce_hilo_kernel(const float* __restric
 //     fp32-like), kept in registers across the workgroup's tiles and stored
 //     at the end into part_b[gm].
 // Two small reductions (over gn and gm, in fixed order) finish dH and dB.
-// The B chunk, transposed to [j][n], stays in LDS for the whole workgroup.
+// The B chunk, transposed to [j][n], stays in LDS for the whole workgroup;
+// each tile's rows of H come in as fp32 and enter LDS as H^T hi and lo.
 // Ranks up to 64 (multiples of 8) are padded to 64 with zeros.
 struct LgParams {
   const uint16_t* dY;   // [M][N]
   const uint16_t* B;    // [N][r]
-  const uint16_t* Ht;   // bf16 hi of H^T [r][M]; lo at Ht + r M
+  const float* H;       // [M][r] fp32 (split into bf16 hi and lo halves on the way into LDS)
   int64_t M, N;
   int r;
   int gm;               // workgroups along M
@@ -1335,19 +1336,21 @@ __global__ void __launch_bounds__(512) lora_grads_kernel(LgParams p) {
     const int q = tid + 512 * u;
     dyo[u] = (uint32_t)(((q >> 4) * p.N + n0 + 8 * (q & 15)) * 2);
   }
-  // H^T tile pieces: half u, row j = tid / 8, piece tid % 8; rows j >= r are 0.
-  const rsrc_t rht = make_rsrc(p.Ht, (uint32_t)(2 * (int64_t)r * p.M * 2));
-  const int hj = tid >> 3, hp = tid & 7;
-  const bool h_ok = hj < r;
-  uint32_t hto[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) hto[u] = (uint32_t)(((int64_t)u * r * p.M + (int64_t)hj * p.M + m0 + 8 * hp) * 2);
+  // H rows of a tile: thread tid loads H[m][j0 .. j0 + 7], m = tid % 64,
+  // j0 = 8 (tid / 64), and stores their bf16 hi and lo halves into the H^T
+  // tile (as f32_to_bf16_t_kernel rounds them); columns j >= r and rows past
+  // M read 0.
+  const rsrc_t rh = make_rsrc(p.H, (uint32_t)(p.M * r * 4));
+  const int hm = tid & 63, hj0 = 8 * (tid >> 6);
+  const bool h_ok = hj0 < r;
+  const uint32_t hoff = (uint32_t)(((m0 + hm) * r + hj0) * 4);
 
   // C steps in flight: step (t, c) sits in register slot c.  Steps past the
   // last tile load through an offset past every resource's end (zeros, no
   // memory traffic) and store into the idle LDS buffer, so the loop carries
   // no branches around its loads.
-  u32x4 ydr[C][2], htr[2];
+  u32x4 ydr[C][2];
+  f32x4 hrow[2];
   auto load = [&](auto CC, int t) {
     constexpr int c = decltype(CC)::value;
     const bool live = t < ntiles;
@@ -1359,8 +1362,9 @@ __global__ void __launch_bounds__(512) lora_grads_kernel(LgParams p) {
     if (c == 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        htr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rht, live && h_ok ? hto[u] + (uint32_t)(t * 128) : 0xFFFFFFF0u, 0, 0));
+        hrow[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rh, live && h_ok ? hoff + (uint32_t)(t * 256 * r) + 16 * u : 0xFFFFFFF0u,
+                                                0, 0));
     }
   };
   auto store = [&](auto CC, int t) {
@@ -1374,7 +1378,13 @@ __global__ void __launch_bounds__(512) lora_grads_kernel(LgParams p) {
     if (c == 0) {
       char* th = sht + (t & 1) * 16384;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) st_lds16(reinterpret_cast<lds_t*>(th + ht_off(u, hj, hp)), htr[u]);
+      for (int e = 0; e < 8; ++e) {
+        const float x = hrow[e >> 2][e & 3];
+        const uint32_t hi = pack_bf16x2(x, 0.f) & 0xFFFFu;
+        const uint32_t lo = pack_bf16x2(x - __uint_as_float(hi << 16), 0.f) & 0xFFFFu;
+        *reinterpret_cast<uint16_t*>(th + ht_off(0, hj0 + e, hm >> 3) + 2 * (hm & 7)) = (uint16_t)hi;
+        *reinterpret_cast<uint16_t*>(th + ht_off(1, hj0 + e, hm >> 3) + 2 * (hm & 7)) = (uint16_t)lo;
+      }
     }
   };
 
@@ -1782,7 +1792,7 @@ static LgPlan lg_plan(int64_t M, int64_t N, int64_t r) {
   g.gm = (int)std::max<int64_t>(1, std::min<int64_t>(g.mtiles, cu_count() / g.gn));
   // 32-bit buffer offsets: a workgroup's rows of dY, B and H^T
   const int64_t rows = 64 * cdiv(g.mtiles, g.gm);
-  g.ok = rows * N * 2 < (1ll << 31) && N * r * 2 < (1ll << 31) && 2 * r * M * 2 < (1ll << 31);
+  g.ok = rows * N * 2 < (1ll << 31) && N * r * 2 < (1ll << 31) && M * r * 4 < (1ll << 31);
   g.part_h = (size_t)g.gn * M * r * sizeof(float);
   g.part_b = (size_t)g.gm * N * r * sizeof(float);
   return g;
@@ -1847,16 +1857,18 @@ hipError_t launch_linear_bwd(const BwdArgs& a, hipStream_t s) {
     uint16_t* Ht = reinterpret_cast<uint16_t*>(ws + plan.off_Ht);
     uint16_t* dHt = reinterpret_cast<uint16_t*>(ws + plan.off_dHt);
     const dim3 tgrid(cdiv(a.M, 16), cdiv(a.r, 64));
-    if (a.M > 0) hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, H, a.M, a.r, Ht, Ht + a.r * a.M);
     const LgPlan lg = lg_plan(a.M, a.N, a.r);
     const bool one_pass = lg.ok && (reinterpret_cast<uintptr_t>(a.dY) % 16) == 0 &&
-                          (reinterpret_cast<uintptr_t>(a.B) % 16) == 0;
+                          (reinterpret_cast<uintptr_t>(a.B) % 16) == 0 && (reinterpret_cast<uintptr_t>(H) % 16) == 0;
+    // H^T as bf16 hi/lo for the separate dB product (the single pass splits H itself)
+    if (a.M > 0 && !one_pass)
+      hipLaunchKernelGGL(f32_to_bf16_t_kernel, tgrid, dim3(256), 0, s, H, a.M, a.r, Ht, Ht + a.r * a.M);
     if (one_pass) {
       // dH and dB from one read of dY, then their reductions
       LgParams q;
       q.dY = a.dY;
       q.B = a.B;
-      q.Ht = Ht;
+      q.H = H;
       q.M = a.M;
       q.N = a.N;
       q.r = (int)a.r;
