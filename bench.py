@@ -352,6 +352,55 @@ def bench_decoder_fused(torch, qa, reps, gen):
 
 # ----------------------------------------------------------------------------- traffic from counters
 
+def plain_gemm_reference(torch, M, N, K, steps=5):
+    """The stack's own dense bf16 GEMM (torch.matmul, dispatched to hipBLASLt) on
+    the same M x N x K, timed with HIP events, with the weight stored [K][N] and
+    [N][K] (the layer's own layout, multiplied as its transpose); the faster
+    is the reference for what the matrix cores reach on this shape without
+    any dequantization.  It is not part of the layer's path."""
+    x = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+    out = {"what": "torch.matmul bf16 (hipBLASLt), same M x N x K, no dequantization"}
+    for name, w, op in (("w_kn", torch.randn(K, N, device="cuda", dtype=torch.bfloat16), lambda w: w),
+                        ("w_nk", torch.randn(N, K, device="cuda", dtype=torch.bfloat16), lambda w: w.t())):
+        for _ in range(2):
+            torch.matmul(x, op(w))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.matmul(x, op(w))
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"{name}_ms"] = e0.elapsed_time(e1) / steps
+        del w
+    del x
+    out["ms"] = min(out["w_kn_ms"], out["w_nk_ms"])
+    out["TFLOPs"] = 2.0 * M * N * K / (out["ms"] * 1e-3) / 1e12
+    return out
+
+
+def plain_dx_reference(torch, M, N, K, steps=5):
+    """The stack's dense bf16 GEMM on the backward's dX shape, dY [M,N] times the
+    weight [N,K] as stored (torch.matmul, hipBLASLt), timed with HIP events: a
+    reference for the dX product, which takes most of the backward.  It is not
+    part of the layer's path."""
+    dy = torch.randn(M, N, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(dy, w)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(dy, w)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del dy, w
+    return {"what": "torch.matmul bf16 (hipBLASLt) of dY [M,N] and W [N,K], no dequantization", "ms": ms,
+            "TFLOPs": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
+
+
 def kernel_source_hash(names):
     """sha256[:16] over the kernel's source files, concatenated in order."""
     h = hashlib.sha256()
@@ -543,6 +592,7 @@ def main():
         torch.cuda.synchronize()
 
     extra = {}
+    plain = None
     if not args.quick:
         for M in (4, 16):
             res = bench_fwd(torch, qa, M, N, K, r, args.steps, args.warmup, copies)
@@ -559,7 +609,10 @@ def main():
         res = bench_fwd(torch, qa, Ml, Nl, Kl, r, 10, 2, 3, graph=False)
         extra["train65b_22016x8192_m4096_fwd"] = res
         log(f"[bench] 65B layer fwd M=4096: {res['ms']:.3f} ms, {res['TFLOPs']:.0f} TFLOP/s")
+        plain = plain_gemm_reference(torch, Ml, Nl, Kl)
+        log(f"[bench] plain bf16 GEMM {Ml}x{Nl}x{Kl}: {plain['ms']:.3f} ms, {plain['TFLOPs']:.0f} TFLOP/s")
         res = bench_bwd(torch, qa, Ml, Nl, Kl, r, 5, 1)
+        res["plain_dx_gemm"] = plain_dx_reference(torch, Ml, Nl, Kl)
         extra["train65b_22016x8192_m4096_bwd"] = res
         log(f"[bench] 65B layer bwd M=4096: {res['ms']:.3f} ms, {res['TFLOPs']:.0f} TFLOP/s")
         res = bench_quantize(torch, qa, Nl, Kl, 5, 1)
@@ -616,6 +669,8 @@ def main():
         f = extra["train65b_22016x8192_m4096_fwd"]
         line["m4096"] = {"workload": "train65b_22016x8192_m4096_fwd", "TFLOPs": round(f["TFLOPs"], 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(f["mfma_frac"], 4), "ms": f["ms"]}
+        if plain is not None:
+            line["m4096"]["attainable"] = {**plain, "frac_of_it": round(f["TFLOPs"] / plain["TFLOPs"], 4)}
     if not args.no_cpu:
         log("[bench] cpu oracle baseline ...")
         line["cpu_baseline"] = cpu_baseline()
