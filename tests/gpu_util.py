@@ -6,12 +6,15 @@ Frobenius error <= 5e-3 and max |err| <= 2e-2 * RMS(reference), each output
 checked against its own reference (fp32 accumulation of bf16 operands, bf16
 outputs).
 
-A rank-one output (the LoRA factors' gradients at M = 1 are outer products)
-has a max/RMS ratio of about the product of its two vectors' ratios, often
-above 10, so rounding even the exact result to bf16 (up to half an ulp, 2^-8
-relative) can exceed 2e-2 * RMS by itself.  For those outputs
-(``bf16_floor=True``) the max criterion is taken on the error beyond half a
-bf16 ulp of each reference value; the Frobenius criterion is unchanged.
+A low-rank output (the LoRA factors' gradients at small M are sums of M
+outer products) can have a max/RMS ratio of about the product of its vectors'
+ratios, often above 5-10, so rounding even the exact result to bf16 (up to
+half an ulp, 2^-8 relative) can exceed 2e-2 * RMS by itself.  For such an
+output the max criterion is taken on the error beyond half a bf16 ulp of each
+reference value: always with ``bf16_floor=True``, and with
+``bf16_floor="auto"`` exactly when the reference rounded once to bf16 misses
+the max criterion (so wherever a bf16 output can meet the plain rule, the
+plain rule applies).  The Frobenius criterion is unchanged.
 """
 
 import numpy as np
@@ -64,6 +67,10 @@ def check_close(got, ref, name, bf16_floor=False):
     rms = ref_norm / np.sqrt(ref.size)
     fro = np.linalg.norm(err) / max(ref_norm, 1e-300)
     aerr = np.abs(err)
+    if bf16_floor == "auto":
+        import oracle
+        rounded_err = np.abs(bf16_f64(oracle.bf16_round_f64(ref)) - ref)
+        bf16_floor = bool(rounded_err.size) and np.max(rounded_err) > MAX_TOL * rms
     if bf16_floor:
         aerr = np.maximum(aerr - half_ulp_bf16(ref), 0.0)
     mx = (np.max(aerr) if aerr.size else 0.0) / max(rms, 1e-300)

@@ -815,3 +815,21 @@ def test_check_close_bf16_floor():
     bad[1, 1] += 3e-2 * rms + half_ulp_bf16(ref[1, 1])
     with pytest.raises(AssertionError):
         check_close(bad, ref, "rank one", bf16_floor=True)
+    # "auto": the floor applies here, where the exactly rounded output misses
+    # the bar, and a real error beyond it still fails ...
+    check_close(got, ref, "rank one", bf16_floor="auto")
+    with pytest.raises(AssertionError):
+        check_close(bad, ref, "rank one", bf16_floor="auto")
+    # ... but not on a full-rank output, whose rounded values meet the plain
+    # rule: an error of 2.5e-2 x RMS (within half an ulp of a large element
+    # plus the bar) fails there without the floor
+    full = rng.standard_normal((300, 1024))
+    rms_f = np.linalg.norm(full) / np.sqrt(full.size)
+    got_f = bf16_f64(o.bf16_round_f64(full))
+    check_close(got_f, full, "full rank", bf16_floor="auto")
+    k = np.unravel_index(np.argmax(np.abs(full)), full.shape)
+    off = got_f.copy()
+    off[k] = full[k] + 2.5e-2 * rms_f
+    assert abs(off[k] - full[k]) - half_ulp_bf16(full[k]) < 2e-2 * rms_f   # the floor would hide it
+    with pytest.raises(AssertionError):
+        check_close(off, full, "full rank", bf16_floor="auto")
