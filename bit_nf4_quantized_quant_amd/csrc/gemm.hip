@@ -897,18 +897,29 @@ __device__ __forceinline__ int uniform(int v) {
 // range of logical tiles (a bijection of [0, T)), and walk logical tiles in
 // grouped-raster order (gm row tiles by every column tile), so the CUs of one
 // XCD work on a compact block of tiles and share X and W slices in their L2.
-__device__ __forceinline__ void tile_of(int L, int mtiles, int ntiles, int gm, int& mi, int& ni) {
-  const int T = mtiles * ntiles;
+__device__ __forceinline__ int xcd_logical(int L, int T) {
   const int x = L & 7, j = L >> 3;
   const int q = T >> 3, rem = T & 7;
-  const int logical = x * q + min(x, rem) + j;
+  return x * q + min(x, rem) + j;
+}
+// (per lane: the tile may differ across a wave)
+__device__ __forceinline__ void group_tile_lane(int logical, int mtiles, int ntiles, int gm, int& mi, int& ni) {
   const int per_group = gm * ntiles;
   const int group = logical / per_group;
   const int first_m = group * gm;
   const int gm_eff = min(gm, mtiles - first_m);
   const int in_group = logical - group * per_group;
-  mi = uniform(first_m + in_group % gm_eff);
-  ni = uniform(in_group / gm_eff);
+  mi = first_m + in_group % gm_eff;
+  ni = in_group / gm_eff;
+}
+// (workgroup-uniform `logical`)
+__device__ __forceinline__ void group_tile(int logical, int mtiles, int ntiles, int gm, int& mi, int& ni) {
+  group_tile_lane(logical, mtiles, ntiles, gm, mi, ni);
+  mi = uniform(mi);
+  ni = uniform(ni);
+}
+__device__ __forceinline__ void tile_of(int L, int mtiles, int ntiles, int gm, int& mi, int& ni) {
+  group_tile(xcd_logical(L, mtiles * ntiles), mtiles, ntiles, gm, mi, ni);
 }
 
 // dynamic LDS of the pipelined products (fragment-major tiles, two buffers)
@@ -938,6 +949,10 @@ struct FwdGemmParams {
   int splits, steps_per_split;
   int mtiles, ntiles, gm;
   Nf4Table tab;
+  // stream-K (fwd_gemm_sk_kernel): sk_w workgroups share the tiles' 64-deep
+  // steps; partial tiles go to slots of slot_rows x BN fp32 values in `part`
+  int sk_w;
+  int slot_rows;
 };
 
 template <int BM, int BN, int WN>
@@ -981,6 +996,101 @@ __global__ void __launch_bounds__(128 * WN) fwd_gemm_kernel(FwdGemmParams p) {
       store4_f32(out, p.N, m0 + i, n0 + j, p.M, p.N, v, (p.N & 3) == 0);
     });
   }
+}
+
+// Stream-K order of the forward product.  The steps of all tiles, tile after
+// tile (logical tile order, ksteps steps each: U = tiles x ksteps), are cut
+// into sk_w ranges [floor(l U / sk_w), floor((l + 1) U / sk_w)), one per
+// workgroup (l: its XCD-contiguous logical index), so every workgroup runs the
+// same number of steps give or take one, in one round of resident
+// workgroups, where split-K's fixed pieces leave the last round part empty.
+// A workgroup takes the pieces of its range tile by tile: a whole tile is
+// stored as bf16 at once; a piece of a tile goes, as fp32, to slot l + t (t:
+// the logical tile), which no other piece uses, and reduce_streamk_kernel sums
+// a tile's pieces in step order.  The LoRA term rides on the piece that holds
+// the tile's first step.
+__host__ __device__ __forceinline__ int64_t sk_owner(int64_t x, int64_t units, int w) {
+  return ((x + 1) * w - 1) / units;   // the range holding step x
+}
+
+template <int BM, int BN, int WN>
+__global__ void __launch_bounds__(128 * WN, 2) fwd_gemm_sk_kernel(FwdGemmParams p) {
+  constexpr int T = 128 * WN;
+  extern __shared__ __attribute__((aligned(16))) lds_t smem[];
+  __shared__ float lut[16];
+  __shared__ float2 lut2[256];
+  lds_t* sa = smem;
+  lds_t* sb = smem + 2 * BM * BK;
+  load_lut2(lut2, lut, p.tab);
+  const int tiles = p.mtiles * p.ntiles;
+  const int ksteps = (int)(p.K / BK);
+  const int64_t units = (int64_t)tiles * ksteps;
+  const int l = xcd_logical((int)blockIdx.x, p.sk_w);
+  const int64_t end = (int64_t)(l + 1) * units / p.sk_w;
+  for (int64_t pos = (int64_t)l * units / p.sk_w; pos < end;) {
+    const int t = uniform((int)(pos / ksteps));
+    const int kt0 = uniform((int)(pos - (int64_t)t * ksteps));
+    const int kt1 = uniform((int)min<int64_t>(ksteps, kt0 + (end - pos)));
+    int mi, ni;
+    group_tile(t, p.mtiles, p.ntiles, p.gm, mi, ni);
+    const int64_t m0 = (int64_t)mi * BM, n0 = (int64_t)ni * BN;
+    Acc<BM, BN, WN> acc;
+    zero(acc);
+    __syncthreads();   // the previous piece's last reads of the LDS tiles are done
+    {
+      XRows<BM, T, true, (WN == 4 ? 2 : 1)> la;
+      la.init(p.X, p.K, p.M, m0);
+      WRows<BN, T> lb;
+      lb.init(p.codes, p.c2, p.c1, *p.mean, p.N, p.K, n0, lut2);
+      run_pipelined<BM, BN, WN>(la, lb, kt0, kt1, sa, sb, acc);
+    }
+    if (kt0 == 0)
+      lora_tail<BM, BN, WN>(
+          acc, p.r,
+          [&](int i, int k0) { return frag_f32_row(p.H, p.r, m0 + i, p.M, k0, p.r, p.scale); },
+          [&](int j, int k0) { return frag_bf16_row(p.B, p.r, n0 + j, p.N, k0, p.r, p.b_vec); });
+    if (kt0 == 0 && kt1 == ksteps) {
+      for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+        store4_bf16(p.Y, p.ldy, m0 + i, n0 + j, p.M, p.N, v, p.y_vec);
+      });
+    } else {
+      float* out = p.part + (int64_t)(l + t) * p.slot_rows * BN;
+      for_each_out4(acc, [&](int i, int j, const f32x4& v) {
+        store4_f32(out, BN, i, j, p.slot_rows, BN, v, true);
+      });
+    }
+    pos += kt1 - kt0;
+  }
+}
+
+// Sum of the stream-K pieces of the tiles that more than one workgroup
+// shared: Y[m0 + i][n0 + j] = bf16(sum over the ranges l_first .. l_last
+// holding the tile's steps, in that order, of slot l + t).  One thread per
+// four columns of a slot row; tiles stored whole by one workgroup are skipped.
+__global__ void __launch_bounds__(256) reduce_streamk_kernel(const float* __restrict__ part, int tiles,
+                                                             int ksteps, int w, int mtiles, int ntiles, int gm,
+                                                             int slot_rows, int64_t M, int64_t N,
+                                                             uint16_t* __restrict__ Y, int64_t ldy, bool y_vec) {
+  constexpr int BN = 128;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tile = (int64_t)slot_rows * (BN / 4);
+  if (q >= (int64_t)tiles * per_tile) return;
+  const int t = (int)(q / per_tile);
+  const int i = (int)((q - t * per_tile) / (BN / 4)), j = 4 * (int)(q % (BN / 4));
+  const int64_t units = (int64_t)tiles * ksteps;
+  const int l0 = (int)sk_owner((int64_t)t * ksteps, units, w);
+  const int l1 = (int)sk_owner((int64_t)(t + 1) * ksteps - 1, units, w);
+  if (l0 == l1) return;
+  int mi, ni;
+  group_tile_lane(t, mtiles, ntiles, gm, mi, ni);
+  if ((int64_t)mi * 128 + i >= M) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int l = l0; l <= l1; ++l) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + ((int64_t)(l + t) * slot_rows + i) * BN + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+  }
+  store4_bf16(Y, ldy, (int64_t)mi * 128 + i, (int64_t)ni * BN + j, M, N, acc, y_vec);
 }
 
 // Generic bf16 x bf16 product with fp32 output (split-K partials or final):
@@ -1679,8 +1789,36 @@ static FwdTail fwd_tail(const GemmPlan& g, int64_t M, int64_t N, int64_t ksteps)
   return t;
 }
 
+// Stream-K (fwd_gemm_sk_kernel) on the 128 x 128 tiles where split-K (more
+// than one piece per tile: partials are written either way) would need more
+// than one round of resident workgroups (two per CU), and every range keeps
+// at least 32 steps.  Measured on MI355X, forward with r = 64: M = 384 and
+// 512 on 11008 x 4096 and M = 512 on 12288 x 4096 (32-48 steps per range)
+// 5-8 % faster; M = 256 on 11008 x 4096 (21.5 steps) 4 % slower, since a
+// step with two workgroups on every CU costs more than one in split-K's
+// lightly loaded second round; M = 1024 (no split: stream-K adds the
+// partials) 9 % slower.
+struct SkPlan {
+  bool on = false;
+  int w = 0, slot_rows = 0;
+  size_t scratch = 0;   // fp32 pieces: w + tiles - 1 slots of slot_rows x 128
+};
+static SkPlan sk_plan(const GemmPlan& g, int64_t M, int64_t ksteps) {
+  SkPlan k;
+  const int64_t slots = 2 * (int64_t)cu_count();
+  const int64_t tiles = (int64_t)g.mtiles * g.ntiles;
+  if (g.tile != 128 || g.splits < 2 || tiles * g.splits <= slots || tiles * ksteps < 32 * slots) return k;
+  k.on = true;
+  k.w = (int)slots;
+  k.slot_rows = (int)std::min<int64_t>(M, 128);
+  k.scratch = (size_t)(k.w + tiles - 1) * k.slot_rows * 128 * sizeof(float);
+  return k;
+}
+
 size_t gemm_fwd_scratch_bytes(int64_t M, int64_t N, int64_t K) {
   const GemmPlan g = gemm_plan(M, N, K / BK);
+  const SkPlan k = sk_plan(g, M, K / BK);
+  if (k.on) return k.scratch;
   const size_t split = g.splits > 1 ? (size_t)g.splits * M * N * sizeof(float) : 0;
   return std::max(split, fwd_tail(g, M, N, K / BK).scratch);
 }
@@ -1718,8 +1856,7 @@ hipError_t ensure_lds_limit(const void* kernel, size_t bytes) {
 
 // The forward product over output columns [n0, n0 + nn) of the layer (rows n0..
 // of the weight), with the given tile size and split.
-hipError_t launch_fwd_cols(const FwdArgs& a, int64_t n0, int64_t nn, int tile, int splits, int steps_per_split,
-                           float* scratch, hipStream_t s) {
+static FwdGemmParams fwd_params(const FwdArgs& a, int64_t n0, int64_t nn, float* scratch) {
   const int64_t nblk = a.K / BK;
   FwdGemmParams p;
   p.X = a.X;
@@ -1739,13 +1876,44 @@ hipError_t launch_fwd_cols(const FwdArgs& a, int64_t n0, int64_t nn, int tile, i
   p.ldy = a.N;
   p.y_vec = (reinterpret_cast<uintptr_t>(p.Y) % 8) == 0 && (a.N % 4) == 0;
   p.part = scratch;
+  p.tab = code_table(a.w.table);
+  p.sk_w = 0;
+  p.slot_rows = 0;
+  return p;
+}
+
+hipError_t launch_fwd_cols(const FwdArgs& a, int64_t n0, int64_t nn, int tile, int splits, int steps_per_split,
+                           float* scratch, hipStream_t s) {
+  FwdGemmParams p = fwd_params(a, n0, nn, scratch);
   p.splits = splits;
   p.steps_per_split = steps_per_split;
-  p.tab = code_table(a.w.table);
   const int mtiles = (int)cdiv(a.M, tile), ntiles = (int)cdiv(nn, tile);
   if (tile == 256)
     return launch_tiled(fwd_gemm_kernel<256, 256, 4>, 512, frag_lds_bytes(256, 256), mtiles, ntiles, splits, p, s);
   return launch_tiled(fwd_gemm_kernel<128, 128, 2>, 256, frag_lds_bytes(128, 128), mtiles, ntiles, splits, p, s);
+}
+
+// The stream-K product and the sum of its shared tiles.
+static hipError_t launch_fwd_sk(const FwdArgs& a, const GemmPlan& g, const SkPlan& k, float* scratch,
+                                hipStream_t s) {
+  FwdGemmParams p = fwd_params(a, 0, a.N, scratch);
+  p.splits = 1;
+  p.steps_per_split = (int)(a.K / BK);
+  p.sk_w = k.w;
+  p.slot_rows = k.slot_rows;
+  p.mtiles = g.mtiles;
+  p.ntiles = g.ntiles;
+  p.gm = g.mtiles >= 8 ? g.mtiles / 8 : 1;
+  const size_t lds = frag_lds_bytes(128, 128);
+  void (*kern)(FwdGemmParams) = fwd_gemm_sk_kernel<128, 128, 2>;
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)k.w), dim3(256), lds, s, p);
+  const int tiles = g.mtiles * g.ntiles;
+  const int64_t threads = (int64_t)tiles * k.slot_rows * 32;
+  hipLaunchKernelGGL(reduce_streamk_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, s, scratch, tiles,
+                     (int)(a.K / BK), k.w, g.mtiles, g.ntiles, p.gm, k.slot_rows, a.M, a.N, a.Y, a.N, p.y_vec);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
@@ -1764,6 +1932,8 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, float* scratch, hipStream_t s) {
                        dim3(256), 0, s, scratch, (int)cdiv(ksteps, half), a.M, nn, a.Y + t.n_main, a.N);
     return hipGetLastError();
   }
+  const SkPlan k = sk_plan(g, a.M, a.K / BK);
+  if (k.on) return launch_fwd_sk(a, g, k, scratch, s);
   if ((e = launch_fwd_cols(a, 0, a.N, g.tile, g.splits, g.steps_per_split, scratch, s)) != hipSuccess) return e;
   if (g.splits == 1) return e;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(a.M * a.N, 256), 4096)),

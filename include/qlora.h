@@ -189,8 +189,10 @@ int qlora_merge(const uint8_t* codes, const uint8_t* c2, const float* c1, const 
  * launch counters and tagged partials (under 70 KiB at M <= 4, about
  * 8 S N M bytes for S slices of K above); at larger M, H (4 M r bytes) and
  * fp32 partials of the LoRA-down and of the main product where it splits
- * its reduction (at mid-size M, and the 256-tile tail of a large layer:
- * 8 M x tail columns, e.g. 50 MB for N = 22016, K = 8192 at M = 4096).
+ * its reduction (at mid-size M: split-K, splits x 4 M N bytes, or stream-K
+ * pieces of 64 KiB each, 2 x CUs + tiles - 1 of them, e.g. 56 MB for
+ * N = 11008 at M = 512; and the 256-tile tail of a large layer: 8 M x tail
+ * columns, e.g. 50 MB for N = 22016, K = 8192 at M = 4096).
  */
 size_t qlora_linear_fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
 

@@ -712,6 +712,39 @@ def test_forward_256_tiles_split_tail_every_output():
     check_close(host(H), Hr, "H (split tail)")
 
 
+STREAM_K_CASES = [
+    # (M, N, K, r): 128 x 128 tiles whose split-K plan (two pieces per tile)
+    # needs more than one round of resident workgroups (two per CU on 256
+    # CUs), so the steps are shared out stream-K, at least 32 per workgroup
+    (1000, 4200, 4032, 16),  # 8 x 33 tiles of 63 steps: 32.5 per workgroup; last row and column tiles 104 wide
+    (600, 6600, 4096, 8),    # 5 x 52 tiles of 64 steps: 32.5 per workgroup; last tiles 88 rows, 72 columns
+]
+
+
+@pytest.mark.parametrize("M,N,K,r", STREAM_K_CASES)
+def test_forward_stream_k_every_output(M, N, K, r):
+    """Forwards on 128 x 128 tiles whose steps are shared out stream-K (each
+    workgroup a contiguous run of steps across tile boundaries, shared tiles
+    summed from their pieces in step order): every output of Y and H against
+    the oracle, and the same Y again from a second call on the same
+    workspace."""
+    alpha = 16.0
+    say(f"[fwd stream-K] M={M} N={N} K={K} r={r}")
+    shape = synth.LayerShape("tsk", M=M, N=N, K=K, r=r, seed_offset=9100 + M)
+    d = synth.make_layer(shape)
+    _, wd = oracle_layer(d, alpha, r)
+    q = gpu_quantize(d["W"])
+    X, A, B = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"])
+    ws = qa.fwd_workspace(M, N, K, r, "cuda")
+    Y, H = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)
+    Y2, _ = qa.linear_fwd(X, q, A, B, alpha, workspace=ws)
+    torch.cuda.synchronize()
+    Yr, Hr = oracle.linear_fwd(d["X"], wd, d["A"], d["B"], alpha, r)
+    check_close(bf16_f64(host_bf16_bits(Y)), Yr, "Y (stream-K)")
+    check_close(host(H), Hr, "H (stream-K)")
+    assert np.array_equal(host_bf16_bits(Y), host_bf16_bits(Y2)), "second call on the same workspace differs"
+
+
 def test_backward_256_tiles_every_output():
     """A backward whose dX runs on 256 x 256 tiles (M = 1000, K = 16384: 4 x 64
     tiles) with a ragged reduction (N = 1004: 15 full steps and 44 rows, dY
