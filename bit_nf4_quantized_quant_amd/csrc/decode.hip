@@ -541,8 +541,7 @@ bool decode_supported(int64_t N, int64_t K, int64_t r) {
 }
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
-  const int64_t r16 = (r + 15) & ~15;
-  if (M <= 4) return kHpartOff + (size_t)(M * r16) * sizeof(uint64_t);   // the GEMV path
+  if (M <= 4) return kHpartOff + (size_t)gemv_hcopies((int)M) * gemv_hcopy_words((int)M, (int)r) * sizeof(uint64_t);   // the GEMV path
   const int64_t S = decode_slices(N, K), G = (N + kTileRows - 1) / kTileRows;
   const int64_t RS = (kTileRows + S - 1) / S;
   const size_t hpart = ((size_t)(S * M * r) * sizeof(uint64_t) + 255) & ~(size_t)255;

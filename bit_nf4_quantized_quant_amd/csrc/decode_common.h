@@ -149,6 +149,24 @@ __device__ __forceinline__ uint64_t take_down_ticket(const DecodeParams& p, int 
   return take_slot_ticket(p.ws, kDownCtr, (uint32_t)tile, (uint32_t)p.n_htiles);
 }
 
+// The GEMV's LoRA-down workgroups publish H in gemv_hcopies(M) copies, each
+// gemv_hcopy_words(M, r) words long, and a weight wave reads copy
+// (4 tile + its row group) % gemv_hcopies(M): every weight wave reads all of
+// H, and with one copy their reads, which go to the coherence point, queue on
+// the same few lines (M = 1 on 4096 x 4096: 5.50 -> 5.36-5.40 us with eight
+// copies; M = 3 8.0 -> 7.85 us).  At M = 4 the weight workgroups run one per
+// CU, so the last of them wait for the LoRA-down workgroups' CUs, and the
+// extra stores cost more than they save (9.08 -> 9.25 us): one copy there.
+__host__ __device__ constexpr int gemv_hcopies(int M) { return M <= 3 ? 8 : 1; }
+__host__ __device__ constexpr int gemv_hcopy_words(int M, int r) {
+  return (((M * ((r + 15) & ~15) * 8 + 255) & ~255) + 256) / 8;
+}
+
+// s_waitcnt operand that waits for every vector memory load and for nothing
+// else (gfx9 encoding: vmcnt in bits 3:0 and 15:14 = 0, expcnt in 6:4 and
+// lgkmcnt in 11:8 at their maxima).
+constexpr int kWaitVm0 = 0x0F70;
+
 __device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
 // A workgroup-uniform value moved to a scalar register (integer division runs

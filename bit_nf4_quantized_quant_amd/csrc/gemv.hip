@@ -130,7 +130,8 @@ __device__ __forceinline__ float wave_sum4(const float (&v)[kGvRowsPerWave]) {
 }
 
 // LoRA-down row j = tile: H[m][j] = sum_k X[m][k] A[j][k] for m < M, published
-// as tagged words Hpart[m * r16 + j].
+// as tagged words Hpart[c * gemv_hcopy_words(M, r) + m * r16 + j] in each
+// copy c.
 template <int M>
 __device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_t* tag_lds, uint64_t ticket) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -162,8 +163,9 @@ __device__ void gemv_down_tile(const DecodeParams& p, int j, float* red, uint32_
   if (threadIdx.x < M) {
     float h = 0.f;
     for (int w = 0; w < kWaves; ++w) h += red[w * M + threadIdx.x];
-    const int r16 = (p.r + 15) & ~15;
-    st_tagged(&p.Hpart[(size_t)threadIdx.x * r16 + j], *tag_lds, h);
+    const int r16 = (p.r + 15) & ~15, cw = gemv_hcopy_words(M, p.r);
+#pragma unroll
+    for (int c = 0; c < gemv_hcopies(M); ++c) st_tagged(&p.Hpart[(size_t)c * cw + threadIdx.x * r16 + j], *tag_lds, h);
   }
 }
 
@@ -209,9 +211,10 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   // for j = lane, lane + 64 and the first read of this launch's H partials
   const bool lora = p.r > 0;
   const int r16 = (p.r + 15) & ~15;
+  const uint64_t* hcopy = p.Hpart + (size_t)((4 * tile + grp) % gemv_hcopies(M)) * gemv_hcopy_words(M, p.r);
   uint32_t bv[kGvRowsPerWave][2];
   uint64_t hv[M][2];
-  auto read_lora = [&]() {
+  auto load_b = [&]() {
     if (finisher && lora) {
       const uint32_t last = (uint32_t)p.N - 1u;
 #pragma unroll
@@ -222,8 +225,17 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
 #pragma unroll
         for (int rr = 0; rr < kGvRowsPerWave; ++rr)
           bv[rr][h] = p.B[(size_t)(row[rr] < last ? row[rr] : last) * p.r + j];
+      }
+    }
+  };
+  auto read_h = [&]() {
+    if (finisher && lora) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) hv[m][h] = ld_tagged(&p.Hpart[(size_t)m * r16 + j]);
+      for (int h = 0; h < 2; ++h) {
+        const int j = lane + 64 * h;
+        if (j >= p.r) continue;
+#pragma unroll
+        for (int m = 0; m < M; ++m) hv[m][h] = ld_tagged(&hcopy[(size_t)m * r16 + j]);
       }
     }
   };
@@ -243,12 +255,23 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
 #pragma unroll
     for (int i = 0; i < kNPL; ++i) {
       GvPiece<M>& cur = L[i % kDepth];
+      if (M == 1 && i == kNPL - 1) {
+        // B and the H partials are read once the last piece has arrived: by
+        // then H has been published (read with the weight loads, the first
+        // read comes back stale and the poll adds a round trip), and the
+        // reads are in flight during the last dot products instead of after
+        // them.  (At M >= 2 the registers that takes would spill.)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        load_b();
+        read_h();
+      }
       if (lane + 64 * i < hp) gv_mul<M, kDw>(cur, mu, lut, lane4, 8u * (((c0 + 64 * i) >> 1) & 3u), acc);
       if (i + kDepth < kNPL) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64 * (i + kDepth), cur);
     }
-    // (read here, H has been published by now: read any earlier, the first
-    // read comes back stale and the poll adds a round trip)
-    read_lora();
+    if constexpr (M > 1) {
+      load_b();
+      read_h();
+    }
   } else {
     // two pieces in flight at M = 1; at M >= 2 one (registers)
     constexpr bool kTwo = M == 1;
@@ -270,7 +293,8 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
         if (lane + 64 * i < hp) gv_mul<M, kDw>(La, mu, lut, lane4, 0u, acc);
       }
     }
-    read_lora();
+    load_b();
+    read_h();
   }
 
   // Epilogue.  Waves of the first half of K reduce their sums and leave them
@@ -306,7 +330,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float hval;
-        if (!poll_tagged(&p.Hpart[(size_t)m * r16 + j], hv[m][h], tag, deadline, &hval))
+        if (!poll_tagged(&hcopy[(size_t)m * r16 + j], hv[m][h], tag, deadline, &hval))
           hval = lane_lora_down(p.X, p.A, p.K, m, j, p.ws);
         if (tile == 0 && grp == 0 && p.H) p.H[m * p.r + j] = hval;
         const float sh = p.scale * hval;
