@@ -41,10 +41,16 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the QLoRA library needs ROCm's hipcc to build")
 
 
+# Per-source flags.  gemv.hip: the decode GEMV's leading pointer and size
+# arguments are preloaded into scalar registers at dispatch (gfx950 kernarg
+# preloading), so its first loads do not wait for a kernel-argument fetch.
+SOURCE_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

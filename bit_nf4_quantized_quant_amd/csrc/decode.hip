@@ -572,7 +572,8 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   return dec::decode_workspace_bytes(M, N, K, r);
 }
 bool decode_supported(int64_t M, int64_t N, int64_t K, int64_t r) {
-  return M <= 4 || dec::decode_supported(N, K, r);
+  // (the GEMV passes K / 64 in 24 bits: K < 2^30)
+  return M <= 4 ? K < (int64_t(1) << 30) : dec::decode_supported(N, K, r);
 }
 size_t decode_wait_counter_offset() { return (size_t)dec::kGiveupCounter; }
 hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) { return dec::launch_decode_fwd(a, s); }

@@ -181,7 +181,6 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
   // 32-row tiles (kFull): rows 4 w .. +3 over all of K
   const int grp = kFull ? wave : (wave & 3), half = kFull ? 0 : (wave >> 2);
   const bool finisher = kFull || half == 1;   // adds the LoRA term and stores
-  const float mu = load_mean(p);
   // this launch's epoch: thread 0's counter update goes out first, and its
   // reply, which comes back ahead of every later load, is used only at the
   // end (no other thread reads the variable)
@@ -250,6 +249,8 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
     GvPiece<M> L[kDepth];
 #pragma unroll
     for (int i = 0; i < kDepth && i < kNPL; ++i) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64 * i, L[i]);
+    // (the mean's pointer comes with the parameter block, after the loads)
+    const float mu = load_mean(p);
     build_pair_table<kThreads>(p, lut);   // while the loads are in flight
     __syncthreads();
 #pragma unroll
@@ -278,6 +279,7 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
     GvPiece<M> La, Lb;
     gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0, La);
     if (kTwo && 1 < npl) gv_load<M, kDw>(p, rc, r2, r1, rx, row, c0 + 64, Lb);
+    const float mu = load_mean(p);
     build_pair_table<kThreads>(p, lut);   // while the loads are in flight
     __syncthreads();
     if constexpr (kTwo) {
@@ -358,13 +360,36 @@ __device__ void gemv_tile(const DecodeParams& p, int tile, char* lut, float* red
 
 // Two workgroups per CU (4 waves per SIMD) up to M = 3; at M = 4 the X
 // registers need more, and one workgroup per CU runs faster than spilling.
+//
+// The pointers and sizes the first loads need come first in the argument
+// list, ahead of the parameter block: they are preloaded into scalar
+// registers at dispatch (this file is built with kernarg preloading; 14
+// dwords fit beside the kernarg pointer), so the weight loads go out without
+// waiting for a kernel-argument fetch; the rest of the block arrives while
+// they are in flight, in the weight tiles and in the LoRA-down workgroups
+// alike.  (The tile counts follow from N and r; K / 64 and r share a dword.
+// Any early use of a field of the block waits for all of it: scalar loads
+// complete out of order, so their only wait is for every one.)
 template <int M, int kNPL, bool kFull>
-__global__ void __launch_bounds__(kThreads, M <= 3 ? 4 : 2) qlora_gemv_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kThreads, M <= 3 ? 4 : 2)
+    qlora_gemv_kernel(const uint16_t* X, const uint8_t* codes, const uint8_t* c2, const float* c1, char* ws,
+                      const uint16_t* A, int N, uint32_t kr, DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];   // 64 KiB
   __shared__ float red[kRows * M];
   __shared__ uint32_t tag;
   const int tile = (int)blockIdx.x;
-  QLORA_FETCH_ARGS(p);
+  p.X = X;
+  p.codes = codes;
+  p.c2 = c2;
+  p.c1 = c1;
+  p.ws = ws;
+  p.A = A;
+  p.K = (int)((kr & 0xFFFFFFu) << 6);   // kr = K / 64 | r << 24
+  p.N = N;
+  const int r = (int)(kr >> 24);
+  p.r = r;
+  p.n_htiles = r;                                                // one LoRA-down workgroup per row of A
+  p.n_wtiles = (N + (kFull ? 2 * kRows : kRows) - 1) / (kFull ? 2 * kRows : kRows);   // the weight tiles
   if (tile < p.n_htiles) {
     uint64_t hticket = 0;
     if (threadIdx.x == 0) hticket = take_down_ticket(p, tile);
@@ -374,7 +399,8 @@ __global__ void __launch_bounds__(kThreads, M <= 3 ? 4 : 2) qlora_gemv_kernel(De
   gemv_tile<M, kNPL, kFull>(p, tile - p.n_htiles, lut, red, &tag);
 }
 
-typedef void (*GemvKernel)(DecodeParams);
+typedef void (*GemvKernel)(const uint16_t*, const uint8_t*, const uint8_t*, const float*, char*, const uint16_t*, int,
+                           uint32_t, DecodeParams);
 template <int M>
 GemvKernel gemv_kernel(int npl, bool full) {
   if (full) {   // 32-row tiles: whole pieces per lane over all of K (the launcher's condition)
@@ -417,7 +443,10 @@ hipError_t launch_gemv_fwd(const DecodeParams& p0, hipStream_t s) {
                       : p.M == 3 ? gemv_kernel<3>(npl, full)
                                  : gemv_kernel<4>(npl, full);
   const dim3 grid(p.n_htiles + p.n_wtiles);
-  hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, p);
+  // K / 64 and r share a dword of the preloaded arguments (K < 2^30, r <= 128:
+  // the decode path's own limits)
+  const uint32_t kr = (uint32_t)(p.K >> 6) | ((uint32_t)p.r << 24);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, p.X, p.codes, p.c2, p.c1, p.ws, p.A, p.N, kr, p);
   return hipGetLastError();
 }
 
