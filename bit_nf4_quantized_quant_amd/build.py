@@ -41,10 +41,12 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the QLoRA library needs ROCm's hipcc to build")
 
 
-# Per-source flags.  gemv.hip: the decode GEMV's leading pointer and size
-# arguments are preloaded into scalar registers at dispatch (gfx950 kernarg
-# preloading), so its first loads do not wait for a kernel-argument fetch.
-SOURCE_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+# Per-source flags.  gemv.hip, decode.hip: the decode kernels' leading pointer
+# and size arguments are preloaded into scalar registers at dispatch (gfx950
+# kernarg preloading), so their first loads do not wait for a kernel-argument
+# fetch.
+_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+SOURCE_FLAGS = {"gemv.hip": _PRELOAD, "decode.hip": _PRELOAD}
 
 
 def _compile(src: str, verbose: bool) -> str:

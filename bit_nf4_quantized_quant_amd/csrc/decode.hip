@@ -123,16 +123,45 @@ __device__ __attribute__((noinline)) float lane_output(const uint16_t* X, const 
 }
 
 // kNB: NF4 blocks per wave at most (the launcher's bound for this shape).
-template <int kNB>
-__global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams p) {
+// kEarly: the pointers and sizes the first loads need come first in the
+// argument list, ahead of the parameter block, and are preloaded into scalar
+// registers at dispatch (this file is built with kernarg preloading), so the
+// X, A and code loads go out without waiting for a kernel-argument fetch; the
+// c2 pointer and the rest of the block arrive behind them.  kr = K / 64 |
+// r << 24, msh = M | S << 8 | hcols << 16.  Otherwise the whole block is
+// fetched first, in one round trip (the leading arguments unused): grids of
+// more than one round of workgroups ran faster that way (11008 x 4096, M =
+// 16: 21.8 against 22.4 us), those of one round slower (4096 x 4096, M = 16:
+// 11.7 against 10.6 us).
+template <int kNB, bool kEarly>
+__global__ void __launch_bounds__(kThreads, 2)
+    qlora_decode_kernel(const uint16_t* X, const uint16_t* A, const uint8_t* codes, const float* c1, char* ws,
+                        int n_out, uint32_t kr, uint32_t msh, DecodeParams p) {
   // pair table (64 KiB); its spare halves hold the staged codes and then the
   // reductions
   __shared__ __attribute__((aligned(16))) char lut[256 * kPairStride];
   __shared__ float hbuf[2048];   // LoRA-down wave partials, then the H partials read back
   __shared__ float lev[16];
   __shared__ uint32_t tag_lds;
-  QLORA_FETCH_ARGS(p);
-  asm volatile("" ::"s"(p.G), "s"(p.S), "s"(p.hcols), "s"(p.Ypart), "s"(p.Hpart));
+  if constexpr (kEarly) {
+    p.X = X;
+    p.A = A;
+    p.codes = codes;
+    p.c1 = c1;
+    p.ws = ws;
+    p.N = n_out;
+    p.K = (int)((kr & 0xFFFFFFu) << 6);
+    p.r = (int)(kr >> 24);
+    p.M = (int)(msh & 0xFFu);
+    p.S = (int)((msh >> 8) & 0xFFu);
+    p.hcols = (int)(msh >> 16);
+    p.G = (n_out + kTileRows - 1) / kTileRows;
+    p.n_htiles = 0;
+    p.n_wtiles = p.G * p.S;
+  } else {
+    QLORA_FETCH_ARGS(p);
+    asm volatile("" ::"s"(p.G), "s"(p.S), "s"(p.hcols), "s"(p.Ypart), "s"(p.Hpart));
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, g4 = lane >> 4;
@@ -143,7 +172,8 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
   const int n0 = g * kTileRows;
   const int K = p.K, N = p.N, M = p.M, r = p.r;
   const int nblk = K >> 6;
-  const float mu = load_mean(p);
+  float mu = 0.f;
+  if constexpr (!kEarly) mu = load_mean(p);
   // this launch's epoch: wave 0 reads this workgroup's counter ahead of
   // every other load, and only then does thread 0 add the workgroup's share
   // (a read after it could see the launch's last share and the next epoch);
@@ -221,6 +251,9 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
                                                   rc, row * (uint32_t)(K / 2) + (uint32_t)blk[i] * 32u + 8u * g4, 0, 0));
     }
   }
+  // (nothing below moves above the code loads: the c2 pointer comes with the
+  // parameter block, and waiting for it there would hold them back)
+  if constexpr (kEarly) __builtin_amdgcn_sched_barrier(0);
   // Block constants with one lane per tile row (row n0 + lane): the c2 byte
   // of each of the wave's blocks, and c1 of its first and last block (a run
   // of <= 4 blocks crosses at most one 256-block boundary of the flattened
@@ -231,6 +264,8 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
   for (int i = 0; i < kNB; ++i) c2r[i] = __builtin_amdgcn_raw_buffer_load_b8(r2, f0 + (uint32_t)i, 0, 0);
   const float c1a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, (f0 >> 8) * 4u, 0, 0));
   const float c1b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, ((f0 + kNB - 1) >> 8) * 4u, 0, 0));
+  // (the mean's pointer comes with the parameter block, after the loads)
+  if constexpr (kEarly) mu = load_mean(p);
   build_pair_table<kThreads>(p, lut);   // while the loads are in flight
   if (threadIdx.x < 16) {
     uint32_t hv = 0;
@@ -487,13 +522,22 @@ __global__ void __launch_bounds__(kThreads, 2) qlora_decode_kernel(DecodeParams 
   }
 }
 
-typedef void (*DecodeKernel)(DecodeParams);
-DecodeKernel decode_kernel(int nb) {
+typedef void (*DecodeKernel)(const uint16_t*, const uint16_t*, const uint8_t*, const float*, char*, int, uint32_t,
+                             uint32_t, DecodeParams);
+DecodeKernel decode_kernel(int nb, bool early) {
+  if (early) {
+    switch (nb) {
+      case 1: return qlora_decode_kernel<1, true>;
+      case 2: return qlora_decode_kernel<2, true>;
+      case 3: return qlora_decode_kernel<3, true>;
+      default: return qlora_decode_kernel<4, true>;
+    }
+  }
   switch (nb) {
-    case 1: return qlora_decode_kernel<1>;
-    case 2: return qlora_decode_kernel<2>;
-    case 3: return qlora_decode_kernel<3>;
-    default: return qlora_decode_kernel<4>;
+    case 1: return qlora_decode_kernel<1, false>;
+    case 2: return qlora_decode_kernel<2, false>;
+    case 3: return qlora_decode_kernel<3, false>;
+    default: return qlora_decode_kernel<4, false>;
   }
 }
 
@@ -562,7 +606,13 @@ hipError_t launch_decode_fwd(const FwdArgs& a, hipStream_t s) {
   p.Ypart = reinterpret_cast<uint64_t*>(p.ws + kHpartOff + hpart);
   const int64_t nblk = a.K / 64, slice = (nblk + S - 1) / S;
   const int nb = (int)((slice + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(decode_kernel(nb), dim3(p.n_wtiles), dim3(kThreads), 0, s, p);
+  // K / 64 (< 2^24), r (<= 128), M (<= 16), S (<= 16) and hcols (<= 16) packed
+  // into two preloaded dwords
+  const uint32_t kr = (uint32_t)(a.K >> 6) | ((uint32_t)a.r << 24);
+  const uint32_t msh = (uint32_t)a.M | ((uint32_t)S << 8) | ((uint32_t)p.hcols << 16);
+  const bool early = p.n_wtiles <= 2 * (int64_t)cu_count();   // one round of resident workgroups
+  hipLaunchKernelGGL(decode_kernel(nb, early), dim3(p.n_wtiles), dim3(kThreads), 0, s, p.X, p.A, p.codes, p.c1,
+                     p.ws, p.N, kr, msh, p);
   return hipGetLastError();
 }
 
