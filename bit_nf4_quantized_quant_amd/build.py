@@ -46,7 +46,7 @@ def _hipcc() -> str:
 # kernarg preloading), so their first loads do not wait for a kernel-argument
 # fetch.
 _PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
-SOURCE_FLAGS = {"gemv.hip": _PRELOAD, "decode.hip": _PRELOAD}
+SOURCE_FLAGS = {"gemv.hip": _PRELOAD, "decode.hip": _PRELOAD, "gemm.hip": _PRELOAD}
 
 
 def _compile(src: str, verbose: bool) -> str:
