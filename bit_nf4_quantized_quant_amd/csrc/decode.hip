@@ -561,7 +561,19 @@ int decode_slices(int64_t N, int64_t K) {
       best_cost = cost;
     }
   }
-  return best == 0 ? kMaxSlices : best;
+  if (best == 0) return kMaxSlices;
+  // Past one round of resident workgroups (two per CU) the model undercounts
+  // the slices' exchange: there the fewest slices that give every CU a
+  // workgroup measured faster (M = 16: 22016 x 4096 S = 8 -> 2, 62.1 -> 31.7
+  // us; 12288 x 4096, M = 12, r = 32, 4 -> 2, 21.0 -> 19.6; 11008 x 4096 4 ->
+  // 2, 21.9 -> 21.6, at M = 8 19.1 -> 19.4).  Within one round the model's
+  // choice stays (4096 x 11008: S = 6 instead of 8 was 21.2 -> 24.3 us).
+  if (G * best > 2 * cus) {
+    int64_t fill = std::max<int64_t>((cus + G - 1) / G, (nblk + kWaves * kMaxWaveBlocks - 1) / (kWaves * kMaxWaveBlocks));
+    fill = std::min<int64_t>(std::max<int64_t>(fill, 1), most);
+    if ((nblk + fill - 1) / fill <= (int64_t)kWaves * kMaxWaveBlocks) return (int)fill;
+  }
+  return best;
 }
 
 // LoRA-down columns per producing workgroup: as few as the row groups allow,

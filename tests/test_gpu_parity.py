@@ -806,12 +806,13 @@ def test_decoder_fused_qkv_full_size_sampled():
     block-structured rank-32 adapter (q rows on columns 0..15, v rows on
     16..31, k rows zero), at M = 1 and M = 512: constants in full and 256
     sampled output columns spread over the three segments, against the
-    oracle."""
+    oracle; also at M = 12 and 16, where the matrix-core decode kernel runs
+    on two K slices (the grid of four would need a second round)."""
     N, K, r = 12288, 4096, 32
     rows = np.sort(np.concatenate([np.random.default_rng(77 + i).choice(4096, 85 + (i == 0), replace=False) + 4096 * i
                                    for i in range(3)]))
     q = ref = None
-    for M in (1, 512):
+    for M in (1, 12, 16, 512):
         sh = synth.LayerShape(f"decoder_qkv_m{M}", M=M, N=N, K=K, r=r, seed_offset=1777)
         say(f"[decoder fused] {sh.name}")
         d = synth.make_layer(sh)
@@ -824,6 +825,27 @@ def test_decoder_fused_qkv_full_size_sampled():
         Y, H = qa.linear_fwd(dev_bf16(d["X"]), q, A, B, synth.FUSED_QKV_ALPHA)
         torch.cuda.synchronize()
         check_fwd_sampled(d, ref, rows, Y, H, synth.FUSED_QKV_ALPHA, r, sh.name)
+
+
+def test_decode_slices_past_one_round_sampled():
+    """The matrix-core decode kernel where the slice model's grid would need
+    several rounds of workgroups (22016 x 4096: 344 row groups, two slices
+    of 32 blocks, the operands loaded straight from memory), M = 5, 8 and 16:
+    constants in full and 256 sampled output columns against the oracle, no
+    bounded wait giving up."""
+    N, K, r, alpha = 22016, 4096, 64, 16.0
+    rows = np.sort(np.random.default_rng(4242).choice(N, 256, replace=False))
+    q = ref = None
+    for M in (5, 8, 16):
+        sh = synth.LayerShape(f"slices_m{M}", M=M, N=N, K=K, r=r, seed_offset=4242)
+        say(f"[decode slices] {sh.name}")
+        d = synth.make_layer(sh)
+        if q is None:
+            ref = oracle_sampled(d["W"], rows)
+            q = gpu_quantize(d["W"])
+            check_quantized(q, ref, rows)
+        Y, H = run_fwd(d, q, alpha, r)
+        check_fwd_sampled(d, ref, rows, Y, H, alpha, r, sh.name)
 
 
 @pytest.mark.parametrize("layer", [0, synth.DECODER_LAYERS - 1])
